@@ -1,0 +1,107 @@
+// Internal parameter blocks and launchers of the MLA library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kMaxRopePairs = 64;   // rotary width <= 128 (half-split head) or <= 64 (decoupled)
+
+// Inverse RoPE frequencies theta_j = base^(-2j/d), split into an fp32 head and an
+// fp32 tail so the device can rebuild them to ~double precision.
+struct RopeTable {
+  float hi[kMaxRopePairs];
+  float lo[kMaxRopePairs];
+};
+void make_rope_table(RopeTable* t, int dim, float base);
+
+// ---------------------------------------------------------------------------
+// Projection GEMM: out[m, n] = sum_k A[m, k] * W[n, k]   (W [N][K], "NT")
+//            or    out[m, n] = sum_k A[m, k] * W[k, n]   (W [K][N], w_kmajor)
+// Rows of A and of the output may live in a cache ([batch][max_seq][.]) and the
+// output columns of a segment may be scattered head by head.
+// ---------------------------------------------------------------------------
+enum RopeKind { ROPE_OFF = 0, ROPE_INTERLEAVED = 1, ROPE_HALFSPLIT = 2 };
+
+struct GemmSeg {
+  const void* w;        // this segment's first weight row (NT) / column (k-major)
+  long long w_ld;       // elements between consecutive W rows
+  int n;                // output columns of this segment
+  void* out;            // output base
+  long long out_ld;     // elements between output rows
+  int out_f32;          // 1: float output, 0: element type of the GEMM
+  int out_hw, out_hs;   // column map oc = (c / hw) * hs + c % hw   (hw = 0: oc = c)
+  int out_cache;        // 1: output row of (b, t) is b * out_bstride + pos0[b] + t
+  int rope;             // RopeKind applied to this segment's columns before the store
+  int rope_d;           // rotary width: pairs live inside [h*rope_d, (h+1)*rope_d)
+};
+
+struct GemmParams {
+  const void* a;            // A base
+  long long a_ld;           // elements between A rows
+  int a_cache;              // 1: A row of (b, t) is b * a_bstride + t
+  long long a_bstride;      // rows per batch entry in A's storage (cache max_seq)
+  long long out_bstride;    // rows per batch entry in a cache output
+  int M, K;
+  int rows_per_batch;       // t = m % rows_per_batch, b = m / rows_per_batch
+  const int* pos0;          // per-batch first position (NULL = 0); RoPE angle uses pos0[b] + t
+  int nseg;
+  GemmSeg seg[2];
+  // grouped launch (blockIdx.z = group): offsets in elements, g = (z / zdiv, z % zdiv)
+  int zdiv;
+  long long a_goff[2];      // added to A's column start
+  long long w_goff[2];      // added to every segment's W pointer
+  long long o_goff[2];      // added to every segment's output column start
+  int w_kmajor;
+  RopeTable rope;
+};
+
+hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Split-context decode over the latent cache + log-sum-exp combine
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+  const void* q_lat;        // q_lat[(b*H + h)*q_lat_hs + d], d < rb
+  const void* q_rope;       // q_rope[(b*H + h)*q_rope_hs + d], d < d_rope (NULL if none)
+  int q_lat_hs, q_rope_hs;
+  const void* ckv;          // cache latent [max_batch][max_seq][r_kv]
+  const void* kr;           // cache rotary key [max_batch][max_seq][d_rope] or NULL
+  long long cache_bstride;  // max_seq
+  const int* ctx_len;       // [B]: the query attends rows 0..ctx_len[b]
+  int B, H, L, hpb;         // hpb = H / L heads per latent block
+  int r_kv, rb, d_rope;     // total latent, block width, rotary width
+  int chunk;                // tokens per split (multiple of 32)
+  int nsplit;               // splits allocated per (b, head)
+  int head_tiles;           // head tiles per latent block
+  float scale_log2;         // softmax scale * log2(e)
+  float* part_z;            // [B][H][nsplit][DLP]
+  float* part_ml;           // [B][H][nsplit][2]  (running max in log2 units, sum)
+  void* z;                  // [B][H][rb] output
+};
+
+hipError_t launch_decode(const DecodeParams& p, bool use_bf16, int dl_pad, int dr_pad, int nw,
+                         hipStream_t s);
+bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, int* dr_pad, int* nw);
+
+// ---------------------------------------------------------------------------
+// Flash-style causal prefill
+// ---------------------------------------------------------------------------
+struct PrefillParams {
+  const void* q;            // [B][S][H][dq]
+  const void* k;            // decompressed keys [B*S][H*dn] (head h at columns h*dn)
+  const void* kr;           // rotated shared key rows: kr + (b*kr_bstride + t)*d_rope, or NULL
+  long long kr_bstride;
+  const void* v;            // values [B*S][H*dv]
+  void* o;                  // [B][S][H][dv]
+  int B, S, H, dn, d_rope, dv;
+  float scale_log2;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, bool use_bf16, int dq_pad, int dv_pad, hipStream_t s);
+bool prefill_supported(bool use_bf16, int dq, int dv, int* dq_pad, int* dv_pad);
+
+int device_cu_count();
+
+}  // namespace mla

@@ -1,0 +1,583 @@
+// Host side of the C ABI: argument checks, workspace layout and the launch sequence of
+// each entry point.  No allocation, no host synchronisation; everything is enqueued on
+// the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/mla.h"
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+
+void make_rope_table(RopeTable* t, int dim, float base) {
+  memset(t, 0, sizeof(*t));
+  if (dim <= 0) return;
+  for (int j = 0; j < dim / 2 && j < kMaxRopePairs; ++j) {
+    double th = pow((double)base, -2.0 * j / (double)dim);
+    float hi = (float)th;
+    t->hi[j] = hi;
+    t->lo[j] = (float)(th - (double)hi);
+  }
+}
+
+int device_cu_count() { return 256; }
+
+}  // namespace mla
+
+using namespace mla;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+// Compute units of one MI355X; the split plan (and hence the workspace size) is a pure
+// function of the shapes so that mla_workspace_bytes() needs no device query.
+constexpr int kCUs = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_bf16(const mla_dims* d) { return d->dtype == MLA_DTYPE_BF16; }
+size_t esize(const mla_dims* d) { return is_bf16(d) ? 2 : 4; }
+int rblock(const mla_dims* d) { return d->r_kv / d->n_latent_heads; }
+int dq_of(const mla_dims* d) { return d->d_nope + d->d_rope; }
+
+float softmax_scale(const mla_dims* d) {
+  if (d->softmax_scale > 0.f) return d->softmax_scale;
+  if (d->rope_mode == MLA_ROPE_DECOUPLED_INTERLEAVED) return (float)(1.0 / sqrt((double)(d->d_nope + d->d_rope)));
+  return (float)(1.0 / sqrt((double)d->d_nope));
+}
+
+// Decode split plan: tokens per split (multiple of 32) and splits per (sequence, head).
+struct SplitPlan {
+  int chunk, nsplit, head_tiles, dl, dr, nw;
+  bool ok;
+};
+
+SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
+  SplitPlan sp{};
+  const int L = d->n_latent_heads, hpb = d->n_heads / L;
+  sp.ok = decode_supported(is_bf16(d), rblock(d), d->d_rope, hpb, &sp.dl, &sp.dr, &sp.nw);
+  if (!sp.ok) return sp;
+  sp.head_tiles = cdiv(hpb, 32 * sp.nw);
+  const long long wgs = (long long)B * L * sp.head_tiles;
+  const int wg_per_cu = sp.nw == 4 ? 1 : 8;
+  const int ntok = max_ctx + 1;
+  int ns = (int)((kCUs * wg_per_cu + wgs - 1) / wgs);
+  if (ns < 1) ns = 1;
+  int chunk = round_up(cdiv(ntok, ns), 32);
+  if (sp.nw == 1 && chunk > 1024) chunk = 1024;
+  if (chunk < 32) chunk = 32;
+  sp.chunk = chunk;
+  sp.nsplit = cdiv(ntok, chunk);
+  return sp;
+}
+
+struct DecodeWs {
+  size_t cq, q, qlat, z, o, part_z, part_ml, total;
+};
+
+DecodeWs decode_layout(const mla_dims* d, int B, int max_ctx, bool attention_only) {
+  DecodeWs w{};
+  SplitPlan sp = plan_decode(d, B, max_ctx);
+  const size_t es = esize(d);
+  const int H = d->n_heads, rb = rblock(d);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  if (!attention_only) {
+    w.cq = take(d->r_q > 0 ? (size_t)B * d->r_q * es : 0);
+    w.q = take((size_t)B * H * dq_of(d) * es);
+    w.qlat = take((size_t)B * H * rb * es);
+    w.z = take((size_t)B * H * rb * es);
+    w.o = take((size_t)B * H * d->d_v * es);
+  }
+  w.part_z = take((size_t)B * H * sp.nsplit * sp.dl * sizeof(float));
+  w.part_ml = take((size_t)B * H * sp.nsplit * 2 * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+struct PrefillWs {
+  size_t cq, q, lat, latr, k, v, o, total;
+};
+
+PrefillWs prefill_layout(const mla_dims* d, int B, int S, bool attention_only) {
+  PrefillWs w{};
+  const size_t es = esize(d);
+  const size_t rows = (size_t)B * S;
+  const int H = d->n_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  if (!attention_only) {
+    w.cq = take(d->r_q > 0 && d->rope_mode == MLA_ROPE_DECOUPLED_INTERLEAVED ? rows * d->r_q * es : 0);
+    w.q = take(rows * H * dq_of(d) * es);
+    w.lat = take(rows * d->r_kv * es);
+    w.latr = take(rows * d->d_rope * es);
+    w.o = take(rows * H * d->d_v * es);
+  }
+  w.k = take(rows * H * d->d_nope * es);
+  w.v = take(rows * H * d->d_v * es);
+  w.total = off;
+  return w;
+}
+
+mla_status check_weights(const mla_dims* d, const mla_weights* w, bool need_q, bool need_kv_up,
+                         bool need_out) {
+  if (!w) return MLA_ERR_INVALID_ARG;
+  if (!w->w_dkv) return MLA_ERR_INVALID_ARG;
+  const bool dec = d->rope_mode == MLA_ROPE_DECOUPLED_INTERLEAVED;
+  if (dec && !w->w_kr) return MLA_ERR_INVALID_ARG;
+  if (need_q) {
+    if (dec && d->r_q > 0) {
+      if (!w->w_dq || !w->w_uq || !w->w_qr) return MLA_ERR_INVALID_ARG;
+    } else {
+      if (!w->w_q) return MLA_ERR_INVALID_ARG;
+      if (dec && !w->w_qr) return MLA_ERR_INVALID_ARG;
+    }
+  }
+  if (need_kv_up && (!w->w_uk || !w->w_uv)) return MLA_ERR_INVALID_ARG;
+  if (need_out && !w->w_o) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+mla_status check_cache(const mla_dims* d, const mla_cache* c) {
+  if (!c || !c->ckv || c->max_batch <= 0 || c->max_seq <= 0) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope > 0 && !c->kr) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+GemmParams gemm_base(const mla_dims* d) {
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.zdiv = 1;
+  p.rows_per_batch = 1;
+  p.nseg = 1;
+  (void)d;
+  return p;
+}
+
+GemmSeg plain_seg(const void* w, long long w_ld, int n, void* out, long long out_ld, bool f32) {
+  GemmSeg s;
+  memset(&s, 0, sizeof(s));
+  s.w = w;
+  s.w_ld = w_ld;
+  s.n = n;
+  s.out = out;
+  s.out_ld = out_ld;
+  s.out_f32 = f32 ? 1 : 0;
+  return s;
+}
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+const char* atc(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
+
+// c = W_DKV x and k_R = RoPE(W_KR x) for `rows` rows, written to cache rows (b, pos0[b]+t)
+// or, without a cache, to plain row-major buffers.
+hipError_t run_latent(const mla_dims* d, const mla_weights* w, const void* x, int B, int T,
+                      const int32_t* pos0, const mla_cache* cache, void* lat, void* latr,
+                      hipStream_t st) {
+  GemmParams p = gemm_base(d);
+  p.a = x;
+  p.a_ld = d->d_model;
+  p.M = B * T;
+  p.K = d->d_model;
+  p.rows_per_batch = T;
+  p.pos0 = pos0;
+  const bool bf = is_bf16(d);
+  p.seg[0] = plain_seg(w->w_dkv, d->d_model, d->r_kv, cache ? cache->ckv : lat, d->r_kv, false);
+  if (cache) {
+    p.seg[0].out_cache = 1;
+    p.out_bstride = cache->max_seq;
+  }
+  if (d->d_rope > 0) {
+    p.nseg = 2;
+    p.seg[1] = plain_seg(w->w_kr, d->d_model, d->d_rope, cache ? cache->kr : latr, d->d_rope, false);
+    p.seg[1].out_cache = cache ? 1 : 0;
+    p.seg[1].rope = ROPE_INTERLEAVED;
+    p.seg[1].rope_d = d->d_rope;
+    make_rope_table(&p.rope, d->d_rope, d->rope_base);
+  }
+  return launch_gemm(p, 1, bf, st);
+}
+
+// Queries q[rows][H][d_nope + d_rope] from x (and the query latent when r_q > 0).
+hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, int rows,
+                       int rows_per_batch, const int32_t* pos0, void* cq, void* q, hipStream_t st) {
+  const bool bf = is_bf16(d);
+  const int H = d->n_heads, dq = dq_of(d);
+  const size_t es = esize(d);
+  const bool dec = d->rope_mode == MLA_ROPE_DECOUPLED_INTERLEAVED;
+  const void* src = x;
+  int src_w = d->d_model;
+  hipError_t e;
+  if (dec && d->r_q > 0) {
+    GemmParams p = gemm_base(d);
+    p.a = x;
+    p.a_ld = d->d_model;
+    p.M = rows;
+    p.K = d->d_model;
+    p.seg[0] = plain_seg(w->w_dq, d->d_model, d->r_q, cq, d->r_q, false);
+    e = launch_gemm(p, 1, bf, st);
+    if (e != hipSuccess) return e;
+    src = cq;
+    src_w = d->r_q;
+  }
+  GemmParams p = gemm_base(d);
+  p.a = src;
+  p.a_ld = src_w;
+  p.M = rows;
+  p.K = src_w;
+  p.rows_per_batch = rows_per_batch;
+  p.pos0 = pos0;
+  const void* wq = (dec && d->r_q > 0) ? w->w_uq : w->w_q;
+  p.seg[0] = plain_seg(wq, src_w, H * d->d_nope, q, (long long)H * dq, false);
+  p.seg[0].out_hw = d->d_nope;
+  p.seg[0].out_hs = dq;
+  if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) {
+    p.seg[0].rope = ROPE_HALFSPLIT;
+    p.seg[0].rope_d = d->d_nope;
+    make_rope_table(&p.rope, d->d_nope, d->rope_base);
+  }
+  if (dec) {
+    p.nseg = 2;
+    p.seg[1] = plain_seg(w->w_qr, src_w, H * d->d_rope, at(q, d->d_nope * es), (long long)H * dq, false);
+    p.seg[1].out_hw = d->d_rope;
+    p.seg[1].out_hs = dq;
+    p.seg[1].rope = ROPE_INTERLEAVED;
+    p.seg[1].rope_d = d->d_rope;
+    make_rope_table(&p.rope, d->d_rope, d->rope_base);
+  }
+  return launch_gemm(p, 1, bf, st);
+}
+
+// Explicit keys / values from the latent rows 0..S-1 of each sequence.
+hipError_t run_kv_up(const mla_dims* d, const mla_weights* w, const void* lat, bool lat_cache,
+                     long long lat_bstride, int B, int S, void* k, void* v, hipStream_t st) {
+  const bool bf = is_bf16(d);
+  const int H = d->n_heads, L = d->n_latent_heads, rb = rblock(d);
+  const int sub_out = H * d->d_nope / L;
+  GemmParams p = gemm_base(d);
+  p.a = lat;
+  p.a_ld = d->r_kv;
+  p.a_cache = lat_cache ? 1 : 0;
+  p.a_bstride = lat_bstride;
+  p.M = B * S;
+  p.K = rb;
+  p.rows_per_batch = S;
+  p.nseg = 2;
+  p.seg[0] = plain_seg(w->w_uk, rb, sub_out, k, (long long)H * d->d_nope, false);
+  p.seg[1] = plain_seg(w->w_uv, rb, sub_out, v, (long long)H * d->d_v, false);
+  if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) {
+    p.seg[0].rope = ROPE_HALFSPLIT;
+    p.seg[0].rope_d = d->d_nope;
+    make_rope_table(&p.rope, d->d_nope, d->rope_base);
+  }
+  // latent block g feeds output columns [g*sub_out, (g+1)*sub_out)
+  p.zdiv = 1;
+  p.a_goff[0] = rb;
+  p.w_goff[0] = (long long)sub_out * rb;
+  p.o_goff[0] = sub_out;
+  return launch_gemm(p, L, bf, st);
+}
+
+// Per head h (block g, index hi in the block): out[:, h*out_w ...] = A_h . W_h, with W_h
+// the head's rows of a (block) up-projection, read k-major (absorb) or [out][in] (W_UV).
+hipError_t run_per_head(const mla_dims* d, const void* a, long long a_ld, long long a_head,
+                        int K, const void* wmat, bool kmajor, int n, void* out, long long out_ld,
+                        long long out_head, int B, hipStream_t st) {
+  const int H = d->n_heads, L = d->n_latent_heads, hpb = H / L, rb = rblock(d);
+  const int sub_out = H * d->d_nope / L;
+  GemmParams p = gemm_base(d);
+  p.a = a;
+  p.a_ld = a_ld;
+  p.M = B;
+  p.K = K;
+  p.w_kmajor = kmajor ? 1 : 0;
+  p.seg[0] = plain_seg(wmat, rb, n, out, out_ld, false);
+  p.zdiv = hpb;
+  p.a_goff[0] = a_head * hpb;
+  p.a_goff[1] = a_head;
+  p.w_goff[0] = (long long)sub_out * rb;
+  p.w_goff[1] = (long long)d->d_nope * rb;
+  p.o_goff[0] = out_head * hpb;
+  p.o_goff[1] = out_head;
+  return launch_gemm(p, H, is_bf16(d), st);
+}
+
+hipError_t run_out_proj(const mla_dims* d, const mla_weights* w, const void* o, int rows, float* y,
+                        hipStream_t st) {
+  GemmParams p = gemm_base(d);
+  const int hv = d->n_heads * d->d_v;
+  p.a = o;
+  p.a_ld = hv;
+  p.M = rows;
+  p.K = hv;
+  p.seg[0] = plain_seg(w->w_o, hv, d->d_model, y, d->d_model, true);
+  return launch_gemm(p, 1, is_bf16(d), st);
+}
+
+DecodeParams decode_params(const mla_dims* d, const mla_cache* cache, const int32_t* ctx_len,
+                           int B, int max_ctx, void* ws, const DecodeWs& lay) {
+  SplitPlan sp = plan_decode(d, B, max_ctx);
+  DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.ckv = cache->ckv;
+  p.kr = cache->kr;
+  p.cache_bstride = cache->max_seq;
+  p.ctx_len = ctx_len;
+  p.B = B;
+  p.H = d->n_heads;
+  p.L = d->n_latent_heads;
+  p.hpb = d->n_heads / d->n_latent_heads;
+  p.r_kv = d->r_kv;
+  p.rb = rblock(d);
+  p.d_rope = d->d_rope;
+  p.chunk = sp.chunk;
+  p.nsplit = sp.nsplit;
+  p.head_tiles = sp.head_tiles;
+  p.scale_log2 = softmax_scale(d) * kLog2e;
+  p.part_z = reinterpret_cast<float*>(at(ws, lay.part_z));
+  p.part_ml = reinterpret_cast<float*>(at(ws, lay.part_ml));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE";
+    case MLA_ERR_CAPACITY: return "MLA_ERR_CAPACITY";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+mla_status mla_validate(const mla_dims* d) {
+  if (!d) return MLA_ERR_INVALID_ARG;
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->d_nope <= 0 || d->d_v <= 0 || d->r_kv <= 0 ||
+      d->r_q < 0 || d->d_rope < 0 || d->n_latent_heads <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (d->dtype != MLA_DTYPE_F32 && d->dtype != MLA_DTYPE_BF16) return MLA_ERR_INVALID_ARG;
+  if (d->rope_mode < MLA_ROPE_NONE || d->rope_mode > MLA_ROPE_FULL_HALFSPLIT) return MLA_ERR_INVALID_ARG;
+  if (!(d->softmax_scale == d->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  // Family rules of the pages.
+  if (d->rope_mode == MLA_ROPE_DECOUPLED_INTERLEAVED) {
+    if (d->d_rope <= 0 || (d->d_rope & 1)) return MLA_ERR_SHAPE;    // even rotary dim
+  } else if (d->d_rope != 0) {
+    return MLA_ERR_SHAPE;
+  }
+  if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT && (d->d_nope & 1)) return MLA_ERR_SHAPE;
+  if (d->rope_mode != MLA_ROPE_NONE && !(d->rope_base > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (d->n_latent_heads > 1) {
+    if (d->r_kv % d->n_latent_heads) return MLA_ERR_SHAPE;          // L | latent rank
+    if (d->n_heads % d->n_latent_heads) return MLA_ERR_SHAPE;       // L | heads
+    if (d->rope_mode != MLA_ROPE_NONE) return MLA_ERR_UNSUPPORTED;  // partitioned latent has no RoPE
+  }
+  // Kernel limits.
+  if (d->d_v != d->d_nope) return MLA_ERR_UNSUPPORTED;
+  if (d->d_nope % 8) return MLA_ERR_UNSUPPORTED;
+  if (d->d_rope > 64) return MLA_ERR_UNSUPPORTED;
+  if (d->d_rope > 0 && (d->r_kv & 1)) return MLA_ERR_UNSUPPORTED;
+  if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT && (128 % d->d_nope)) return MLA_ERR_UNSUPPORTED;
+  int a, b;
+  if (!prefill_supported(is_bf16(d), dq_of(d), d->d_v, &a, &b)) return MLA_ERR_UNSUPPORTED;
+  if (d->rope_mode != MLA_ROPE_FULL_HALFSPLIT) {
+    int x, y, z;
+    if (!decode_supported(is_bf16(d), rblock(d), d->d_rope, d->n_heads / d->n_latent_heads, &x, &y, &z))
+      return MLA_ERR_UNSUPPORTED;
+  }
+  return MLA_OK;
+}
+
+size_t mla_workspace_bytes(const mla_dims* d, int op, int32_t batch, int32_t seq) {
+  if (mla_validate(d) != MLA_OK || batch <= 0 || seq < 0) return 0;
+  switch (op) {
+    case MLA_OP_CACHE_APPEND: return 0;
+    case MLA_OP_PREFILL: return seq > 0 ? prefill_layout(d, batch, seq, false).total : 0;
+    case MLA_OP_PREFILL_ATTENTION: return seq > 0 ? prefill_layout(d, batch, seq, true).total : 0;
+    case MLA_OP_DECODE:
+      if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) return 0;
+      return decode_layout(d, batch, seq, false).total;
+    case MLA_OP_DECODE_ATTENTION:
+      if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) return 0;
+      return decode_layout(d, batch, seq, true).total;
+    default: return 0;
+  }
+}
+
+mla_status mla_cache_append(const mla_dims* d, const mla_weights* w, const void* x, int32_t B,
+                            int32_t T, const int32_t* start_pos_dev, int32_t max_start,
+                            const mla_cache* cache, void* stream) {
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (!x || !start_pos_dev || B <= 0 || T <= 0 || max_start < 0) return MLA_ERR_INVALID_ARG;
+  if ((s = check_weights(d, w, false, false, false)) != MLA_OK) return s;
+  if ((s = check_cache(d, cache)) != MLA_OK) return s;
+  if (B > cache->max_batch || (long long)max_start + T > cache->max_seq) return MLA_ERR_CAPACITY;
+  return hip_status(run_latent(d, w, x, B, T, start_pos_dev, cache, nullptr, nullptr,
+                               static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_prefill_attention(const mla_dims* d, const mla_weights* w, const void* q,
+                                 int32_t B, int32_t S, const mla_cache* cache, void* o,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (!q || !o || B <= 0 || S <= 0 || !w || !w->w_uk || !w->w_uv) return MLA_ERR_INVALID_ARG;
+  if ((s = check_cache(d, cache)) != MLA_OK) return s;
+  if (B > cache->max_batch || S > cache->max_seq) return MLA_ERR_CAPACITY;
+  PrefillWs lay = prefill_layout(d, B, S, true);
+  if (!ws || ws_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* k = at(ws, lay.k);
+  void* v = at(ws, lay.v);
+  hipError_t e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  int dqp, dvp;
+  prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp);
+  PrefillParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.q = q;
+  pp.k = k;
+  pp.kr = cache->kr;
+  pp.kr_bstride = cache->max_seq;
+  pp.v = v;
+  pp.o = o;
+  pp.B = B;
+  pp.S = S;
+  pp.H = d->n_heads;
+  pp.dn = d->d_nope;
+  pp.d_rope = d->d_rope;
+  pp.dv = d->d_v;
+  pp.scale_log2 = softmax_scale(d) * kLog2e;
+  return hip_status(launch_prefill(pp, is_bf16(d), dqp, dvp, st));
+}
+
+mla_status mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t S,
+                       const mla_cache* cache, float* y, void* ws, size_t ws_bytes, void* stream) {
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (!x || !y || B <= 0 || S <= 0) return MLA_ERR_INVALID_ARG;
+  if ((s = check_weights(d, w, true, true, true)) != MLA_OK) return s;
+  if (cache) {
+    if ((s = check_cache(d, cache)) != MLA_OK) return s;
+    if (B > cache->max_batch || S > cache->max_seq) return MLA_ERR_CAPACITY;
+  }
+  PrefillWs lay = prefill_layout(d, B, S, false);
+  if (!ws || ws_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  void* q = at(ws, lay.q);
+  e = run_queries(d, w, x, B * S, S, nullptr, at(ws, lay.cq), q, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  void* lat = at(ws, lay.lat);
+  void* latr = at(ws, lay.latr);
+  e = run_latent(d, w, x, B, S, nullptr, cache, lat, latr, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  void* k = at(ws, lay.k);
+  void* v = at(ws, lay.v);
+  if (cache)
+    e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st);
+  else
+    e = run_kv_up(d, w, lat, false, 0, B, S, k, v, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  int dqp, dvp;
+  prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp);
+  PrefillParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.q = q;
+  pp.k = k;
+  pp.kr = cache ? cache->kr : latr;
+  pp.kr_bstride = cache ? cache->max_seq : S;
+  pp.v = v;
+  pp.o = at(ws, lay.o);
+  pp.B = B;
+  pp.S = S;
+  pp.H = d->n_heads;
+  pp.dn = d->d_nope;
+  pp.d_rope = d->d_rope;
+  pp.dv = d->d_v;
+  pp.scale_log2 = softmax_scale(d) * kLog2e;
+  e = launch_prefill(pp, is_bf16(d), dqp, dvp, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return hip_status(run_out_proj(d, w, pp.o, B * S, y, st));
+}
+
+mla_status mla_decode_attention(const mla_dims* d, const void* q_lat, const void* q_rope, int32_t B,
+                                const int32_t* ctx_len_dev, int32_t max_ctx, const mla_cache* cache,
+                                void* z, void* ws, size_t ws_bytes, void* stream) {
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) return MLA_ERR_UNSUPPORTED;
+  if (!q_lat || !z || !ctx_len_dev || B <= 0 || max_ctx < 0) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope > 0 && !q_rope) return MLA_ERR_INVALID_ARG;
+  if ((s = check_cache(d, cache)) != MLA_OK) return s;
+  if (B > cache->max_batch || (long long)max_ctx + 1 > cache->max_seq) return MLA_ERR_CAPACITY;
+  DecodeWs lay = decode_layout(d, B, max_ctx, true);
+  if (!ws || ws_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  DecodeParams p = decode_params(d, cache, ctx_len_dev, B, max_ctx, ws, lay);
+  p.q_lat = q_lat;
+  p.q_lat_hs = rblock(d);
+  p.q_rope = q_rope;
+  p.q_rope_hs = d->d_rope;
+  p.z = z;
+  SplitPlan sp = plan_decode(d, B, max_ctx);
+  return hip_status(launch_decode(p, is_bf16(d), sp.dl, sp.dr, sp.nw, static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B,
+                      const int32_t* ctx_len_dev, int32_t max_ctx, const mla_cache* cache, float* y,
+                      void* ws, size_t ws_bytes, void* stream) {
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) return MLA_ERR_UNSUPPORTED;
+  if (!x || !y || !ctx_len_dev || B <= 0 || max_ctx < 0) return MLA_ERR_INVALID_ARG;
+  if ((s = check_weights(d, w, true, true, true)) != MLA_OK) return s;
+  if ((s = check_cache(d, cache)) != MLA_OK) return s;
+  if (B > cache->max_batch || (long long)max_ctx + 1 > cache->max_seq) return MLA_ERR_CAPACITY;
+  DecodeWs lay = decode_layout(d, B, max_ctx, false);
+  if (!ws || ws_bytes < lay.total) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int H = d->n_heads, dq = dq_of(d), rb = rblock(d);
+  const size_t es = esize(d);
+  hipError_t e;
+  void* q = at(ws, lay.q);
+  // 1. queries of the new tokens, rotated at position ctx_len[b]
+  e = run_queries(d, w, x, B, 1, ctx_len_dev, at(ws, lay.cq), q, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 2. append the new latent / rotary key at row ctx_len[b]
+  e = run_latent(d, w, x, B, 1, ctx_len_dev, cache, nullptr, nullptr, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 3. absorbed query q_lat[b][h] = W_UK,h^T q_C[b][h]
+  void* qlat = at(ws, lay.qlat);
+  e = run_per_head(d, q, (long long)H * dq, dq, d->d_nope, w->w_uk, true, rb, qlat,
+                   (long long)H * rb, rb, B, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 4. split-context attention over the latent cache + combine
+  DecodeParams p = decode_params(d, cache, ctx_len_dev, B, max_ctx, ws, lay);
+  p.q_lat = qlat;
+  p.q_lat_hs = rb;
+  p.q_rope = d->d_rope > 0 ? atc(q, d->d_nope * es) : nullptr;
+  p.q_rope_hs = dq;
+  void* z = at(ws, lay.z);
+  p.z = z;
+  SplitPlan sp = plan_decode(d, B, max_ctx);
+  e = launch_decode(p, is_bf16(d), sp.dl, sp.dr, sp.nw, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 5. o[b][h] = W_UV,h z[b][h], then y = W_O o
+  void* o = at(ws, lay.o);
+  e = run_per_head(d, z, (long long)H * rb, rb, rb, w->w_uv, false, d->d_v, o,
+                   (long long)H * d->d_v, d->d_v, B, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return hip_status(run_out_proj(d, w, o, B, y, st));
+}
+
+}  // extern "C"

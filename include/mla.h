@@ -1,0 +1,200 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) multi-head latent attention library.
+ *
+ * The library computes one attention layer of multi-head latent attention (MLA):
+ * keys and values are jointly compressed into a low-rank latent c = W_DKV x, and only
+ * that latent (plus, for the decoupled form, one rotary key k_R shared by all heads)
+ * is cached.  Three families are supported, each as defined on one of the pages:
+ *
+ *   MLA_ROPE_DECOUPLED_INTERLEAVED -- bird-of-paradise/deepseek-mla ``src/mla.py``,
+ *       ``MultiHeadLatentAttention.forward``: query latent c_Q = W_DQ x,
+ *       q_C = W_UQ c_Q, q_R = RoPE(W_QR c_Q); cached c = W_DKV x and
+ *       k_R = RoPE(W_KR x); keys [W_UK c ; k_R], values W_UV c;
+ *       scale 1/sqrt(d_nope + d_rope).  RoPE pairs (2j, 2j+1) (``apply_rotary_emb``).
+ *   MLA_ROPE_FULL_HALFSPLIT -- frankenstein-transformer ``latent/mla_attn``,
+ *       ``MLAAttention.forward``: q = RoPE(W_Q x), k = RoPE(W_UK c), v = W_UV c,
+ *       scale 1/sqrt(d_nope).  RoPE pairs (j, j + d/2) (``_apply_rope``).
+ *   MLA_ROPE_NONE with n_latent_heads = L > 1 -- frankenstein-transformer
+ *       ``latent/mlra_attn``, ``MLRAAttention.forward``: the latent is L disjoint
+ *       blocks; query head h reads block g = h / (n_heads / L) through its own
+ *       block up-projections; q = W_Q x; no RoPE; scale 1/sqrt(d_nope).
+ *
+ * Every row computes causal softmax attention (query at position p sees keys at
+ * positions <= p), then y = W_O [o_1; ...; o_H].
+ *
+ * Conventions for every entry point:
+ *   - Weights are row-major [out_features][in_features] (torch.nn.Linear layout) in
+ *     the element type of dims->dtype.  MLRA up-projections w_uk / w_uv are L dense
+ *     blocks [n_heads*d_nope/L][r_kv/L] stored back to back.
+ *   - Activations x are row-major in dims->dtype; outputs y are float32.
+ *   - All pointers named *_dev or pointing at tensors are device pointers (hipMalloc
+ *     or torch CUDA tensors).  The caller owns every buffer; the library never
+ *     allocates, frees or keeps a pointer after returning.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous: no host synchronisation happens inside.
+ *   - Host-visible argument errors are reported before anything is launched; a
+ *     failed launch returns MLA_ERR_HIP.  Device-side lengths (start_pos_dev,
+ *     ctx_len_dev) are trusted to respect the host bounds passed beside them.
+ *   - Work on one workspace must not overlap in time (two streams using the same
+ *     workspace race).  Inputs, outputs, caches and workspaces must not alias.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad enum */
+  MLA_ERR_SHAPE = 2,         /* dimension rules of the pages violated (odd RoPE dim, L not dividing r_kv or n_heads) */
+  MLA_ERR_CAPACITY = 3,      /* batch or positions exceed the cache's max_batch / max_seq */
+  MLA_ERR_UNSUPPORTED = 4,   /* valid MLA, but outside what the kernels implement (listed per entry point) */
+  MLA_ERR_WORKSPACE = 5,     /* workspace pointer missing or smaller than mla_workspace_bytes() */
+  MLA_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+typedef enum {
+  MLA_ROPE_NONE = 0,
+  MLA_ROPE_DECOUPLED_INTERLEAVED = 1,
+  MLA_ROPE_FULL_HALFSPLIT = 2
+} mla_rope_mode;
+
+typedef enum {
+  MLA_OP_CACHE_APPEND = 0,
+  MLA_OP_PREFILL = 1,
+  MLA_OP_DECODE = 2,
+  MLA_OP_DECODE_ATTENTION = 3,
+  MLA_OP_PREFILL_ATTENTION = 4
+} mla_op;
+
+/* Layer dimensions.
+ *   d_model        input / output width
+ *   n_heads        H, query heads
+ *   d_nope         per-head query/key width of the decompressed part (head_dim)
+ *   d_v            per-head value width; must equal d_nope (all pages use one head_dim)
+ *   d_rope         decoupled rotary width (DECOUPLED only; 0 otherwise); even
+ *   r_kv           latent rank (total over all latent heads)
+ *   r_q            query latent rank; 0 = queries straight from x through w_q
+ *                  (and, for DECOUPLED, q_R through w_qr applied to x)
+ *   n_latent_heads L (1 = MLA); L > 1 requires MLA_ROPE_NONE, L | r_kv and L | n_heads
+ *   rope_mode      mla_rope_mode
+ *   dtype          mla_dtype of x, weights and cache
+ *   rope_base      RoPE base (the pages default to 10000)
+ *   softmax_scale  <= 0 selects the family default given above
+ */
+typedef struct {
+  int32_t d_model, n_heads, d_nope, d_v, d_rope, r_kv, r_q, n_latent_heads;
+  int32_t rope_mode, dtype;
+  float rope_base, softmax_scale;
+} mla_dims;
+
+/* Projection weights; a family leaves the matrices it does not use NULL.
+ *   w_dq [r_q][d_model]            w_uq [H*d_nope][r_q]        w_qr [H*d_rope][r_q or d_model]
+ *   w_q  [H*d_nope][d_model]       w_dkv [r_kv][d_model]       w_kr [d_rope][d_model]
+ *   w_uk, w_uv [H*d_nope][r_kv] (MLRA: [L][H*d_nope/L][r_kv/L])  w_o [d_model][H*d_v]   */
+typedef struct {
+  const void *w_dq, *w_uq, *w_qr, *w_q, *w_dkv, *w_kr, *w_uk, *w_uv, *w_o;
+} mla_weights;
+
+/* The latent cache (the only inference state; the DSV2 page's cache_kv / cache_rk).
+ *   ckv [max_batch][max_seq][r_kv]   latent rows, dtype of dims
+ *   kr  [max_batch][max_seq][d_rope] rotary keys, stored AFTER rotation at their
+ *       absolute position (NULL when d_rope == 0)
+ * Row t of sequence b holds token position t. */
+typedef struct {
+  void *ckv, *kr;
+  int32_t max_batch, max_seq;
+} mla_cache;
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_str(mla_status s);
+
+/* Checks dims against the pages' rules and the kernels' limits.
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_SHAPE or MLA_ERR_UNSUPPORTED.
+ * Kernel limits: d_nope <= 256 (FULL_HALFSPLIT: d_nope divides 128), d_rope <= 64,
+ * r_kv / L <= 512, n_heads / L <= 128 * 64.  Host only; no GPU needed. */
+mla_status mla_validate(const mla_dims* dims);
+
+/* Bytes of device workspace entry point `op` needs for `batch` sequences of
+ * `seq_or_max_ctx` tokens (prefill: S; decode: the largest ctx_len).  Returns 0 for
+ * invalid arguments and for ops that need none (MLA_OP_CACHE_APPEND).  Host only. */
+size_t mla_workspace_bytes(const mla_dims* dims, int op, int32_t batch, int32_t seq_or_max_ctx);
+
+/* Fused down-projection + RoPE + cache write ([DSV2 page] ``forward`` cached path:
+ * the current latent and rotary key are written at rows start_pos .. start_pos+T-1).
+ *   x              [B][T][d_model], tokens of sequence b at positions start_pos_dev[b]+t
+ *   start_pos_dev  int32 [B] device array; max_start >= every entry (host bound)
+ *   cache          rows start_pos[b] .. start_pos[b]+T-1 of sequence b are overwritten
+ *                  with c = W_DKV x and k_R = RoPE(W_KR x, position); nothing else changes.
+ * Errors: CAPACITY if B > max_batch or max_start + T > max_seq. */
+mla_status mla_cache_append(const mla_dims* dims, const mla_weights* w, const void* x,
+                            int32_t B, int32_t T, const int32_t* start_pos_dev, int32_t max_start,
+                            const mla_cache* cache, void* stream);
+
+/* Causal prefill of B sequences of S tokens at positions 0..S-1 (the pages'
+ * ``forward(x)``): explicit K/V up-projection from the latent, flash-style causal
+ * attention on bf16 MFMA (fp32 MFMA for MLA_DTYPE_F32), then W_O.
+ *   x      [B][S][d_model]
+ *   cache  optional (NULL allowed): rows 0..S-1 of each sequence are written
+ *   y      [B][S][d_model] float32, fully overwritten
+ * Errors: CAPACITY if a cache is given and B > max_batch or S > max_seq. */
+mla_status mla_prefill(const mla_dims* dims, const mla_weights* w, const void* x,
+                       int32_t B, int32_t S, const mla_cache* cache, float* y,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* One decode step: one new token per sequence, absorbed form.
+ * The new token of sequence b sits at position ctx_len_dev[b]: its latent and rotary key
+ * are appended at that row, then it attends over rows 0..ctx_len[b] (ctx_len[b]+1 keys,
+ * itself included) with W_UK folded into the query and W_UV applied to the
+ * attention-weighted latent sum.  The caller advances ctx_len; the library never does.
+ *   x            [B][d_model]
+ *   ctx_len_dev  int32 [B] device array, 0 <= ctx_len[b] <= max_ctx
+ *   y            [B][d_model] float32
+ * Errors: CAPACITY if B > max_batch or max_ctx + 1 > max_seq;
+ *         UNSUPPORTED for MLA_ROPE_FULL_HALFSPLIT (RoPE on the decompressed key does not
+ *         commute with the absorption). */
+mla_status mla_decode(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B,
+                      const int32_t* ctx_len_dev, int32_t max_ctx, const mla_cache* cache,
+                      float* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* The attention core of one decode step over the latent cache (split-context kernel
+ * plus log-sum-exp combine), for absorbed queries that the caller already formed.
+ * Head h (latent block g = h / (H/L), width rb = r_kv/L) computes
+ *   s_j = scale * (q_lat[b][h] . ckv[b][j][g*rb : (g+1)*rb] + q_rope[b][h] . kr[b][j]),
+ *   z[b][h] = sum_j softmax_j(s) ckv[b][j][g*rb : (g+1)*rb],   j = 0 .. ctx_len[b]
+ * where scale is dims->softmax_scale or the family default.
+ *   q_lat   [B][H][rb]      dtype of dims (unscaled W_UK,h^T q_C,h)
+ *   q_rope  [B][H][d_rope]  dtype of dims (rotated; NULL when d_rope == 0)
+ *   z       [B][H][rb]      dtype of dims, fully overwritten
+ * The cache rows 0..ctx_len[b] must already hold the latents (this call writes nothing
+ * to the cache).  Errors as mla_decode. */
+mla_status mla_decode_attention(const mla_dims* dims, const void* q_lat, const void* q_rope,
+                                int32_t B, const int32_t* ctx_len_dev, int32_t max_ctx,
+                                const mla_cache* cache, void* z,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/* The attention core of prefill: explicit K/V up-projection of the cached latent rows
+ * 0..S-1 ([DSV2 page] ``forward``: UK_proj / UV_proj of C_KV) and flash-style causal
+ * attention over them.
+ *   q       [B][S][H][d_nope + d_rope] dtype of dims: per head the decompressed query
+ *           followed by its rotated decoupled part (FULL_HALFSPLIT: the rotated query)
+ *   cache   rows 0..S-1 hold the latent (and rotated k_R)
+ *   w       uses w_uk and w_uv only
+ *   o       [B][S][H][d_v] dtype of dims, fully overwritten (softmax-weighted values)
+ * Errors: CAPACITY if B > max_batch or S > max_seq. */
+mla_status mla_prefill_attention(const mla_dims* dims, const mla_weights* w, const void* q,
+                                 int32_t B, int32_t S, const mla_cache* cache, void* o,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

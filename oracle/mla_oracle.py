@@ -306,6 +306,23 @@ def decode(x_seq: np.ndarray, W: Dict[str, np.ndarray], d: Dims) -> np.ndarray:
     return forward(x_seq, W, d, q_rows=[S - 1])[0]
 
 
+def latent_attention(q_lat: np.ndarray, q_rope: Optional[np.ndarray], lat: np.ndarray,
+                     kr: Optional[np.ndarray], scale: float) -> np.ndarray:
+    """Attention of one query per head over latent rows, without up-projection.
+
+    q_lat [H, r] and q_rope [H, d_rope] (or None) against latent rows lat [n, r] and
+    rotated keys kr [n, d_rope]: s_j = scale (q_lat . lat_j + q_rope . kr_j); returns
+    z [H, r] = sum_j softmax_j(s) lat_j.  All n rows are visible (the query is the last
+    token, so causality admits every cached row).
+    """
+    q_lat = np.asarray(q_lat, dtype=F64)
+    lat = np.asarray(lat, dtype=F64)
+    s = scale * (q_lat @ lat.T)                                # [H, n]
+    if q_rope is not None:
+        s = s + scale * (np.asarray(q_rope, dtype=F64) @ np.asarray(kr, dtype=F64).T)
+    return softmax_last(s) @ lat
+
+
 def absorbed_decode(x_seq: np.ndarray, W: Dict[str, np.ndarray], d: Dims) -> np.ndarray:
     """The same decode step computed over the latent itself (W_UK folded into the
     query, W_UV applied after the attention-weighted latent sum).
@@ -322,29 +339,43 @@ def absorbed_decode(x_seq: np.ndarray, W: Dict[str, np.ndarray], d: Dims) -> np.
     c, kr = latent_rows(x_seq, W, d, pos)
     q = _queries(x_seq[S - 1:], W, d, pos[S - 1:])[0]        # [H, dq]
     H, dn = d.n_heads, d.d_nope
-    tau = d.scale()
-    z_heads = []
+    o = np.empty((H, d.d_v), dtype=F64)
     for h in range(H):
-        if d.family == FAMILY_MLRA:
-            L = d.n_latent_heads
-            hpg, sr = H // L, d.r_kv // L
-            g, hi = h // hpg, h % hpg
-            wuk = _w(W, "w_uk")[g][hi * dn:(hi + 1) * dn]      # [dn, sr]
-            wuv = _w(W, "w_uv")[g][hi * dn:(hi + 1) * dn]
-            lat = c[:, g * sr:(g + 1) * sr]
-            s = tau * (lat @ (wuk.T @ q[h, :dn]))
-        else:
-            wuk = _w(W, "w_uk")[h * dn:(h + 1) * dn]           # [dn, r_kv]
-            wuv = _w(W, "w_uv")[h * dn:(h + 1) * dn]
-            lat = c
-            s = tau * (lat @ (wuk.T @ q[h, :dn]))
-            if kr is not None:
-                s = s + tau * (kr @ q[h, dn:])
-        p = softmax_last(s)
-        z = p @ lat
-        z_heads.append(wuv @ z)
-    o = np.stack(z_heads)[None]                                # [1, H, dv]
-    return _output(o, W)[0]
+        wuk, wuv, lat = head_up_projections(W, d, h, c)
+        q_lat = (wuk.T @ q[h, :dn])[None]
+        q_rope = q[h, dn:][None] if kr is not None else None
+        z = latent_attention(q_lat, q_rope, lat, kr, d.scale())[0]
+        o[h] = wuv @ z
+    return _output(o[None], W)[0]
+
+
+def head_up_projections(W: Dict[str, np.ndarray], d: Dims, h: int, c: np.ndarray):
+    """(W_UK rows of head h [dn, rb], W_UV rows of head h [dv, rb], latent block [n, rb]).
+
+    MLA: rows h*dn .. of the full up-projections and the whole latent.  MLRA: the rows of
+    head h inside its block g = h // (H/L) and latent columns g*rb .. (g+1)*rb.
+    """
+    dn = d.d_nope
+    if d.family == FAMILY_MLRA:
+        L = d.n_latent_heads
+        hpg, sr = d.n_heads // L, d.r_kv // L
+        g, hi = h // hpg, h % hpg
+        return (_w(W, "w_uk")[g][hi * dn:(hi + 1) * dn], _w(W, "w_uv")[g][hi * dn:(hi + 1) * dn],
+                np.asarray(c, dtype=F64)[:, g * sr:(g + 1) * sr])
+    return (_w(W, "w_uk")[h * dn:(h + 1) * dn], _w(W, "w_uv")[h * dn:(h + 1) * dn],
+            np.asarray(c, dtype=F64))
+
+
+def queries(x: np.ndarray, W: Dict[str, np.ndarray], d: Dims, pos: np.ndarray) -> np.ndarray:
+    """Per-head queries [n, H, d_nope + d_rope] of tokens x at positions pos."""
+    return _queries(x, W, d, np.asarray(pos))
+
+
+def keys_values(c: np.ndarray, kr: Optional[np.ndarray], W: Dict[str, np.ndarray], d: Dims,
+                pos: np.ndarray):
+    """Explicit per-head keys [n, H, dq] and values [n, H, dv] from latent rows."""
+    return _keys_values(np.asarray(c, dtype=F64), None if kr is None else np.asarray(kr, dtype=F64),
+                        W, d, np.asarray(pos))
 
 
 def prefill_batch(xs: Sequence[np.ndarray], W, d: Dims) -> np.ndarray:
@@ -355,6 +386,7 @@ def prefill_batch(xs: Sequence[np.ndarray], W, d: Dims) -> np.ndarray:
 __all__ = [
     "rope_inv_freq", "rope_interleaved", "rope_halfsplit", "softmax_last",
     "causal_attention", "Dims", "latent_rows", "forward", "forward_from_cache",
-    "decode", "absorbed_decode", "prefill_batch",
+    "decode", "absorbed_decode", "prefill_batch", "latent_attention", "head_up_projections",
+    "queries", "keys_values",
     "FAMILY_DECOUPLED", "FAMILY_FULLROPE", "FAMILY_MLRA",
 ]

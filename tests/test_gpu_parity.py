@@ -1,0 +1,242 @@
+"""GPU parity of the HIP kernels against the fp64 oracle, through the C ABI.
+
+Sizes are small enough for the oracle to finish in seconds but span several tiles and a
+ragged tail (query tiles of 128, key tiles of 64, decode tiles of 32 tokens and context
+splits).  Tolerances: fp32 rel-L2 <= 1e-5; bf16-in / fp32-accumulate rel-L2 <= 1e-2 and
+max-abs <= 3e-2 (whole tensor).
+"""
+import numpy as np
+import pytest
+
+import mla_synth as S
+from oracle import mla_oracle as O
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 3.0   # canary value of untouched cache rows (exact in bf16)
+
+# Scaled cases of the five workloads (same families and per-head shapes).
+TINY = S.CONFIGS["tiny_fp32"]
+SMALL = S.CONFIGS["small_lm"].replace(batch=2, seq=200)
+DSV2 = S.CONFIGS["dsv2_decode"].replace(d_model=512, batch=3, seq=1000)   # reduced d_model
+DSV2_P = S.CONFIGS["dsv2_prefill"].replace(d_model=512, batch=2, seq=300)
+MLRA = S.CONFIGS["mlra_decode"].replace(d_model=512, batch=4, ctx_lo=0, ctx_hi=0)
+TINY_BF16_MLRA = S.MLAConfig("mlra_tiny", S.FAMILY_MLRA, "decode", 2, 40, d_model=64, n_heads=8,
+                             d_nope=16, d_rope=0, r_kv=32, r_q=0, n_latent_heads=4, seed=77)
+
+
+@pytest.fixture(scope="module")
+def gu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_util
+    return gpu_util
+
+
+_layers = {}
+
+
+def layer(gu, cfg):
+    key = cfg
+    if key not in _layers:
+        _layers[key] = gu.Layer(cfg)
+    return _layers[key]
+
+
+def _dims(cfg):
+    return O.Dims.from_cfg(cfg)
+
+
+# ---------------------------------------------------------------------------
+# mla_cache_append: fused down-projection + RoPE + cache write
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [TINY, SMALL, DSV2, MLRA], ids=lambda c: c.name)
+def test_cache_append(gu, cfg):
+    gu.say(f"[append] {cfg.name} seed={cfg.seed}")
+    lay = layer(gu, cfg)
+    B, T, max_seq = 3, 37, 96
+    starts = [0, 5, 59]
+    ckv, kr = lay.new_cache(B, max_seq, fill=SENTINEL)
+    xs = [S.make_x(cfg, b, starts[b] + T)[starts[b]:] for b in range(B)]
+    x = gu.to_dev(np.stack(xs), cfg)
+    lay.append(x, starts, lay.cache_view(ckv, kr, 0, B))
+    torch.cuda.synchronize()
+    ckv_h, kr_h = gu.to_host(ckv), (gu.to_host(kr) if kr is not None else None)
+    d = _dims(cfg)
+    for b in range(B):
+        pos = np.arange(starts[b], starts[b] + T)
+        c, krr = O.latent_rows(xs[b], lay.prob.weights, d, pos)
+        gu.assert_close(ckv_h[b, pos], c, cfg.dtype, f"latent rows b={b}")
+        if krr is not None:
+            gu.assert_close(kr_h[b, pos], krr, cfg.dtype, f"rotary key rows b={b}")
+        outside = np.ones(max_seq, bool)
+        outside[pos] = False
+        assert np.all(ckv_h[b, outside] == SENTINEL), "rows outside the append changed"
+        if kr_h is not None:
+            assert np.all(kr_h[b, outside] == SENTINEL)
+
+
+# ---------------------------------------------------------------------------
+# mla_prefill: causal prefill, explicit K/V up-projection
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [TINY, SMALL, DSV2_P, MLRA.replace(mode="prefill", batch=2, seq=150)],
+                         ids=lambda c: c.name)
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_prefill(gu, cfg, with_cache):
+    gu.say(f"[prefill] {cfg.name} B={cfg.batch} S={cfg.seq} cache={with_cache}")
+    lay = layer(gu, cfg)
+    B, S_ = cfg.batch, cfg.seq
+    xs = [S.make_x(cfg, b, S_) for b in range(B)]
+    x = gu.to_dev(np.stack(xs), cfg)
+    cache = None
+    if with_cache:
+        ckv, kr = lay.new_cache(B, S_ + 5, fill=SENTINEL)
+        cache = lay.cache_view(ckv, kr, 0, B)
+    y = gu.to_host(lay.prefill(x, cache))
+    d = _dims(cfg)
+    for b in range(B):
+        want = O.forward(xs[b], lay.prob.weights, d)
+        gu.assert_close(y[b], want, cfg.dtype, f"y b={b}")
+    if with_cache:
+        ckv_h = gu.to_host(ckv)
+        for b in range(B):
+            c, _ = O.latent_rows(xs[b], lay.prob.weights, d, np.arange(S_))
+            gu.assert_close(ckv_h[b, :S_], c, cfg.dtype, f"cache b={b}")
+            assert np.all(ckv_h[b, S_:] == SENTINEL)
+
+
+# ---------------------------------------------------------------------------
+# mla_decode: absorbed decode over the latent cache
+# ---------------------------------------------------------------------------
+DECODE_CASES = [
+    (DSV2, [37, 300, 1000]),          # one, several and many 32-token tiles; several splits
+    (MLRA, [5, 100, 700, 1500]),      # ragged, 4 latent heads
+    (TINY_BF16_MLRA, [0, 39]),        # empty context (attends to itself only)
+    (TINY.replace(mode="decode"), [0, 7]),
+]
+
+
+@pytest.mark.parametrize("cfg,ctx", DECODE_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_decode(gu, cfg, ctx):
+    gu.say(f"[decode] {cfg.name} ctx={ctx}")
+    lay = layer(gu, cfg)
+    B = len(ctx)
+    max_seq = max(ctx) + 9
+    ckv, kr = lay.new_cache(B, max_seq, fill=SENTINEL)
+    lay.fill_cache(ckv, kr, ctx)
+    seqs = [S.make_x(cfg, b, ctx[b] + 1) for b in range(B)]
+    x = gu.to_dev(np.stack([s[-1] for s in seqs]), cfg)
+    y = gu.to_host(lay.decode(x, ctx, lay.cache_view(ckv, kr, 0, B)))
+    d = _dims(cfg)
+    ckv_h = gu.to_host(ckv)
+    for b in range(B):
+        gu.assert_close(y[b], O.decode(seqs[b], lay.prob.weights, d), cfg.dtype, f"y b={b} ctx={ctx[b]}")
+        c, _ = O.latent_rows(seqs[b][-1:], lay.prob.weights, d, np.array([ctx[b]]))
+        gu.assert_close(ckv_h[b, ctx[b]], c[0], cfg.dtype, f"appended row b={b}")
+        assert np.all(ckv_h[b, ctx[b] + 1:] == SENTINEL)
+
+
+def test_decode_every_position_tiny(gu):
+    """fp32: decoding token t after a cache of t tokens equals prefill row t, for all t."""
+    cfg = TINY
+    lay = layer(gu, cfg)
+    d = _dims(cfg)
+    Sq = cfg.seq
+    xs = [S.make_x(cfg, b, Sq) for b in range(cfg.batch)]
+    want = [O.forward(xs[b], lay.prob.weights, d) for b in range(cfg.batch)]
+    ckv, kr = lay.new_cache(cfg.batch, Sq + 1, fill=SENTINEL)
+    for t in range(Sq):
+        gu.say(f"[decode-every] t={t}")
+        x = gu.to_dev(np.stack([xs[b][t] for b in range(cfg.batch)]), cfg)
+        y = gu.to_host(lay.decode(x, [t] * cfg.batch, lay.cache_view(ckv, kr, 0, cfg.batch)))
+        for b in range(cfg.batch):
+            gu.assert_close(y[b], want[b][t], cfg.dtype, f"row t={t} b={b}")
+
+
+def test_decode_is_deterministic(gu):
+    cfg, ctx = DSV2, [37, 300, 1000]
+    lay = layer(gu, cfg)
+    B = len(ctx)
+    ckv, kr = lay.new_cache(B, max(ctx) + 1)
+    lay.fill_cache(ckv, kr, ctx)
+    x = gu.to_dev(np.stack([S.make_x(cfg, b, ctx[b] + 1)[-1] for b in range(B)]), cfg)
+    cs = lay.cache_view(ckv, kr, 0, B)
+    y1 = lay.decode(x, ctx, cs).clone()
+    y2 = lay.decode(x, ctx, cs).clone()
+    assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------
+# Staged entry points with oracle-made inputs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,ctx", [(DSV2, [40, 513, 999]), (MLRA, [5, 1030])], ids=["dsv2", "mlra"])
+def test_decode_attention_entry(gu, cfg, ctx):
+    """mla_decode_attention on latent rows and absorbed queries made by the oracle."""
+    import head_latent_attention_dkv_amd as M
+    gu.say(f"[decode_attention] {cfg.name} ctx={ctx}")
+    lay = layer(gu, cfg)
+    d = _dims(cfg)
+    B, H, L = len(ctx), cfg.n_heads, cfg.n_latent_heads
+    rb = cfg.r_kv // L
+    max_seq = max(ctx) + 1
+    ckv_h = np.zeros((B, max_seq, cfg.r_kv), np.float32)
+    kr_h = np.zeros((B, max_seq, cfg.d_rope), np.float32) if cfg.d_rope else None
+    q_lat = np.zeros((B, H, rb), np.float32)
+    q_rope = np.zeros((B, H, cfg.d_rope), np.float32) if cfg.d_rope else None
+    want = np.zeros((B, H, rb))
+    rng = np.random.default_rng(5)
+    for b in range(B):
+        n = ctx[b] + 1
+        xs = S.make_x(cfg, b, n)
+        c, kr = O.latent_rows(xs, lay.prob.weights, d, np.arange(n))
+        ckv_h[b, :n] = S.round_bf16(c.astype(np.float32))
+        if kr is not None:
+            kr_h[b, :n] = S.round_bf16(kr.astype(np.float32))
+        q_lat[b] = S.round_bf16(rng.standard_normal((H, rb)).astype(np.float32) * 4)
+        if q_rope is not None:
+            q_rope[b] = S.round_bf16(rng.standard_normal((H, cfg.d_rope)).astype(np.float32) * 4)
+        for h in range(H):
+            g = h // (H // L)
+            lat = ckv_h[b, :n, g * rb:(g + 1) * rb]
+            want[b, h] = O.latent_attention(q_lat[b, h][None], None if q_rope is None else q_rope[b, h][None],
+                                            lat, None if kr_h is None else kr_h[b, :n], d.scale())[0]
+    ckv, kr = gu.to_dev(ckv_h, cfg), (gu.to_dev(kr_h, cfg) if kr_h is not None else None)
+    z = torch.empty((B, H, rb), dtype=gu.tdtype(cfg), device="cuda")
+    cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    ws, nbytes = lay.workspace(M.MLA_OP_DECODE_ATTENTION, B, max(ctx))
+    M.mla_decode_attention(lay.dims, gu.to_dev(q_lat, cfg), None if q_rope is None else gu.to_dev(q_rope, cfg),
+                           B, cl, max(ctx), M.cache_struct(ckv, kr, B, max_seq), z, ws, nbytes)
+    gu.assert_close(gu.to_host(z), want, cfg.dtype, "z")
+
+
+@pytest.mark.parametrize("cfg", [DSV2_P, SMALL], ids=lambda c: c.name)
+def test_prefill_attention_entry(gu, cfg):
+    """mla_prefill_attention on oracle queries and oracle latent rows."""
+    import head_latent_attention_dkv_amd as M
+    gu.say(f"[prefill_attention] {cfg.name}")
+    lay = layer(gu, cfg)
+    d = _dims(cfg)
+    B, S_, H = cfg.batch, cfg.seq, cfg.n_heads
+    dq = cfg.d_nope + cfg.d_rope
+    ckv_h = np.zeros((B, S_, cfg.r_kv), np.float32)
+    kr_h = np.zeros((B, S_, cfg.d_rope), np.float32) if cfg.d_rope else None
+    q_h = np.zeros((B, S_, H, dq), np.float32)
+    want = np.zeros((B, S_, H, cfg.d_v))
+    pos = np.arange(S_)
+    for b in range(B):
+        xs = S.make_x(cfg, b, S_)
+        c, kr = O.latent_rows(xs, lay.prob.weights, d, pos)
+        ckv_h[b] = S.round_bf16(c.astype(np.float32))
+        if kr is not None:
+            kr_h[b] = S.round_bf16(kr.astype(np.float32))
+        q_h[b] = S.round_bf16(O.queries(xs, lay.prob.weights, d, pos).astype(np.float32))
+        k, v = O.keys_values(ckv_h[b], None if kr_h is None else kr_h[b], lay.prob.weights, d, pos)
+        want[b] = O.causal_attention(q_h[b], k, v, d.scale(), pos, pos)
+    ckv, kr = gu.to_dev(ckv_h, cfg), (gu.to_dev(kr_h, cfg) if kr_h is not None else None)
+    o = torch.empty((B, S_, H, cfg.d_v), dtype=gu.tdtype(cfg), device="cuda")
+    ws, nbytes = lay.workspace(M.MLA_OP_PREFILL_ATTENTION, B, S_)
+    M.mla_prefill_attention(lay.dims, lay.ws_struct, gu.to_dev(q_h, cfg), B, S_, M.cache_struct(ckv, kr, B, S_),
+                            o, ws, nbytes)
+    gu.assert_close(gu.to_host(o), want, cfg.dtype, "o")
