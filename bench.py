@@ -1,0 +1,391 @@
+"""Benchmark of the MLA hot path on one MI355X.
+
+One "step" is one whole mla_decode call of the DeepSeek-V2-shaped decode workload
+(B=64 sequences, 4096 cached tokens + 1 new token each, H=128, latent 512 + rotary 64,
+query latent 1536, d_model 5120, absorbed form): append, query path, absorbed query,
+split-context latent attention + combine, W_UV and W_O.  `value` is the latent-cache
+bytes that step streams (sum over sequences of (ctx+1) * (512+64) * 2 B = 302.06 MB)
+divided by the measured step time.  The latent cache rotates between two copies
+(604 MB > the 256 MB Infinity Cache) so that every step reads it from HBM.
+
+The same run also measures (reported beside the headline, not folded into it):
+  * the dominant kernel unit -- mla_decode_attention (split-context attention over the
+    latent cache + combine) -- timed with HIP events on the stream it runs on, against
+    the 8 TB/s HBM roofline;
+  * the DeepSeek-V2-shaped causal prefill (B=4, S=4096): whole mla_prefill and the
+    attention core unit mla_prefill_attention (explicit K/V up-projection + flash
+    attention) against the 2.5 PFLOP/s bf16 MFMA peak;
+  * the MLRA decode (B=128, ragged contexts, 4 latent heads of rank 128);
+  * the small-LM prefill (B=8, S=1024);
+  * the fp64 CPU oracle on a bounded sample of the decode workload (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only PART]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import mla_synth as S  # noqa: E402
+
+METRIC = "MLA decode latent-cache GB/s + prefill TFLOP/s (1 MI355X, % roofline)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def host_threads():
+    return S.host_threads()
+
+
+# ---------------------------------------------------------------------------
+# Device setup helpers (allocation and copies only; all compute is in libmla)
+# ---------------------------------------------------------------------------
+class Dev:
+    def __init__(self, cfg):
+        import torch
+        import head_latent_attention_dkv_amd as M
+        self.torch, self.M = torch, M
+        self.cfg = cfg
+        self.prob = S.make_problem(cfg)
+        self.dims = M.dims_from_cfg(cfg)
+        self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.w = {k: self.up(v) for k, v in self.prob.weights.items()}
+        self.wst = M.weights_struct(self.w)
+
+    def up(self, a):
+        t = self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        return t.to("cuda").to(self.dt).contiguous()
+
+    def workspace(self, op, B, S_):
+        n = self.M.mla_workspace_bytes(self.dims, op, B, S_)
+        return self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda"), n
+
+    def new_cache(self, B, max_seq):
+        cfg, torch = self.cfg, self.torch
+        ckv = torch.zeros((B, max_seq, cfg.r_kv), dtype=self.dt, device="cuda")
+        kr = torch.zeros((B, max_seq, cfg.d_rope), dtype=self.dt, device="cuda") if cfg.d_rope else None
+        return ckv, kr
+
+    def fill(self, ckv, kr, lens, keep_last=True):
+        """Cache rows 0..lens[b]-1 from the seeded inputs; returns the new-token rows."""
+        from concurrent.futures import ThreadPoolExecutor
+        torch, M = self.torch, self.M
+        nt = host_threads()
+        last = np.zeros((len(lens), self.cfg.d_model), np.float32)
+        for i0 in range(0, len(lens), nt):
+            idx = list(range(i0, min(len(lens), i0 + nt)))
+            with ThreadPoolExecutor(nt) as ex:
+                xs = list(ex.map(lambda b: S.make_x(self.cfg, b, int(lens[b]) + 1), idx))
+            for b, x in zip(idx, xs):
+                last[b] = x[-1]
+                n = int(lens[b])
+                if n == 0:
+                    continue
+                xd = self.up(x[:n])[None]
+                sp = torch.zeros(1, dtype=torch.int32, device="cuda")
+                cs = M.cache_struct(ckv[b:b + 1], kr[b:b + 1] if kr is not None else None, 1, ckv.shape[1])
+                M.mla_cache_append(self.dims, self.wst, xd, 1, n, sp, 0, cs)
+            del xs
+        torch.cuda.synchronize()
+        return last
+
+
+def timed(torch, fn, steps, warmup):
+    """Average ms per call of fn(i) over `steps` calls after `warmup` calls (HIP events on
+    the current stream, synchronised on both sides)."""
+    if steps <= 0:
+        return float("nan")
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def src_digest(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "head_latent_attention_dkv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(name, digest):
+    """HBM bytes per launch measured by rocprofv3 counters for kernel unit `name`, if the
+    stored measurement was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{name}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("src_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None):
+    torch = __import__("torch")
+    d = Dev(cfg)
+    M = d.M
+    B = cfg.batch
+    ctx = [int(c) for c in d.prob.ctx_lens]
+    max_ctx = max(ctx)
+    max_seq = max_ctx + 8
+    log(f"[bench] {cfg.name}: filling latent cache ({sum(ctx)} tokens)")
+    caches = [d.new_cache(B, max_seq)]
+    last = d.fill(*caches[0], ctx)
+    for _ in range(copies - 1):
+        caches.append(tuple(t.clone() if t is not None else None for t in caches[0]))
+    cstructs = [M.cache_struct(ck, kr, B, max_seq) for ck, kr in caches]
+    x = d.up(last)
+    cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    y = torch.empty((B, cfg.d_model), dtype=torch.float32, device="cuda")
+    ws, nws = d.workspace(M.MLA_OP_DECODE, B, max_ctx)
+    cache_bytes = sum((c + 1) * (cfg.r_kv + cfg.d_rope) for c in ctx) * 2
+    weight_bytes = sum(v.size for v in d.prob.weights.values()) * 2
+
+    def step(i):
+        M.mla_decode(d.dims, d.wst, x, B, cl, max_ctx, cstructs[i % copies], y, ws, nws)
+
+    log(f"[bench] {cfg.name}: timing mla_decode")
+    ms = timed(torch, step, steps, warmup)
+
+    # dominant kernel unit: split-context latent attention + combine
+    H, L = cfg.n_heads, cfg.n_latent_heads
+    rb = cfg.r_kv // L
+    g = torch.Generator(device="cpu").manual_seed(cfg.seed)
+    q_lat = (torch.randn((B, H, rb), generator=g) * 0.6).to(d.dt).cuda()
+    q_rope = (torch.randn((B, H, cfg.d_rope), generator=g) * 0.6).to(d.dt).cuda() if cfg.d_rope else None
+    z = torch.empty((B, H, rb), dtype=d.dt, device="cuda")
+    wsa, nwsa = d.workspace(M.MLA_OP_DECODE_ATTENTION, B, max_ctx)
+
+    def att(i):
+        M.mla_decode_attention(d.dims, q_lat, q_rope, B, cl, max_ctx, cstructs[i % copies], z, wsa, nwsa)
+
+    log(f"[bench] {cfg.name}: timing mla_decode_attention")
+    ms_att = timed(torch, att, attention_steps or steps, warmup)
+    res = {
+        "workload": cfg.name, "batch": B, "ctx_total": int(sum(ctx)), "max_ctx": max_ctx,
+        "ms_per_call": ms, "cache_bytes": int(cache_bytes), "weight_bytes": int(weight_bytes),
+        "cache_GBps_call": cache_bytes / ms / 1e6,
+        "call_GBps_incl_weights": (cache_bytes + weight_bytes) / ms / 1e6,
+        "attention_ms": ms_att, "attention_GBps": cache_bytes / ms_att / 1e6,
+    }
+    del caches, cstructs
+    torch.cuda.empty_cache()
+    return res, d
+
+
+def bench_prefill(cfg, steps, warmup):
+    torch = __import__("torch")
+    d = Dev(cfg)
+    M = d.M
+    B, S_ = cfg.batch, cfg.seq
+    log(f"[bench] {cfg.name}: inputs")
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(host_threads()) as ex:
+        xs = list(ex.map(lambda b: S.make_x(cfg, b, S_), range(B)))
+    x = d.up(np.stack(xs))
+    del xs
+    ckv, kr = d.new_cache(B, S_)
+    cs = M.cache_struct(ckv, kr, B, S_)
+    y = torch.empty((B, S_, cfg.d_model), dtype=torch.float32, device="cuda")
+    ws, nws = d.workspace(M.MLA_OP_PREFILL, B, S_)
+
+    def call(i):
+        M.mla_prefill(d.dims, d.wst, x, B, S_, cs, y, ws, nws)
+
+    log(f"[bench] {cfg.name}: timing mla_prefill")
+    ms = timed(torch, call, steps, warmup)
+    H, dn, dr, dv = cfg.n_heads, cfg.d_nope, cfg.d_rope, cfg.d_v
+    g = torch.Generator(device="cpu").manual_seed(cfg.seed)
+    q = torch.randn((B, S_, H, dn + dr), generator=g).to(d.dt).cuda()
+    o = torch.empty((B, S_, H, dv), dtype=d.dt, device="cuda")
+    wsa, nwsa = d.workspace(M.MLA_OP_PREFILL_ATTENTION, B, S_)
+
+    def att(i):
+        M.mla_prefill_attention(d.dims, d.wst, q, B, S_, cs, o, wsa, nwsa)
+
+    log(f"[bench] {cfg.name}: timing mla_prefill_attention")
+    ms_att = timed(torch, att, steps, warmup)
+    core = 2.0 * B * H * (S_ * (S_ + 1) / 2) * (dn + dr + dv)
+    kvup = 2.0 * B * S_ * cfg.r_kv * H * (dn + dv) / cfg.n_latent_heads
+    w = d.prob.weights
+    proj = 2.0 * B * S_ * sum(v.size for k, v in w.items() if k not in ("w_uk", "w_uv"))
+    layer = core + kvup + proj
+    res = {
+        "workload": cfg.name, "batch": B, "seq": S_, "ms_per_call": ms,
+        "layer_flop": layer, "layer_TFLOPs": layer / ms / 1e9,
+        "attention_ms": ms_att, "attention_flop": core + kvup,
+        "attention_TFLOPs": (core + kvup) / ms_att / 1e9,
+    }
+    return res
+
+
+def cpu_baseline(cfg, budget_s=20.0, max_seqs=8):
+    """fp64 oracle on a bounded sample of the decode workload (whole sequences)."""
+    from oracle import mla_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"] or [0])
+    except Exception:  # pragma: no cover
+        cores = 0
+    prob = S.make_problem(cfg)
+    d = O.Dims.from_cfg(cfg)
+    done, t_tot, nbytes = 0, 0.0, 0
+    while done < max_seqs and (t_tot < budget_s or done == 0):
+        b = done
+        n = int(prob.ctx_lens[b]) + 1
+        x = S.make_x(cfg, b, n)
+        t0 = time.perf_counter()
+        O.decode(x, prob.weights, d)
+        t_tot += time.perf_counter() - t0
+        nbytes += n * (cfg.r_kv + cfg.d_rope) * 2
+        done += 1
+    return {"value": nbytes / t_tot / 1e9, "unit": "GB/s", "cores": int(cores or host_threads()),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences of {cfg.name} (fp64 numpy decode step with "
+                      f"explicit K/V up-projection), {t_tot:.1f} s; value = their latent-cache bytes / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all",
+                    choices=["all", "decode", "decode_attention", "prefill", "prefill_attention", "mlra",
+                             "small", "copy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import head_latent_attention_dkv_amd as M
+    M.lib()
+    torch.cuda.set_device(0)
+
+    if args.only == "copy":
+        # plain device copy of a known size (counter calibration for HBM traffic)
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        ms = timed(torch, lambda i: b.copy_(a), args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": n, "ms": ms, "GBps_read_plus_write": 2 * n / ms / 1e6}))
+        return
+    if args.only == "decode_attention":
+        r, _ = bench_decode(S.CONFIGS["dsv2_decode"], 0, 0, attention_steps=args.steps)
+        print(json.dumps(r))
+        return
+    if args.only == "prefill_attention":
+        print(json.dumps(bench_prefill(S.CONFIGS["dsv2_prefill"], args.steps, args.warmup)))
+        return
+
+    out = {}
+    if args.only in ("all", "decode"):
+        dec, _ = bench_decode(S.CONFIGS["dsv2_decode"], args.steps, args.warmup)
+        out["decode"] = dec
+    if args.only in ("all", "prefill"):
+        out["prefill"] = bench_prefill(S.CONFIGS["dsv2_prefill"], max(3, args.steps // 4), max(1, args.warmup // 2))
+    if args.only in ("all", "mlra"):
+        out["mlra"], _ = bench_decode(S.CONFIGS["mlra_decode"], args.steps, args.warmup)
+    if args.only in ("all", "small"):
+        out["small"] = bench_prefill(S.CONFIGS["small_lm"], args.steps, args.warmup)
+    if args.only != "all":
+        print(json.dumps(out))
+        return
+
+    dec = out["decode"]
+    dig_dec = src_digest("decode.hip", "common.h")
+    dig_pre = src_digest("prefill.hip", "gemm.hip", "common.h")
+    line = {
+        "metric": METRIC,
+        "value": dec["cache_GBps_call"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, bf16-rounded)",
+        "config": {
+            "workload": "DeepSeek-V2-shaped single-layer MLA decode, absorbed form: B=64, 4096 cached "
+                        "tokens + 1 new per sequence, H=128, d_nope=128, d_rope=64, r_kv=512, r_q=1536, "
+                        "d_model=5120; whole mla_decode call per step; latent cache rotated over 2 copies",
+            "global_batch": 64, "seq_len": 4097, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": "mla_decode_attention (split-context latent attention + combine)",
+            "bound": "hbm",
+            "achieved": dec["attention_GBps"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec["attention_GBps"] / HBM_PEAK_GBS,
+            "traffic": traffic_from_profiles("dsv2_decode_attention", dig_dec),
+            "algorithmic_bytes_per_launch": dec["cache_bytes"],
+            "ms_per_launch": dec["attention_ms"],
+        },
+        "decode_call": {"cache_GBps": dec["cache_GBps_call"], "GBps_incl_weights": dec["call_GBps_incl_weights"],
+                        "weight_bytes": dec["weight_bytes"]},
+    }
+    pre = out["prefill"]
+    line["prefill"] = {
+        "workload": "DeepSeek-V2-shaped MLA causal prefill B=4, S=4096 (dims as decode)",
+        "ms_per_call": pre["ms_per_call"], "layer_TFLOPs": pre["layer_TFLOPs"],
+        "roofline": {"kernel": "mla_prefill_attention (explicit K/V up-projection + flash causal attention)",
+                     "bound": "mfma", "achieved": pre["attention_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": pre["attention_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic_from_profiles("dsv2_prefill_attention", dig_pre),
+                     "algorithmic_flop_per_launch": pre["attention_flop"], "ms_per_launch": pre["attention_ms"]},
+    }
+    ml = out["mlra"]
+    line["mlra_decode"] = {
+        "workload": "MLRA decode B=128, ctx ~ U[512,16384], 4 latent heads x rank 128, H=16, d_model=2048",
+        "ms_per_call": ml["ms_per_call"], "cache_GBps_call": ml["cache_GBps_call"],
+        "roofline": {"kernel": "mla_decode_attention", "bound": "hbm", "achieved": ml["attention_GBps"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ml["attention_GBps"] / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_launch": ml["cache_bytes"], "ms_per_launch": ml["attention_ms"]},
+    }
+    sm = out["small"]
+    line["small_lm_prefill"] = {"workload": "small-LM MLA prefill B=8, S=1024, d_model=512, H=8, r_kv=256",
+                                "ms_per_call": sm["ms_per_call"], "layer_TFLOPs": sm["layer_TFLOPs"],
+                                "attention_TFLOPs": sm["attention_TFLOPs"]}
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(S.CONFIGS["dsv2_decode"])
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -242,14 +242,17 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   }
 }
 
+template <typename T, int DL>
+hipError_t launch_combine_impl(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((combine_kernel<T, DL>), dim3(p.H, p.B), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
 template <typename T, int DL, int DR, int NW>
 hipError_t launch_impl(const DecodeParams& p, hipStream_t s) {
   using C = DecodeCfg<T, DL, DR, NW>;
   dim3 grid(p.nsplit, p.L * p.head_tiles, p.B);
   hipLaunchKernelGGL((decode_kernel<T, DL, DR, NW>), grid, dim3(NW * 64), C::LDS, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<T, DL>), dim3(p.H, p.B), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -268,6 +271,17 @@ bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, i
   *dr_pad = d_rope == 0 ? 0 : (d_rope <= 16 ? 16 : 64);
   *nw = 1;
   return true;
+}
+
+hipError_t launch_combine(const DecodeParams& p, bool use_bf16, int dl, hipStream_t s) {
+  if (use_bf16) {
+    if (dl == 512) return launch_combine_impl<bf16, 512>(p, s);
+    if (dl == 128) return launch_combine_impl<bf16, 128>(p, s);
+  } else {
+    if (dl == 32) return launch_combine_impl<float, 32>(p, s);
+    if (dl == 128) return launch_combine_impl<float, 128>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeParams& p, bool use_bf16, int dl, int dr, int nw, hipStream_t s) {

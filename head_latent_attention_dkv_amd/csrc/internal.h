@@ -84,6 +84,13 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, bool use_bf16, int dl_pad, int dr_pad, int nw,
                          hipStream_t s);
 bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, int* dr_pad, int* nw);
+hipError_t launch_combine(const DecodeParams& p, bool use_bf16, int dl_pad, hipStream_t s);
+
+// bf16 fast path (direct-to-LDS staging, LDS transpose loads): shapes it serves, the
+// heads one workgroup covers, and the launch (split kernel only; combine separately).
+bool decode_fast_supported(const DecodeParams& p, int* variant);
+int decode_fast_head_tile(int variant);
+hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Flash-style causal prefill

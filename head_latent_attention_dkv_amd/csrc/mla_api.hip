@@ -49,10 +49,23 @@ float softmax_scale(const mla_dims* d) {
 }
 
 // Decode split plan: tokens per split (multiple of 32) and splits per (sequence, head).
+// The bf16 fast path covers MLA with a 512-wide latent (+ rotary 64) and MLRA with four
+// latent blocks of 128; it runs one 256-thread workgroup per CU (its LDS pipeline takes
+// most of the CU's 160 KB), so the plan aims at whole waves of 256 workgroups.
 struct SplitPlan {
   int chunk, nsplit, head_tiles, dl, dr, nw;
+  int fast_variant;   // -1: generic kernel
+  int fast_head_tiles;
   bool ok;
 };
+
+int fast_variant_for(const mla_dims* d) {
+  if (!is_bf16(d)) return -1;
+  const int L = d->n_latent_heads, hpb = d->n_heads / L;
+  if (L == 1 && d->r_kv == 512 && (d->d_rope == 64 || d->d_rope == 0)) return d->d_rope ? 0 : 1;
+  if (L == 4 && d->r_kv == 512 && d->d_rope == 0 && hpb <= 16) return 2;
+  return -1;
+}
 
 SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
   SplitPlan sp{};
@@ -60,17 +73,46 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
   sp.ok = decode_supported(is_bf16(d), rblock(d), d->d_rope, hpb, &sp.dl, &sp.dr, &sp.nw);
   if (!sp.ok) return sp;
   sp.head_tiles = cdiv(hpb, 32 * sp.nw);
-  const long long wgs = (long long)B * L * sp.head_tiles;
-  const int wg_per_cu = sp.nw == 4 ? 1 : 8;
+  sp.fast_variant = fast_variant_for(d);
   const int ntok = max_ctx + 1;
-  int ns = (int)((kCUs * wg_per_cu + wgs - 1) / wgs);
-  if (ns < 1) ns = 1;
-  int chunk = round_up(cdiv(ntok, ns), 32);
-  if (sp.nw == 1 && chunk > 1024) chunk = 1024;
+  int chunk;
+  if (sp.fast_variant >= 0) {
+    sp.fast_head_tiles = sp.fast_variant == 2 ? 1 : cdiv(hpb, 128);
+    const long long wgs = (long long)B * sp.fast_head_tiles;
+    int ns = (int)((kCUs + wgs - 1) / wgs);
+    chunk = round_up(cdiv(ntok, ns < 1 ? 1 : ns), 32);
+    if (sp.fast_variant == 2 && chunk > 512) chunk = 512;   // ragged contexts: many small splits
+  } else {
+    const long long wgs = (long long)B * L * sp.head_tiles;
+    const int wg_per_cu = sp.nw == 4 ? 1 : 8;
+    int ns = (int)((kCUs * wg_per_cu + wgs - 1) / wgs);
+    chunk = round_up(cdiv(ntok, ns < 1 ? 1 : ns), 32);
+    if (sp.nw == 1 && chunk > 1024) chunk = 1024;
+  }
   if (chunk < 32) chunk = 32;
   sp.chunk = chunk;
   sp.nsplit = cdiv(ntok, chunk);
   return sp;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Split kernel (fast path when shapes and alignment allow) followed by the combine.
+hipError_t run_decode_attention(const mla_dims* d, DecodeParams p, const SplitPlan& sp, hipStream_t st) {
+  int variant = -1;
+  const bool fast = sp.fast_variant >= 0 && decode_fast_supported(p, &variant) &&
+                    aligned16(p.q_lat) && (p.q_lat_hs % 8 == 0) && aligned16(p.ckv) &&
+                    (p.d_rope == 0 || (aligned16(p.q_rope) && p.q_rope_hs % 8 == 0 && aligned16(p.kr)));
+  hipError_t e;
+  if (fast) {
+    p.head_tiles = sp.fast_head_tiles;
+    e = launch_decode_fast(p, variant, st);
+  } else {
+    p.head_tiles = sp.head_tiles;
+    e = launch_decode(p, is_bf16(d), sp.dl, sp.dr, sp.nw, st);
+  }
+  if (e != hipSuccess) return e;
+  return launch_combine(p, is_bf16(d), sp.dl, st);
 }
 
 struct DecodeWs {
@@ -530,7 +572,7 @@ mla_status mla_decode_attention(const mla_dims* d, const void* q_lat, const void
   p.q_rope_hs = d->d_rope;
   p.z = z;
   SplitPlan sp = plan_decode(d, B, max_ctx);
-  return hip_status(launch_decode(p, is_bf16(d), sp.dl, sp.dr, sp.nw, static_cast<hipStream_t>(stream)));
+  return hip_status(run_decode_attention(d, p, sp, static_cast<hipStream_t>(stream)));
 }
 
 mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B,
@@ -570,7 +612,7 @@ mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, in
   void* z = at(ws, lay.z);
   p.z = z;
   SplitPlan sp = plan_decode(d, B, max_ctx);
-  e = launch_decode(p, is_bf16(d), sp.dl, sp.dr, sp.nw, st);
+  e = run_decode_attention(d, p, sp, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   // 5. o[b][h] = W_UV,h z[b][h], then y = W_O o
   void* o = at(ws, lay.o);
