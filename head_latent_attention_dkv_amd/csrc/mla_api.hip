@@ -62,7 +62,7 @@ struct SplitPlan {
 int fast_variant_for(const mla_dims* d) {
   if (!is_bf16(d)) return -1;
   const int L = d->n_latent_heads, hpb = d->n_heads / L;
-  if (L == 1 && d->r_kv == 512 && (d->d_rope == 64 || d->d_rope == 0)) return d->d_rope ? 0 : 1;
+  if (L == 1 && d->r_kv == 512 && (d->d_rope == 64 || d->d_rope == 0)) return d->d_rope ? 3 : 4;
   if (L == 4 && d->r_kv == 512 && d->d_rope == 0 && hpb <= 16) return 2;
   return -1;
 }

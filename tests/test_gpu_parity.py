@@ -240,3 +240,37 @@ def test_prefill_attention_entry(gu, cfg):
     M.mla_prefill_attention(lay.dims, lay.ws_struct, gu.to_dev(q_h, cfg), B, S_, M.cache_struct(ckv, kr, B, S_),
                             o, ws, nbytes)
     gu.assert_close(gu.to_host(o), want, cfg.dtype, "o")
+
+
+@pytest.mark.parametrize("spike_at", [[3, 450, 990], [0, 700, 31]], ids=["late", "early"])
+def test_decode_attention_score_spikes(gu, spike_at):
+    """Scores that jump far above the first tile's maximum (exercises the exact-maximum
+    re-stream): one cache row per sequence is aligned with the absorbed query."""
+    import head_latent_attention_dkv_amd as M
+    cfg = DSV2
+    lay = layer(gu, cfg)
+    d = _dims(cfg)
+    ctx = [40, 513, 999]
+    B, H, rb = len(ctx), cfg.n_heads, cfg.r_kv
+    max_seq = max(ctx) + 1
+    rng = np.random.default_rng(11)
+    u = S.round_bf16(rng.standard_normal(rb).astype(np.float32))
+    ckv_h = S.round_bf16(rng.standard_normal((B, max_seq, rb)).astype(np.float32))
+    kr_h = S.round_bf16(rng.standard_normal((B, max_seq, cfg.d_rope)).astype(np.float32))
+    for b in range(B):
+        ckv_h[b, spike_at[b]] = S.round_bf16(2.0 * u)
+    q_lat = np.broadcast_to(u, (B, H, rb)).astype(np.float32).copy()
+    q_rope = S.round_bf16(rng.standard_normal((B, H, cfg.d_rope)).astype(np.float32))
+    want = np.zeros((B, H, rb))
+    for b in range(B):
+        n = ctx[b] + 1
+        for h in range(H):
+            want[b, h] = O.latent_attention(q_lat[b, h][None], q_rope[b, h][None], ckv_h[b, :n], kr_h[b, :n],
+                                            d.scale())[0]
+    ckv, kr = gu.to_dev(ckv_h, cfg), gu.to_dev(kr_h, cfg)
+    z = torch.empty((B, H, rb), dtype=gu.tdtype(cfg), device="cuda")
+    cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    ws, nbytes = lay.workspace(M.MLA_OP_DECODE_ATTENTION, B, max(ctx))
+    M.mla_decode_attention(lay.dims, gu.to_dev(q_lat, cfg), gu.to_dev(q_rope, cfg), B, cl, max(ctx),
+                           M.cache_struct(ckv, kr, B, max_seq), z, ws, nbytes)
+    gu.assert_close(gu.to_host(z), want, cfg.dtype, f"z spikes at {spike_at}")
