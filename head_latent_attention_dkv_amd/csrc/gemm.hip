@@ -14,6 +14,7 @@
 // the 16 rows of one fragment read on distinct LDS banks); the next stage's global loads
 // are issued before the current stage's MFMAs.
 #include "common.h"
+#include "gemm_epilogue.h"
 #include "internal.h"
 
 namespace mla {
@@ -191,51 +192,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
       }
   __syncthreads();
 
-  for (int e = tid; e < BM * BN; e += 256) {
-    int r = e / BN, c = e - r * BN;
-    int m = m0 + r, n = n0 + c;
-    if (m >= p.M || n >= N) continue;
-    int s = (n < p.seg[0].n) ? 0 : 1;
-    const GemmSeg& sg = p.seg[s];
-    int nn = n - (s ? p.seg[0].n : 0);
-    float v = Cs[r * LDC + c];
-    int b = m / p.rows_per_batch;
-    int t = m - b * p.rows_per_batch;
-    if (sg.rope != ROPE_OFF) {
-      int pos = (p.pos0 ? p.pos0[b] : 0) + t;
-      int hh = nn % sg.rope_d;
-      float sn, cs;
-      if (sg.rope == ROPE_INTERLEAVED) {
-        int j = hh >> 1;
-        rope_sincos(pos, p.rope.hi[j], p.rope.lo[j], &sn, &cs);
-        if ((hh & 1) == 0) {
-          float o = Cs[r * LDC + c + 1];
-          v = v * cs - o * sn;
-        } else {
-          float o = Cs[r * LDC + c - 1];
-          v = o * sn + v * cs;
-        }
-      } else {
-        int half = sg.rope_d >> 1;
-        int j = hh % half;
-        rope_sincos(pos, p.rope.hi[j], p.rope.lo[j], &sn, &cs);
-        if (hh < half) {
-          float o = Cs[r * LDC + c + half];
-          v = v * cs - o * sn;
-        } else {
-          float o = Cs[r * LDC + c - half];
-          v = o * sn + v * cs;
-        }
-      }
-    }
-    long long oc = sg.out_hw ? (long long)(nn / sg.out_hw) * sg.out_hs + (nn % sg.out_hw) : nn;
-    oc += o_goff;
-    long long orow = sg.out_cache ? (long long)b * p.out_bstride + (p.pos0 ? p.pos0[b] : 0) + t : m;
-    if (sg.out_f32)
-      reinterpret_cast<float*>(sg.out)[orow * sg.out_ld + oc] = v;
-    else
-      reinterpret_cast<T*>(sg.out)[orow * sg.out_ld + oc] = from_f32<T>(v);
-  }
+  epilogue_block<T>(p, Cs, LDC, m0, BM, n0, BN, o_goff, tid, 256);
 }
 
 template <typename T, int BM, int BN>
@@ -259,6 +216,7 @@ hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream
   for (int i = 0; i < p.nseg; ++i)
     if (p.seg[i].rope == ROPE_HALFSPLIT && p.seg[i].rope_d > max_rope_d) max_rope_d = p.seg[i].rope_d;
   if (!use_bf16) return launch_tile<float, 64, 64>(p, groups, s);
+  if (skinny_supported(p, groups)) return launch_skinny(p, groups, s);
   bool big = (long long)cdiv(p.M, 128) * cdiv(N, 128) * groups >= 512;
   if (big || max_rope_d > 64) return launch_tile<bf16, 128, 128>(p, groups, s);
   return launch_tile<bf16, 64, 64>(p, groups, s);

@@ -55,9 +55,20 @@ struct GemmParams {
   long long o_goff[2];      // added to every segment's output column start
   int w_kmajor;
   RopeTable rope;
+  // split-K partial sums for few-row products: workspace supplied by the caller (may be
+  // NULL: then the product runs unsplit); splits / kchunk are set by the launcher
+  float* part;
+  size_t part_bytes;
+  int splits, kchunk;
 };
 
 hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream_t s);
+
+// Few-row (M <= 128) weight-streaming path used by launch_gemm when its layout allows.
+bool skinny_supported(const GemmParams& p, int groups);
+hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s);
+// workspace bytes launch_skinny uses for split-K partials of an M x N x K product
+size_t skinny_ws_bytes(int M, int N, int K, int groups);
 
 // ---------------------------------------------------------------------------
 // Split-context decode over the latent cache + log-sum-exp combine

@@ -116,8 +116,23 @@ hipError_t run_decode_attention(const mla_dims* d, DecodeParams p, const SplitPl
 }
 
 struct DecodeWs {
-  size_t cq, q, qlat, z, o, part_z, part_ml, total;
+  size_t cq, q, qlat, z, o, gsplit, gsplit_bytes, part_z, part_ml, total;
 };
+
+// Split-K partial sums of the few-row projections of one decode step (largest of them).
+size_t decode_gemm_split_bytes(const mla_dims* d, int B) {
+  const bool dec = d->rope_mode == MLA_ROPE_DECOUPLED_INTERLEAVED;
+  const int H = d->n_heads;
+  const int src_w = (dec && d->r_q > 0) ? d->r_q : d->d_model;
+  size_t m = 0;
+  auto take = [&](size_t v) { m = v > m ? v : m; };
+  if (dec && d->r_q > 0) take(skinny_ws_bytes(B, d->r_q, d->d_model, 1));
+  take(skinny_ws_bytes(B, H * d->d_nope + (dec ? H * d->d_rope : 0), src_w, 1));
+  take(skinny_ws_bytes(B, d->r_kv + d->d_rope, d->d_model, 1));
+  take(skinny_ws_bytes(B, d->d_v, rblock(d), H));
+  take(skinny_ws_bytes(B, d->d_model, H * d->d_v, 1));
+  return m;
+}
 
 DecodeWs decode_layout(const mla_dims* d, int B, int max_ctx, bool attention_only) {
   DecodeWs w{};
@@ -132,6 +147,8 @@ DecodeWs decode_layout(const mla_dims* d, int B, int max_ctx, bool attention_onl
     w.qlat = take((size_t)B * H * rb * es);
     w.z = take((size_t)B * H * rb * es);
     w.o = take((size_t)B * H * d->d_v * es);
+    w.gsplit_bytes = decode_gemm_split_bytes(d, B);
+    w.gsplit = take(w.gsplit_bytes);
   }
   w.part_z = take((size_t)B * H * sp.nsplit * sp.dl * sizeof(float));
   w.part_ml = take((size_t)B * H * sp.nsplit * 2 * sizeof(float));
@@ -213,14 +230,25 @@ GemmSeg plain_seg(const void* w, long long w_ld, int n, void* out, long long out
 }
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+// Scratch for split-K partial sums of few-row projections (none: products run unsplit).
+struct SplitWs {
+  float* part = nullptr;
+  size_t bytes = 0;
+};
+void use_split(GemmParams& p, const SplitWs& sw) {
+  p.part = sw.part;
+  p.part_bytes = sw.bytes;
+}
 const char* atc(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
 
 // c = W_DKV x and k_R = RoPE(W_KR x) for `rows` rows, written to cache rows (b, pos0[b]+t)
 // or, without a cache, to plain row-major buffers.
 hipError_t run_latent(const mla_dims* d, const mla_weights* w, const void* x, int B, int T,
                       const int32_t* pos0, const mla_cache* cache, void* lat, void* latr,
-                      hipStream_t st) {
+                      hipStream_t st, const SplitWs& sw = SplitWs()) {
   GemmParams p = gemm_base(d);
+  use_split(p, sw);
   p.a = x;
   p.a_ld = d->d_model;
   p.M = B * T;
@@ -246,7 +274,8 @@ hipError_t run_latent(const mla_dims* d, const mla_weights* w, const void* x, in
 
 // Queries q[rows][H][d_nope + d_rope] from x (and the query latent when r_q > 0).
 hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, int rows,
-                       int rows_per_batch, const int32_t* pos0, void* cq, void* q, hipStream_t st) {
+                       int rows_per_batch, const int32_t* pos0, void* cq, void* q, hipStream_t st,
+                       const SplitWs& sw = SplitWs()) {
   const bool bf = is_bf16(d);
   const int H = d->n_heads, dq = dq_of(d);
   const size_t es = esize(d);
@@ -256,6 +285,7 @@ hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, i
   hipError_t e;
   if (dec && d->r_q > 0) {
     GemmParams p = gemm_base(d);
+    use_split(p, sw);
     p.a = x;
     p.a_ld = d->d_model;
     p.M = rows;
@@ -267,6 +297,7 @@ hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, i
     src_w = d->r_q;
   }
   GemmParams p = gemm_base(d);
+  use_split(p, sw);
   p.a = src;
   p.a_ld = src_w;
   p.M = rows;
@@ -328,10 +359,11 @@ hipError_t run_kv_up(const mla_dims* d, const mla_weights* w, const void* lat, b
 // the head's rows of a (block) up-projection, read k-major (absorb) or [out][in] (W_UV).
 hipError_t run_per_head(const mla_dims* d, const void* a, long long a_ld, long long a_head,
                         int K, const void* wmat, bool kmajor, int n, void* out, long long out_ld,
-                        long long out_head, int B, hipStream_t st) {
+                        long long out_head, int B, hipStream_t st, const SplitWs& sw = SplitWs()) {
   const int H = d->n_heads, L = d->n_latent_heads, hpb = H / L, rb = rblock(d);
   const int sub_out = H * d->d_nope / L;
   GemmParams p = gemm_base(d);
+  use_split(p, sw);
   p.a = a;
   p.a_ld = a_ld;
   p.M = B;
@@ -349,8 +381,9 @@ hipError_t run_per_head(const mla_dims* d, const void* a, long long a_ld, long l
 }
 
 hipError_t run_out_proj(const mla_dims* d, const mla_weights* w, const void* o, int rows, float* y,
-                        hipStream_t st) {
+                        hipStream_t st, const SplitWs& sw = SplitWs()) {
   GemmParams p = gemm_base(d);
+  use_split(p, sw);
   const int hv = d->n_heads * d->d_v;
   p.a = o;
   p.a_ld = hv;
@@ -591,12 +624,15 @@ mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, in
   const int H = d->n_heads, dq = dq_of(d), rb = rblock(d);
   const size_t es = esize(d);
   hipError_t e;
+  SplitWs sw;
+  sw.part = reinterpret_cast<float*>(at(ws, lay.gsplit));
+  sw.bytes = lay.gsplit_bytes;
   void* q = at(ws, lay.q);
   // 1. queries of the new tokens, rotated at position ctx_len[b]
-  e = run_queries(d, w, x, B, 1, ctx_len_dev, at(ws, lay.cq), q, st);
+  e = run_queries(d, w, x, B, 1, ctx_len_dev, at(ws, lay.cq), q, st, sw);
   if (e != hipSuccess) return MLA_ERR_HIP;
   // 2. append the new latent / rotary key at row ctx_len[b]
-  e = run_latent(d, w, x, B, 1, ctx_len_dev, cache, nullptr, nullptr, st);
+  e = run_latent(d, w, x, B, 1, ctx_len_dev, cache, nullptr, nullptr, st, sw);
   if (e != hipSuccess) return MLA_ERR_HIP;
   // 3. absorbed query q_lat[b][h] = W_UK,h^T q_C[b][h]
   void* qlat = at(ws, lay.qlat);
@@ -617,9 +653,9 @@ mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, in
   // 5. o[b][h] = W_UV,h z[b][h], then y = W_O o
   void* o = at(ws, lay.o);
   e = run_per_head(d, z, (long long)H * rb, rb, rb, w->w_uv, false, d->d_v, o,
-                   (long long)H * d->d_v, d->d_v, B, st);
+                   (long long)H * d->d_v, d->d_v, B, st, sw);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  return hip_status(run_out_proj(d, w, o, B, y, st));
+  return hip_status(run_out_proj(d, w, o, B, y, st, sw));
 }
 
 }  // extern "C"

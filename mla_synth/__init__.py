@@ -17,8 +17,10 @@ Recipe (every workload):
   * Ragged context lengths (if any) are drawn next from the same rng:
         rng.integers(lo, hi, batch, endpoint=True).
   * Token activations of sequence b come from a child generator
-    PCG64([seed, b]) as x[t, :] ~ N(0, 1), t = 0, 1, ... so that any sequence can
-    be regenerated on its own (the oracle streams sequence by sequence).
+    PCG64([seed, b + 1]) as x[t, :] ~ N(0, 1), t = 0, 1, ... so that any sequence can
+    be regenerated on its own (the oracle streams sequence by sequence).  The key is
+    b + 1, not b: numpy's SeedSequence zero-pads its entropy, so [seed, 0] would replay
+    the weight stream PCG64(seed) and sequence 0 would be scaled copies of weight rows.
   * bf16 workloads round x and every weight to bf16 with round-to-nearest-even
     before either side sees them; both sides consume the identical values.
 """
@@ -184,7 +186,7 @@ def make_problem(cfg: MLAConfig) -> Problem:
 
 def make_x(cfg: MLAConfig, b: int, n_tokens: int) -> np.ndarray:
     """Activations of sequence b, tokens 0..n_tokens-1 (prefixes are stable)."""
-    rng = np.random.Generator(np.random.PCG64([cfg.seed, b]))
+    rng = np.random.Generator(np.random.PCG64([cfg.seed, b + 1]))
     return _finish(rng.standard_normal((n_tokens, cfg.d_model), dtype=np.float32), cfg.dtype)
 
 

@@ -465,3 +465,20 @@ def test_synthetic_inputs_are_seeded_and_scaled():
     m = S.make_problem(S.CONFIGS["mlra_decode"])
     assert m.ctx_lens.min() >= 512 and m.ctx_lens.max() <= 16384 and len(m.ctx_lens) == 128
     assert m.weights["w_uk"].shape == (4, 512, 128)
+
+
+def test_activations_are_independent_of_the_weights():
+    """No sequence's activation stream may replay the weight stream (numpy's SeedSequence
+    zero-pads its entropy, so a key [seed, 0] would equal [seed])."""
+    cfg = S.CONFIGS["mlra_decode"].replace(dtype="f32")
+    w0 = np.random.Generator(np.random.PCG64(cfg.seed)).standard_normal(4096, dtype=np.float32)
+    for b in (0, 1, 2):
+        x = S.make_x(cfg, b, 2).reshape(-1)
+        assert not np.allclose(x, w0[:x.size])
+        assert abs(np.corrcoef(x, w0[:x.size])[0, 1]) < 0.1
+    # latents of sequence 0 stay at the N(0, 1) scale (a replayed weight row would give
+    # c_i = sqrt(d_model) |W_DKV,i|^2 ~ 45 for the rows that align with W_DKV)
+    p = S.make_problem(cfg)
+    x = S.make_x(cfg, 0, 2600)
+    c = x @ p.weights["w_dkv"].T
+    assert np.abs(c).max() < 8.0
