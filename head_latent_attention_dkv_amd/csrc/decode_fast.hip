@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace mla {
 
@@ -30,29 +31,12 @@ constexpr float kRestartGap = 64.0f;       // log2 units: p <= 2^64 keeps bf16 /
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
-// 16-byte global -> LDS copy per lane (lane l writes lds_addr + 16 l).  Issued as inline
-// assembly so the compiler does not drain all outstanding copies (vmcnt(0)) before every
-// LDS read it cannot disambiguate; completion is tracked explicitly with wait_vmcnt<>.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
-}
-
 // Stage layout (per 32-token tile):
 //   latent region: 32 rows x 1024 B (64 chunks of 16 B).  Logical chunk c of token row t
 //     sits at physical chunk c ^ bitrev4(t & 15) (XOR inside aligned groups of 16), so
 //     the 16 rows of a score-operand read and the 4 rows x 32 B of a transpose read fall
 //     on distinct LDS banks.
 //   rotary region: 32 rows x 128 B (8 chunks), chunk c of row t at c ^ ((t >> 1) & 7).
-__device__ __forceinline__ int bitrev4(int x) {
-  return ((x & 1) << 3) | ((x & 2) << 1) | ((x & 4) >> 1) | ((x & 8) >> 3);
-}
-
 template <int VL, int VR, int NW, int NSTAGE>
 struct FastCfg {
   static constexpr int LAT_BYTES = TT * 1024;

@@ -14,6 +14,7 @@
 #include "common.h"
 #include "gemm_epilogue.h"
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace mla {
 
@@ -21,7 +22,7 @@ namespace {
 
 constexpr int kCols = 64;           // output columns per block
 constexpr int kLdc = kCols + 4;     // LDS row stride (floats)
-constexpr int kTargetBlocks = 256;  // one block per compute unit
+constexpr int kTargetBlocks = 512;  // two blocks per compute unit
 
 struct Goff {
   long long a, w, o;
@@ -44,7 +45,8 @@ template <int CB, int U>
 __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
   __shared__ float Cs[32 * CB * kLdc];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform k schedule
   const int col = lane & 31, half = lane >> 5;
   const int n0 = blockIdx.x * kCols;
   const int split = blockIdx.y;
@@ -77,23 +79,57 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16{};
 
-  for (int kb = k_begin + 16 * wave; kb < k_end; kb += 64 * U) {
-    Frag<bf16> fw[U][2], fx[U][CB];
+  // Two register buffers of U k-steps per wave (a trip covers 64 U elements of K for the
+  // block): the loads of the next trip are in flight while the MFMAs of the current one
+  // run.  Whole pairs of trips run unpredicated; a remainder (K not a multiple of the
+  // pair) runs trip by trip with predicated loads.
+  Frag<bf16> fw[2][U][2], fx[2][U][CB];
+  auto load = [&](int buf, int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = kb + 64 * u;
-      const bool ok = k < k_end;   // k_end - k is a multiple of 16
+      const int k = kb + 16 * wave + 64 * u;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) fw[u][rb] = ok ? frag_load<bf16>(wrow[rb] + k) : frag_zero<bf16>();
+      for (int rb = 0; rb < 2; ++rb) fw[buf][u][rb] = frag_load<bf16>(wrow[rb] + k);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) fx[u][cb] = ok ? frag_load<bf16>(xrow[cb] + k) : frag_zero<bf16>();
+      for (int cb = 0; cb < CB; ++cb) fx[buf][u][cb] = frag_load<bf16>(xrow[cb] + k);
     }
+  };
+  auto mma = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mma32(fw[u][rb], fx[u][cb], acc[rb][cb]);
+        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mma32(fw[buf][u][rb], fx[buf][u][cb], acc[rb][cb]);
+  };
+  constexpr int TRIP = 64 * U;
+  int kb = k_begin;
+  const int pairs = (k_end - k_begin) / (2 * TRIP);
+  if (pairs > 0) {
+    load(0, kb);
+    for (int i = 1; i < pairs; ++i) {
+      load(1, kb + TRIP);
+      mma(0);
+      load(0, kb + 2 * TRIP);
+      mma(1);
+      kb += 2 * TRIP;
+    }
+    load(1, kb + TRIP);
+    mma(0);
+    mma(1);
+    kb += 2 * TRIP;
+  }
+  for (; kb < k_end; kb += TRIP) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kb + 16 * wave + 64 * u;
+      const bool ok = k < k_end;   // k_end - k is a multiple of 16
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) fw[0][u][rb] = ok ? frag_load<bf16>(wrow[rb] + k) : frag_zero<bf16>();
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) fx[0][u][cb] = ok ? frag_load<bf16>(xrow[cb] + k) : frag_zero<bf16>();
+    }
+    mma(0);
   }
 
   // Sum the four waves' partial products in wave order.  Accumulator element e of lane l
@@ -124,54 +160,283 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
   }
 }
 
-// Sum of the slabs' partial blocks (slab order) followed by the shared epilogue.
+// Streaming variant.  Per stage of KT k-elements, the block's 128 weight rows and its
+// 32 CB activation rows move global -> LDS with 16-byte direct-to-LDS copies; each copy
+// instruction reads ROWS_PER_COPY whole row segments (coalesced, unlike the 32-row operand
+// pattern of the direct kernel), and NST stages are in flight.  Both operands are read
+// back in the 32x32x16 layout (lane -> row l%32, k-group l/32) through an XOR swizzle:
+// 16-byte chunk c of row r sits at c ^ (r mod CHUNKS), so the 8 rows of one LDS read
+// phase hit distinct banks.  Wave w takes k-steps KSW w .. KSW w + KSW - 1 of every
+// stage; the waves' partial sums meet in LDS as in the direct kernel.
+template <int CB, int ROWS_, int KT, int NST>
+struct StreamCfg {
+  static constexpr int ROWS = ROWS_;               // weight rows per block (32, 64 or 128)
+  static constexpr int RB = ROWS / 32;
+  static constexpr int XROWS = 32 * CB;            // activation rows per block
+  static constexpr int CHUNKS = KT / 8;            // 16-byte chunks per row segment
+  static constexpr int RPC = 64 / CHUNKS;          // rows per copy instruction
+  static constexpr int WPW = ROWS / RPC / 4;       // weight copies per wave per stage
+  static constexpr int XPW = XROWS / RPC / 4;      // activation copies per wave per stage
+  static constexpr int DPW = WPW + XPW;
+  static constexpr int KSW = KT / 64;              // k-steps per wave per stage
+  static constexpr int WBYTES = ROWS * KT * 2;
+  static constexpr int STAGE = (ROWS + XROWS) * KT * 2;
+  static constexpr int LDC = ROWS + 4;
+  static constexpr size_t LDS = (size_t)NST * STAGE > (size_t)XROWS * LDC * 4
+                                    ? (size_t)NST * STAGE : (size_t)XROWS * LDC * 4;
+  static_assert(KT == 64 || KT == 128, "stage width");
+  static_assert(XPW >= 1 && WPW >= 1 && NST >= 2 && NST <= 4, "pipeline shape");
+};
+
+template <int CB, int ROWS, int KT, int NST>
+__global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_kernel(GemmParams p) {
+  using C = StreamCfg<CB, ROWS, KT, NST>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int n0 = blockIdx.x * C::ROWS;
+  const int split = blockIdx.y;
+  const int z = blockIdx.z;
+  const Goff g = group_offsets(p, z);
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int k_begin = split * p.kchunk;
+  const int nst = (min(p.K, k_begin + p.kchunk) - k_begin) / KT;   // stages of this slab
+  const uint32_t lds0 = lds_addr_of(smem);
+  const int pc = lane % C::CHUNKS;                 // physical chunk this lane's copies fill
+
+  // copy sources (row t of a copy = copy index * RPC + lane / CHUNKS; the lane fetches the
+  // logical chunk that belongs at physical chunk pc)
+  const bf16* wsrc[C::WPW];
+#pragma unroll
+  for (int i = 0; i < C::WPW; ++i) {
+    const int t = (wave * C::WPW + i) * C::RPC + lane / C::CHUNKS;
+    const int n = min(n0 + t, N - 1);
+    const int s = (n < p.seg[0].n) ? 0 : 1;
+    const int nn = n - (s ? p.seg[0].n : 0);
+    wsrc[i] = reinterpret_cast<const bf16*>(p.seg[s].w) + g.w + (long long)nn * p.seg[s].w_ld + k_begin +
+              8 * (pc ^ (t % C::CHUNKS));
+  }
+  const bf16* xsrc[C::XPW];
+#pragma unroll
+  for (int i = 0; i < C::XPW; ++i) {
+    const int t = (wave * C::XPW + i) * C::RPC + lane / C::CHUNKS;
+    const int m = min(t, p.M - 1);
+    xsrc[i] = reinterpret_cast<const bf16*>(p.a) + a_row(p, m) * p.a_ld + g.a + k_begin + 8 * (pc ^ (t % C::CHUNKS));
+  }
+  // operand LDS offsets: row col (+ 32 per row block), logical chunk 2 (KSW w + j) + half
+  int off[C::KSW];
+#pragma unroll
+  for (int j = 0; j < C::KSW; ++j) {
+    const int c = 2 * (C::KSW * wave + j) + half;
+    off[j] = col * (KT * 2) + ((c ^ (col % C::CHUNKS)) << 4);
+  }
+
+  auto issue = [&](int st) {
+    const uint32_t base = lds0 + (st % NST) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::WPW; ++i)
+      dma16(wsrc[i] + st * KT, __builtin_amdgcn_readfirstlane(base + (wave * C::WPW + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < C::XPW; ++i)
+      dma16(xsrc[i] + st * KT, __builtin_amdgcn_readfirstlane(base + C::WBYTES + (wave * C::XPW + i) * 1024));
+  };
+
+  f32x16 acc[C::RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16{};
+
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < nst) issue(st);
+  for (int it = 0; it < nst; ++it) {
+    const int left = nst - 1 - it;                 // stages after this one
+    if (NST >= 4 && left >= 2) wait_vmcnt<2 * C::DPW>();
+    else if (NST >= 3 && left >= 1) wait_vmcnt<C::DPW>();
+    else wait_vmcnt<0>();
+    barrier_only();
+    if (it + NST - 1 < nst) issue(it + NST - 1);
+
+    const unsigned char* T = smem + (it % NST) * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::KSW; ++j) {
+      Frag<bf16> fx[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        fx[cb] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + C::WBYTES + off[j] + cb * 32 * KT * 2));
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        const Frag<bf16> fa = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off[j] + rb * 32 * KT * 2));
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mma32(fa, fx[cb], acc[rb][cb]);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Sum the four waves' partial products in wave order (Cs aliases the stages).
+  float* Cs = reinterpret_cast<float*>(smem);
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float* dst = &Cs[(32 * cb + col) * C::LDC + 32 * rb + 8 * (e >> 2) + 4 * half + (e & 3)];
+            *dst = (w == 0) ? acc[rb][cb][e] : *dst + acc[rb][cb][e];
+          }
+    }
+    __syncthreads();
+  }
+  if (p.splits == 1) {
+    epilogue_block<bf16>(p, Cs, C::LDC, 0, C::XROWS, n0, C::ROWS, g.o, tid, 256);
+    return;
+  }
+  float* part = p.part + ((long long)z * p.splits + split) * p.M * N;
+  for (int e = tid; e < C::XROWS * C::ROWS; e += 256) {
+    const int r = e / C::ROWS, c = e - r * C::ROWS;
+    if (r < p.M && n0 + c < N) part[(long long)r * N + n0 + c] = Cs[r * C::LDC + c];
+  }
+}
+
+// Sum of the slabs' partial blocks (slab order) followed by the shared epilogue; a
+// block covers kRedRows rows x 64 columns, one element per thread.
+constexpr int kRedRows = 4;
+
 __global__ void __launch_bounds__(256) split_reduce_kernel(GemmParams p) {
-  __shared__ float Cs[128 * kLdc];
+  __shared__ float Cs[kRedRows * kLdc];
   const int tid = threadIdx.x;
   const int n0 = blockIdx.x * kCols;
+  const int m0 = blockIdx.y * kRedRows;
   const int z = blockIdx.z;
   const Goff g = group_offsets(p, z);
   const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
   const long long plane = (long long)p.M * N;
-  const float* part = p.part + (long long)z * p.splits * plane;
-  for (int e = tid; e < p.M * kCols; e += 256) {
-    const int r = e / kCols, c = e - r * kCols;
-    float v = 0.f;
-    if (n0 + c < N) {
-      const float* src = part + (long long)r * N + n0 + c;
-      for (int s = 0; s < p.splits; ++s) v += src[s * plane];
+  const int r = tid / kCols, c = tid - r * kCols;
+  float v = 0.f;
+  if (m0 + r < p.M && n0 + c < N) {
+    const float* src = p.part + (long long)z * p.splits * plane + (long long)(m0 + r) * N + n0 + c;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= p.splits; s += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = src[(s + j) * plane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v += a[j];
     }
-    Cs[r * kLdc + c] = v;
+    for (; s < p.splits; ++s) v += src[s * plane];
   }
+  Cs[r * kLdc + c] = v;
   __syncthreads();
-  epilogue_block<bf16>(p, Cs, kLdc, 0, p.M, n0, kCols, g.o, tid, 256);
+  epilogue_block<bf16>(p, Cs, kLdc, m0, kRedRows, n0, kCols, g.o, tid, 256);
 }
 
 bool aligned16(const void* ptr, long long elem_off) {
   return ((reinterpret_cast<uintptr_t>(ptr) + 2 * elem_off) & 15) == 0;
 }
 
-void plan(int M, int N, int K, int groups, int* splits, int* kchunk) {
-  const int tiles = cdiv(N, kCols) * groups;
-  int s = kTargetBlocks / tiles;
+// Per-wave k-steps of one loop trip of the direct kernel for an M-row product.
+int trip_steps(int M) { return M <= 64 ? 4 : 2; }
+
+// Split-K plan: enough blocks for `slots` resident blocks, K slabs a multiple of `unit`,
+// and a bounded volume of fp32 partials (2 S M / K of the weight bytes).
+void plan_splits(int M, int N, int K, int groups, int cols, int slots, int unit, int* splits,
+                 int* kchunk) {
+  const int tiles = cdiv(N, cols) * groups;
+  int s = slots / tiles;
+  // partials up to half the weight bytes, or up to all of them when the tiles are few
+  const int by_bytes = tiles >= 64 ? K / (4 * M) : K / (2 * M);
+  const int by_unit = K / unit;
+  s = s > by_bytes ? by_bytes : s;
+  s = s > by_unit ? by_unit : s;
   s = s < 1 ? 1 : s;
-  const int max_s = K / 64 > 0 ? K / 64 : 1;
-  s = s > max_s ? max_s : s;
-  int kc = round_up(cdiv(K, s), 64);
+  int kc = round_up(cdiv(K, s), unit);
   s = cdiv(K, kc);
   if (s <= 1) kc = K;
   *splits = s;
   *kchunk = kc;
-  (void)M;
+}
+
+constexpr int kStreamKT = 64;
+constexpr int kMinBlocks = 384;          // enough resident blocks to keep HBM busy
+constexpr int kMinStagesPerSlab = 4;
+
+bool use_stream(int K) { return K % kStreamKT == 0; }
+
+struct SkinnyPlan {
+  int rows, splits, kchunk;
+};
+
+// Streaming plan: the weight-row tile (32, 64 or 128 rows) and the number of K slabs that
+// reach kMinBlocks blocks (or as many as the shape allows) with the least extra traffic:
+// fp32 partials written and read back (8 S M N bytes when S > 1) plus the activations
+// re-read from L2 by every row tile (weighted 1/2: they do not come from HBM).
+SkinnyPlan plan_stream(int M, int N, int K, int groups) {
+  SkinnyPlan best{128, 1, K};
+  double best_cost = 1e300;
+  int best_blocks = 0;
+  const int max_s = K / (kStreamKT * kMinStagesPerSlab) > 0 ? K / (kStreamKT * kMinStagesPerSlab) : 1;
+  for (int rows : {128, 64, 32}) {
+    if (M > 64 && rows == 128) continue;                 // accumulator budget
+    const long long tiles = (long long)cdiv(N, rows) * groups;
+    int s = (int)((kMinBlocks + tiles - 1) / tiles);
+    s = s < 1 ? 1 : (s > max_s ? max_s : s);
+    int kc = round_up(cdiv(K, s), kStreamKT);
+    s = cdiv(K, kc);
+    if (s <= 1) kc = K;
+    const long long blocks = tiles * s;
+    const double cost = (s > 1 ? 8.0 * s * M * N * groups : 0.0) + 0.5 * (double)tiles * M * K * 2;
+    const bool enough = blocks >= kMinBlocks;
+    const bool best_enough = best_blocks >= kMinBlocks;
+    if ((enough && !best_enough) || (enough == best_enough && (enough ? cost < best_cost : blocks > best_blocks))) {
+      best = {rows, s, kc};
+      best_cost = cost;
+      best_blocks = (int)blocks;
+    }
+  }
+  return best;
+}
+
+SkinnyPlan plan_direct(int M, int N, int K, int groups) {
+  int s, kc;
+  plan_splits(M, N, K, groups, kCols, kTargetBlocks, 2 * 64 * trip_steps(M), &s, &kc);
+  return {kCols, s, kc};
+}
+
+SkinnyPlan plan(int M, int N, int K, int groups) {
+  return use_stream(K) ? plan_stream(M, N, K, groups) : plan_direct(M, N, K, groups);
+}
+
+template <int CB, int ROWS>
+hipError_t launch_stream(const GemmParams& p, int groups, hipStream_t s) {
+  constexpr int NST = ROWS == 128 ? 3 : 4;
+  using C = StreamCfg<CB, ROWS, kStreamKT, NST>;
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  dim3 grid(cdiv(N, ROWS), p.splits, groups);
+  hipLaunchKernelGGL((skinny_stream_kernel<CB, ROWS, kStreamKT, NST>), grid, dim3(256), C::LDS, s, p);
+  return hipGetLastError();
+}
+
+template <int CB>
+hipError_t launch_stream_rows(const GemmParams& p, int rows, int groups, hipStream_t s) {
+  if (rows == 32) return launch_stream<CB, 32>(p, groups, s);
+  if (rows == 64) return launch_stream<CB, 64>(p, groups, s);
+  if constexpr (CB <= 2) return launch_stream<CB, 128>(p, groups, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 size_t skinny_ws_bytes(int M, int N, int K, int groups) {
   if (M <= 0 || M > 128 || N <= 0 || K <= 0 || groups <= 0) return 0;
-  int s, kc;
-  plan(M, N, K, groups, &s, &kc);
-  return s > 1 ? (size_t)s * groups * M * N * sizeof(float) : 0;
+  const SkinnyPlan pl = plan(M, N, K, groups);
+  return pl.splits > 1 ? (size_t)pl.splits * groups * M * N * sizeof(float) : 0;
 }
 
 bool skinny_supported(const GemmParams& p, int groups) {
@@ -194,25 +459,31 @@ bool skinny_supported(const GemmParams& p, int groups) {
 
 hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s) {
   const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
-  int splits, kc;
-  plan(p.M, N, p.K, groups, &splits, &kc);
-  const size_t need = splits > 1 ? (size_t)splits * groups * p.M * N * sizeof(float) : 0;
-  if (splits > 1 && (p.part == nullptr || p.part_bytes < need)) {
-    splits = 1;
-    kc = p.K;
+  SkinnyPlan pl = plan(p.M, N, p.K, groups);
+  const size_t need = pl.splits > 1 ? (size_t)pl.splits * groups * p.M * N * sizeof(float) : 0;
+  if (pl.splits > 1 && (p.part == nullptr || p.part_bytes < need)) {
+    pl.splits = 1;
+    pl.kchunk = p.K;
   }
-  p.splits = splits;
-  p.kchunk = kc;
-  dim3 grid(cdiv(N, kCols), splits, groups);
-  if (p.M <= 32)
-    hipLaunchKernelGGL((skinny_kernel<1, 8>), grid, dim3(256), 0, s, p);
-  else if (p.M <= 64)
-    hipLaunchKernelGGL((skinny_kernel<2, 8>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((skinny_kernel<4, 4>), grid, dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(split_reduce_kernel, dim3(cdiv(N, kCols), 1, groups), dim3(256), 0, s, p);
+  p.splits = pl.splits;
+  p.kchunk = pl.kchunk;
+  hipError_t e;
+  if (use_stream(p.K)) {
+    if (p.M <= 32) e = launch_stream_rows<1>(p, pl.rows, groups, s);
+    else if (p.M <= 64) e = launch_stream_rows<2>(p, pl.rows, groups, s);
+    else e = launch_stream_rows<4>(p, pl.rows, groups, s);
+  } else {
+    dim3 grid(cdiv(N, kCols), p.splits, groups);
+    if (p.M <= 32)
+      hipLaunchKernelGGL((skinny_kernel<1, 4>), grid, dim3(256), 0, s, p);
+    else if (p.M <= 64)
+      hipLaunchKernelGGL((skinny_kernel<2, 4>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((skinny_kernel<4, 2>), grid, dim3(256), 0, s, p);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(cdiv(N, kCols), cdiv(p.M, kRedRows), groups), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
