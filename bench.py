@@ -6,20 +6,26 @@ query latent 1536, d_model 5120, absorbed form): append, query path, absorbed qu
 split-context latent attention + combine, W_UV and W_O.  `value` is the latent-cache
 bytes that step streams (sum over sequences of (ctx+1) * (512+64) * 2 B = 302.06 MB)
 divided by the measured step time.  The latent cache rotates between two copies
-(604 MB > the 256 MB Infinity Cache) so that every step reads it from HBM.
+(604 MB > the 256 MB Infinity Cache) so that every step reads it from HBM.  All inputs
+are resident in device memory before the timed region; HIP events on the library's
+stream bracket the timed steps, with a device synchronisation on both sides.
 
-The same run also measures (reported beside the headline, not folded into it):
-  * the dominant kernel unit -- mla_decode_attention (split-context attention over the
-    latent cache + combine) -- timed with HIP events on the stream it runs on, against
-    the 8 TB/s HBM roofline;
-  * the DeepSeek-V2-shaped causal prefill (B=4, S=4096): whole mla_prefill and the
-    attention core unit mla_prefill_attention (explicit K/V up-projection + flash
-    attention) against the 2.5 PFLOP/s bf16 MFMA peak;
-  * the MLRA decode (B=128, ragged contexts, 4 latent heads of rank 128);
-  * the small-LM prefill (B=8, S=1024);
-  * the fp64 CPU oracle on a bounded sample of the decode workload (cpu_baseline).
+The JSON line also carries:
+  * roofline -- the step's dominant unit, mla_decode_attention (split-context attention
+    kernel + combine kernel), timed live with HIP events, against 8 TB/s HBM; `traffic`
+    is the HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by
+    a copy kernel of known size (profiles/dsv2_decode_attention_traffic.json, used only
+    while the kernel sources match the digest stored with it);
+  * decode_step -- the whole call against HBM including the 298 MB of weights it reads;
+  * prefill -- the DeepSeek-V2-shaped causal prefill (B=4, S=4096): whole mla_prefill and
+    the attention core unit mla_prefill_attention against the 2.5 PFLOP/s bf16 MFMA peak;
+  * mlra_decode -- the MLRA decode (B=128, ragged contexts, 4 latent heads of rank 128);
+  * small_lm_prefill -- the small-LM prefill (B=8, S=1024);
+  * cpu_baseline -- the fp64 CPU oracle timed on the host on a bounded sample of the
+    decode workload (whole sequences, ~15 s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only PART]
+       python bench.py --summarize DIR     (profile summaries from rocprofv3 output)
 """
 from __future__ import annotations
 
@@ -106,21 +112,36 @@ class Dev:
         return last
 
 
-def timed(torch, fn, steps, warmup):
-    """Average ms per call of fn(i) over `steps` calls after `warmup` calls (HIP events on
-    the current stream, synchronised on both sides)."""
+def timed(torch, fn, steps, warmup, stats=None):
+    """Average ms per call of fn(i) over `steps` calls after `warmup` calls.
+
+    HIP events on the current stream (the stream the library launches on) bracket the
+    timed calls, with a device synchronisation on both sides; an event between calls gives
+    each call's duration, whose median / p10 / p90 go into `stats` when it is a dict.
+    """
     if steps <= 0:
         return float("nan")
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
     for i in range(steps):
         fn(warmup + i)
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    if stats is not None:
+        stats.update({"median_ms": float(np.median(per)), "p10_ms": float(np.percentile(per, 10)),
+                      "p90_ms": float(np.percentile(per, 90))})
+    return ev[0].elapsed_time(ev[steps]) / steps
+
+
+# Sources of each measured kernel unit (a stored counter measurement is valid only for them).
+UNIT_SOURCES = {
+    "dsv2_decode_attention": ("decode_fast.hip", "decode.hip", "lds_dma.h", "common.h", "internal.h"),
+    "dsv2_prefill_attention": ("prefill.hip", "gemm.hip", "gemm_epilogue.h", "common.h", "internal.h"),
+}
 
 
 def src_digest(*files):
@@ -173,7 +194,8 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None):
         M.mla_decode(d.dims, d.wst, x, B, cl, max_ctx, cstructs[i % copies], y, ws, nws)
 
     log(f"[bench] {cfg.name}: timing mla_decode")
-    ms = timed(torch, step, steps, warmup)
+    st_call = {}
+    ms = timed(torch, step, steps, warmup, st_call)
 
     # dominant kernel unit: split-context latent attention + combine
     H, L = cfg.n_heads, cfg.n_latent_heads
@@ -188,8 +210,10 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None):
         M.mla_decode_attention(d.dims, q_lat, q_rope, B, cl, max_ctx, cstructs[i % copies], z, wsa, nwsa)
 
     log(f"[bench] {cfg.name}: timing mla_decode_attention")
-    ms_att = timed(torch, att, attention_steps or steps, warmup)
+    st_att = {}
+    ms_att = timed(torch, att, attention_steps or steps, warmup, st_att)
     res = {
+        "call_stats": st_call, "attention_stats": st_att,
         "workload": cfg.name, "batch": B, "ctx_total": int(sum(ctx)), "max_ctx": max_ctx,
         "ms_per_call": ms, "cache_bytes": int(cache_bytes), "weight_bytes": int(weight_bytes),
         "cache_GBps_call": cache_bytes / ms / 1e6,
@@ -221,7 +245,8 @@ def bench_prefill(cfg, steps, warmup):
         M.mla_prefill(d.dims, d.wst, x, B, S_, cs, y, ws, nws)
 
     log(f"[bench] {cfg.name}: timing mla_prefill")
-    ms = timed(torch, call, steps, warmup)
+    st_call = {}
+    ms = timed(torch, call, steps, warmup, st_call)
     H, dn, dr, dv = cfg.n_heads, cfg.d_nope, cfg.d_rope, cfg.d_v
     g = torch.Generator(device="cpu").manual_seed(cfg.seed)
     q = torch.randn((B, S_, H, dn + dr), generator=g).to(d.dt).cuda()
@@ -232,13 +257,15 @@ def bench_prefill(cfg, steps, warmup):
         M.mla_prefill_attention(d.dims, d.wst, q, B, S_, cs, o, wsa, nwsa)
 
     log(f"[bench] {cfg.name}: timing mla_prefill_attention")
-    ms_att = timed(torch, att, steps, warmup)
+    st_att = {}
+    ms_att = timed(torch, att, steps, warmup, st_att)
     core = 2.0 * B * H * (S_ * (S_ + 1) / 2) * (dn + dr + dv)
     kvup = 2.0 * B * S_ * cfg.r_kv * H * (dn + dv) / cfg.n_latent_heads
     w = d.prob.weights
     proj = 2.0 * B * S_ * sum(v.size for k, v in w.items() if k not in ("w_uk", "w_uv"))
     layer = core + kvup + proj
     res = {
+        "call_stats": st_call, "attention_stats": st_att,
         "workload": cfg.name, "batch": B, "seq": S_, "ms_per_call": ms,
         "layer_flop": layer, "layer_TFLOPs": layer / ms / 1e9,
         "attention_ms": ms_att, "attention_flop": core + kvup,
@@ -247,7 +274,7 @@ def bench_prefill(cfg, steps, warmup):
     return res
 
 
-def cpu_baseline(cfg, budget_s=20.0, max_seqs=8):
+def cpu_baseline(cfg, budget_s=15.0, max_seqs=64):
     """fp64 oracle on a bounded sample of the decode workload (whole sequences)."""
     from oracle import mla_oracle as O
     try:
@@ -274,6 +301,146 @@ def cpu_baseline(cfg, budget_s=20.0, max_seqs=8):
                       f"explicit K/V up-projection), {t_tot:.1f} s; value = their latent-cache bytes / time"}
 
 
+def summarize_profiles(d):
+    """Turn rocprofv3 CSV output under directory d into the committed summaries.
+
+    d/stats/*kernel_stats.csv        (--kernel-trace --stats of `bench.py --only decode`)
+    d/fetch/*counter_collection.csv  (--pmc FETCH_SIZE of `bench.py --only decode_attention`)
+    d/write/*counter_collection.csv  (--pmc WRITE_SIZE of the same)
+    d/copy_fetch, d/copy_write       (the same counters on `bench.py --only copy`)
+    Writes profiles/dsv2_decode_attention_traffic.json (bytes per launch of the unit,
+    scaled by the copy kernel's bytes-per-counter-KiB) for the current kernel sources.
+    """
+    import csv
+    import glob
+
+    def rows(sub, pattern):
+        out = []
+        for f in glob.glob(os.path.join(d, sub, "**", pattern), recursive=True):
+            with open(f) as fh:
+                out.extend(csv.DictReader(fh))
+        return out
+
+    def per_dispatch(sub, counter, match):
+        vals = {}
+        for r in rows(sub, "*counter_collection.csv"):
+            name = r.get("Kernel_Name", "")
+            if r.get("Counter_Name") != counter or not match(name):
+                continue
+            key = (name, r.get("Dispatch_Id"))
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    def unit_kib(sub, counter):
+        v = per_dispatch(sub, counter, lambda n: "decode_wide_kernel" in n or "combine_kernel" in n)
+        by = {}
+        for (name, _), x in v.items():
+            by.setdefault("combine" if "combine_kernel" in name else "split", []).append(x)
+        return {k: float(np.median(x)) for k, x in by.items()}
+
+    def copy_kib(sub, counter):
+        v = per_dispatch(sub, counter, lambda n: "copy" in n.lower() or "elementwise" in n.lower())
+        xs = [x for x in v.values() if x > 1e5]
+        return float(np.median(xs)) if xs else None
+
+    n_copy = 1 << 30
+    cf, cw = copy_kib("copy_fetch", "FETCH_SIZE"), copy_kib("copy_write", "WRITE_SIZE")
+    uf, uw = unit_kib("fetch", "FETCH_SIZE"), unit_kib("write", "WRITE_SIZE")
+    rec = {"unit": "mla_decode_attention: split kernel + combine kernel, DeepSeek-V2 decode shape",
+           "copy_bytes": n_copy, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_kib": uf, "write_kib": uw}
+    if cf and cw and uf and uw:
+        ff, fw = n_copy / (cf * 1024.0), n_copy / (cw * 1024.0)
+        rec["fetch_scale"], rec["write_scale"] = ff, fw
+        rec["hbm_read_bytes_per_launch"] = sum(uf.values()) * 1024.0 * ff
+        rec["hbm_write_bytes_per_launch"] = sum(uw.values()) * 1024.0 * fw
+        rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    rec["src_digest"] = src_digest(*UNIT_SOURCES["dsv2_decode_attention"])
+    out = os.path.join(PROFILES, "dsv2_decode_attention_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+    # kernel-time summary of `bench.py --only decode`
+    def short(name):
+        name = name.replace("mla::(anonymous namespace)::", "").replace("(mla::GemmParams)", "")
+        name = name.replace("(mla::DecodeParams)", "").replace("void ", "")
+        if name.startswith("_ZN3mla"):
+            name = {"_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi64ELi64EEEvNS_10GemmParamsE": "gemm_kernel<bf16,64,64>",
+                    "_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi128ELi128EEEvNS_10GemmParamsE":
+                        "gemm_kernel<bf16,128,128>",
+                    "_ZN3mla12_GLOBAL__N_114combine_kernelIDF16bLi512EEEvNS_12DecodeParamsE":
+                        "combine_kernel<bf16,512>"}.get(name, name)
+        return name[:70]
+
+    lines = ["# Kernel times: DeepSeek-V2-shaped decode step (B=64, 4096 cached tokens, H=128)", "",
+             "Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
+             "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/stats -o run -- "
+             "python3 bench.py --only decode --steps 20 --warmup 5",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- "
+             "python3 bench.py --only decode_attention --steps 3",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- "
+             "python3 bench.py --only decode_attention --steps 3",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/copy_fetch -o run -- "
+             "python3 bench.py --only copy --steps 3 --warmup 1",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/copy_write -o run -- "
+             "python3 bench.py --only copy --steps 3 --warmup 1",
+             "python3 bench.py --summarize <dir>",
+             "```", ""]
+    trace = rows("stats", "*kernel_trace.csv")
+    if trace:
+        trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+        # one timed mla_decode step.  Launch order inside the call: W_DQ (+reduce), queries
+        # (+reduce), latent (+reduce), absorbed query, attention, combine, W_UV (+reduce),
+        # W_O (+reduce); the first timing loop runs whole calls, so a step ends after the
+        # W_O product that follows a combine, and starts after the previous step's end.
+        names = [short(r["Kernel_Name"]) for r in trace]
+
+        def step_end(c):
+            j = c + 1                                   # W_UV
+            if j + 1 < len(names) and names[j + 1] == "split_reduce_kernel":
+                j += 1
+            j += 1                                      # W_O
+            if j + 1 < len(names) and names[j + 1] == "split_reduce_kernel":
+                j += 1
+            return j
+
+        combines = [i for i, n in enumerate(names) if n.startswith("combine_kernel")]
+        ends = [step_end(c) for c in combines if c + 2 < len(names) and names[c + 1].startswith("skinny")]
+        step = (ends[-2] + 1, ends[-1]) if len(ends) >= 2 else None
+        if step:
+            lines += ["One timed mla_decode step (kernel trace):", "",
+                      "| kernel | blocks (grid x) | µs |", "|---|---|---|"]
+            tot = 0.0
+            for r in trace[step[0]:step[1] + 1]:
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                tot += us
+                blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]) if "Grid_Size_X" in r else r.get("Grid_Size")
+                lines.append(f"| {short(r['Kernel_Name'])} | {blocks} | {us:.1f} |")
+            lines += [f"| **sum** | | **{tot:.1f}** |", ""]
+    stats = rows("stats", "*kernel_stats.csv")
+    if stats:
+        lines += ["rocprofv3 --stats (whole command, including the cache fill's append GEMMs):", "",
+                  "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+        for r in stats[:14]:
+            lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        lines.append("")
+    lines += ["HBM traffic of the mla_decode_attention unit (median per dispatch; FETCH_SIZE scaled by "
+              f"{rec.get('fetch_scale', float('nan')):.3f}, WRITE_SIZE by {rec.get('write_scale', float('nan')):.3f}, "
+              "the factors that make a 1 GiB device copy read and write 1 GiB):", "",
+              f"- split kernel: read {uf.get('split', 0) * 1024 * rec.get('fetch_scale', 0) / 1e6:.1f} MB, "
+              f"write {uw.get('split', 0) * 1024 * rec.get('write_scale', 0) / 1e6:.1f} MB",
+              f"- combine kernel: read {uf.get('combine', 0) * 1024 * rec.get('fetch_scale', 0) / 1e6:.1f} MB, "
+              f"write {uw.get('combine', 0) * 1024 * rec.get('write_scale', 0) / 1e6:.1f} MB",
+              f"- unit total: {rec.get('hbm_bytes_per_launch', 0) / 1e6:.1f} MB per launch vs 302.1 MB algorithmic "
+              "(latent + rotary cache)", "",
+              f"Kernel sources digest: {rec['src_digest']}", ""]
+    with open(os.path.join(PROFILES, "dsv2_decode_step_kernels.md"), "w") as fh:
+        fh.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,9 +450,13 @@ def main():
                     choices=["all", "decode", "decode_attention", "prefill", "prefill_attention", "mlra",
                              "small", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR", help="write profile summaries from rocprofv3 output in DIR")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: there is no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -316,7 +487,7 @@ def main():
     if args.only in ("all", "prefill"):
         out["prefill"] = bench_prefill(S.CONFIGS["dsv2_prefill"], max(3, args.steps // 4), max(1, args.warmup // 2))
     if args.only in ("all", "mlra"):
-        out["mlra"], _ = bench_decode(S.CONFIGS["mlra_decode"], args.steps, args.warmup)
+        out["mlra"], _ = bench_decode(S.CONFIGS["mlra_decode"], args.steps, args.warmup, copies=1)
     if args.only in ("all", "small"):
         out["small"] = bench_prefill(S.CONFIGS["small_lm"], args.steps, args.warmup)
     if args.only != "all":
@@ -324,8 +495,7 @@ def main():
         return
 
     dec = out["decode"]
-    dig_dec = src_digest("decode.hip", "common.h")
-    dig_pre = src_digest("prefill.hip", "gemm.hip", "common.h")
+    cfg3 = S.CONFIGS["dsv2_decode"]
     line = {
         "metric": METRIC,
         "value": dec["cache_GBps_call"],
@@ -338,43 +508,56 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, bf16-rounded)",
+        "data": "synthetic: seeded N(0,1) activations and N(0,1/fan_in) weights, bf16-rounded; "
+                "latent cache filled by the library from the seeded activations",
         "config": {
-            "workload": "DeepSeek-V2-shaped single-layer MLA decode, absorbed form: B=64, 4096 cached "
-                        "tokens + 1 new per sequence, H=128, d_nope=128, d_rope=64, r_kv=512, r_q=1536, "
-                        "d_model=5120; whole mla_decode call per step; latent cache rotated over 2 copies",
-            "global_batch": 64, "seq_len": 4097, "parallelism": "none (1 GPU)",
+            "workload": "DeepSeek-V2-shaped single-layer MLA decode, absorbed form: one mla_decode call "
+                        "(append, query path, absorbed query, split-context latent attention + combine, "
+                        "W_UV, W_O) for 64 sequences of 4096 cached tokens + 1 new token",
+            "batch": cfg3.batch, "cached_tokens": cfg3.seq, "n_heads": cfg3.n_heads, "d_nope": cfg3.d_nope,
+            "d_rope": cfg3.d_rope, "r_kv": cfg3.r_kv, "r_q": cfg3.r_q, "d_model": cfg3.d_model,
+            "value_definition": "latent-cache bytes streamed per step (302.06 MB) / step time",
+            "cache_copies": 2,
         },
         "roofline": {
-            "kernel": "mla_decode_attention (split-context latent attention + combine)",
+            "kernel": "mla_decode_attention unit: split-context latent attention kernel + combine kernel "
+                      "(the step's dominant kernels)",
             "bound": "hbm",
             "achieved": dec["attention_GBps"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": dec["attention_GBps"] / HBM_PEAK_GBS,
-            "traffic": traffic_from_profiles("dsv2_decode_attention", dig_dec),
+            "traffic": traffic_from_profiles("dsv2_decode_attention", src_digest(*UNIT_SOURCES["dsv2_decode_attention"])),
             "algorithmic_bytes_per_launch": dec["cache_bytes"],
             "ms_per_launch": dec["attention_ms"],
+            "timing": dec["attention_stats"],
         },
-        "decode_call": {"cache_GBps": dec["cache_GBps_call"], "GBps_incl_weights": dec["call_GBps_incl_weights"],
-                        "weight_bytes": dec["weight_bytes"]},
+        "decode_step": {"ms": dec["ms_per_call"], "timing": dec["call_stats"],
+                        "GBps_incl_weights": dec["call_GBps_incl_weights"], "weight_bytes": dec["weight_bytes"],
+                        "cache_bytes": dec["cache_bytes"],
+                        "frac_of_hbm_incl_weights": dec["call_GBps_incl_weights"] / HBM_PEAK_GBS,
+                        "tokens_per_s": cfg3.batch / (dec["ms_per_call"] * 1e-3)},
     }
     pre = out["prefill"]
     line["prefill"] = {
         "workload": "DeepSeek-V2-shaped MLA causal prefill B=4, S=4096 (dims as decode)",
-        "ms_per_call": pre["ms_per_call"], "layer_TFLOPs": pre["layer_TFLOPs"],
+        "ms_per_call": pre["ms_per_call"], "timing": pre["call_stats"], "layer_TFLOPs": pre["layer_TFLOPs"],
+        "tokens_per_s": 4 * 4096 / (pre["ms_per_call"] * 1e-3),
         "roofline": {"kernel": "mla_prefill_attention (explicit K/V up-projection + flash causal attention)",
                      "bound": "mfma", "achieved": pre["attention_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": pre["attention_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic_from_profiles("dsv2_prefill_attention", dig_pre),
-                     "algorithmic_flop_per_launch": pre["attention_flop"], "ms_per_launch": pre["attention_ms"]},
+                     "traffic": traffic_from_profiles("dsv2_prefill_attention",
+                                                      src_digest(*UNIT_SOURCES["dsv2_prefill_attention"])),
+                     "algorithmic_flop_per_launch": pre["attention_flop"], "ms_per_launch": pre["attention_ms"],
+                     "timing": pre["attention_stats"]},
     }
     ml = out["mlra"]
     line["mlra_decode"] = {
         "workload": "MLRA decode B=128, ctx ~ U[512,16384], 4 latent heads x rank 128, H=16, d_model=2048",
-        "ms_per_call": ml["ms_per_call"], "cache_GBps_call": ml["cache_GBps_call"],
-        "roofline": {"kernel": "mla_decode_attention", "bound": "hbm", "achieved": ml["attention_GBps"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ml["attention_GBps"] / HBM_PEAK_GBS,
+        "ms_per_call": ml["ms_per_call"], "cache_GBps_call": ml["cache_GBps_call"], "cache_bytes": ml["cache_bytes"],
+        "roofline": {"kernel": "mla_decode_attention unit (split kernel + combine)", "bound": "hbm",
+                     "achieved": ml["attention_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ml["attention_GBps"] / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": ml["cache_bytes"], "ms_per_launch": ml["attention_ms"]},
     }
     sm = out["small"]
