@@ -35,7 +35,23 @@ struct GemmSeg {
   int out_cache;        // 1: output row of (b, t) is b * out_bstride + pos0[b] + t
   int rope;             // RopeKind applied to this segment's columns before the store
   int rope_d;           // rotary width: pairs live inside [h*rope_d, (h+1)*rope_d)
+  // Output layout (row m = (b, t) with t = m % rows_per_batch; column c = head * out_hw + j):
+  //   OUT_ROWS        out[row * out_ld + column map above]
+  //   OUT_HEAD_MAJOR  out[((b * out_nh + head) * rows_per_batch + t) * out_hw + j]
+  //   OUT_HEAD_T16    out[((b * out_nh + head) * out_hw + j) * out_ld + perm16(t)], perm16
+  //                   swapping positions 4..7 and 8..11 inside every group of 16
+  int layout;
+  int out_nh;
 };
+
+enum OutLayout { OUT_ROWS = 0, OUT_HEAD_MAJOR = 1, OUT_HEAD_T16 = 2 };
+
+// Position of token t inside a group of 16 in the OUT_HEAD_T16 layout (an involution):
+// 0..3 -> 0..3, 4..7 -> 8..11, 8..11 -> 4..7, 12..15 -> 12..15.
+__host__ __device__ inline int perm16(int t) {
+  const int q = (t >> 2) & 3;
+  return (t & ~15) | (((q == 1) ? 2 : (q == 2) ? 1 : q) << 2) | (t & 3);
+}
 
 struct GemmParams {
   const void* a;            // A base
@@ -118,6 +134,20 @@ struct PrefillParams {
 };
 
 hipError_t launch_prefill(const PrefillParams& p, bool use_bf16, int dq_pad, int dv_pad, hipStream_t s);
+
+// bf16 flash prefill over head-major keys and transposed values (see prefill_fast.hip).
+struct FlashParams {
+  const void* q;            // [B][S][H][dn + d_rope]
+  const void* k;            // decompressed keys, head-major [B][H][S][dn]
+  const void* kr;           // rotated shared key rows: kr + (b*kr_bstride + t)*d_rope, or NULL
+  long long kr_bstride;
+  const void* vt;           // values, per head transposed [B][H][dv][S] (perm16 token order)
+  void* o;                  // [B][S][H][dv]
+  int B, S, H, dn, d_rope;
+  float scale_log2;
+};
+bool prefill_fast_supported(int dn, int d_rope, int dv, int S);
+hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s);
 bool prefill_supported(bool use_bf16, int dq, int dv, int* dq_pad, int* dv_pad);
 
 int device_cu_count();

@@ -326,8 +326,15 @@ hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, i
 }
 
 // Explicit keys / values from the latent rows 0..S-1 of each sequence.
+// Flash-prefill layouts: keys head-major [B][H][S][dn], values per head transposed
+// [B][H][dv][S] (perm16 token order).  Otherwise both [B*S][H][d].
+bool use_flash(const mla_dims* d, int S) {
+  return is_bf16(d) && prefill_fast_supported(d->d_nope, d->d_rope, d->d_v, S);
+}
+
 hipError_t run_kv_up(const mla_dims* d, const mla_weights* w, const void* lat, bool lat_cache,
-                     long long lat_bstride, int B, int S, void* k, void* v, hipStream_t st) {
+                     long long lat_bstride, int B, int S, void* k, void* v, hipStream_t st,
+                     bool flash_layout) {
   const bool bf = is_bf16(d);
   const int H = d->n_heads, L = d->n_latent_heads, rb = rblock(d);
   const int sub_out = H * d->d_nope / L;
@@ -342,6 +349,15 @@ hipError_t run_kv_up(const mla_dims* d, const mla_weights* w, const void* lat, b
   p.nseg = 2;
   p.seg[0] = plain_seg(w->w_uk, rb, sub_out, k, (long long)H * d->d_nope, false);
   p.seg[1] = plain_seg(w->w_uv, rb, sub_out, v, (long long)H * d->d_v, false);
+  if (flash_layout) {
+    p.seg[0].layout = OUT_HEAD_MAJOR;
+    p.seg[0].out_hw = d->d_nope;
+    p.seg[0].out_nh = H;
+    p.seg[1].layout = OUT_HEAD_T16;
+    p.seg[1].out_hw = d->d_v;
+    p.seg[1].out_nh = H;
+    p.seg[1].out_ld = S;
+  }
   if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) {
     p.seg[0].rope = ROPE_HALFSPLIT;
     p.seg[0].rope_d = d->d_nope;
@@ -391,6 +407,25 @@ hipError_t run_out_proj(const mla_dims* d, const mla_weights* w, const void* o, 
   p.K = hv;
   p.seg[0] = plain_seg(w->w_o, hv, d->d_model, y, d->d_model, true);
   return launch_gemm(p, 1, is_bf16(d), st);
+}
+
+hipError_t run_flash(const mla_dims* d, const void* q, const void* k, const void* kr, long long kr_bstride,
+                     const void* vt, void* o, int B, int S, hipStream_t st) {
+  FlashParams fp;
+  memset(&fp, 0, sizeof(fp));
+  fp.q = q;
+  fp.k = k;
+  fp.kr = d->d_rope > 0 ? kr : nullptr;
+  fp.kr_bstride = kr_bstride;
+  fp.vt = vt;
+  fp.o = o;
+  fp.B = B;
+  fp.S = S;
+  fp.H = d->n_heads;
+  fp.dn = d->d_nope;
+  fp.d_rope = d->d_rope;
+  fp.scale_log2 = softmax_scale(d) * kLog2e;
+  return launch_prefill_fast(fp, st);
 }
 
 DecodeParams decode_params(const mla_dims* d, const mla_cache* cache, const int32_t* ctx_len,
@@ -514,8 +549,10 @@ mla_status mla_prefill_attention(const mla_dims* d, const mla_weights* w, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* k = at(ws, lay.k);
   void* v = at(ws, lay.v);
-  hipError_t e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st);
+  const bool flash = use_flash(d, S);
+  hipError_t e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st, flash);
   if (e != hipSuccess) return MLA_ERR_HIP;
+  if (flash) return hip_status(run_flash(d, q, k, cache->kr, cache->max_seq, v, o, B, S, st));
   int dqp, dvp;
   prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp);
   PrefillParams pp;
@@ -559,11 +596,18 @@ mla_status mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, i
   if (e != hipSuccess) return MLA_ERR_HIP;
   void* k = at(ws, lay.k);
   void* v = at(ws, lay.v);
+  const bool flash = use_flash(d, S);
   if (cache)
-    e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st);
+    e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st, flash);
   else
-    e = run_kv_up(d, w, lat, false, 0, B, S, k, v, st);
+    e = run_kv_up(d, w, lat, false, 0, B, S, k, v, st, flash);
   if (e != hipSuccess) return MLA_ERR_HIP;
+  if (flash) {
+    void* o = at(ws, lay.o);
+    e = run_flash(d, q, k, cache ? cache->kr : latr, cache ? cache->max_seq : S, v, o, B, S, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    return hip_status(run_out_proj(d, w, o, B * S, y, st));
+  }
   int dqp, dvp;
   prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp);
   PrefillParams pp;

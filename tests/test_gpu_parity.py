@@ -23,6 +23,12 @@ SMALL = S.CONFIGS["small_lm"].replace(batch=2, seq=200)
 DSV2 = S.CONFIGS["dsv2_decode"].replace(d_model=512, batch=3, seq=1000)   # reduced d_model
 DSV2_P = S.CONFIGS["dsv2_prefill"].replace(d_model=512, batch=2, seq=300)
 MLRA = S.CONFIGS["mlra_decode"].replace(d_model=512, batch=4, ctx_lo=0, ctx_hi=0)
+# Shapes of the flash prefill path (sequence a multiple of 64 key rows; 320 = one full and
+# one partial 256-query tile, five key tiles).
+DSV2_PF = S.CONFIGS["dsv2_prefill"].replace(name="dsv2_prefill_s320", d_model=512, batch=2, seq=320)
+SMALL_PF = S.CONFIGS["small_lm"].replace(name="small_lm_s320", batch=2, seq=320)
+MLRA_PF = S.CONFIGS["mlra_decode"].replace(name="mlra_prefill_s384", mode="prefill", d_model=512, batch=2,
+                                           seq=384, ctx_lo=0, ctx_hi=0)
 TINY_BF16_MLRA = S.MLAConfig("mlra_tiny", S.FAMILY_MLRA, "decode", 2, 40, d_model=64, n_heads=8,
                              d_nope=16, d_rope=0, r_kv=32, r_q=0, n_latent_heads=4, seed=77)
 
@@ -81,7 +87,9 @@ def test_cache_append(gu, cfg):
 # ---------------------------------------------------------------------------
 # mla_prefill: causal prefill, explicit K/V up-projection
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", [TINY, SMALL, DSV2_P, MLRA.replace(mode="prefill", batch=2, seq=150)],
+@pytest.mark.parametrize("cfg", [TINY, SMALL, DSV2_P, MLRA.replace(name="mlra_prefill_s150", mode="prefill", batch=2,
+                                                                  seq=150),
+                                 DSV2_PF, SMALL_PF, MLRA_PF],
                          ids=lambda c: c.name)
 @pytest.mark.parametrize("with_cache", [False, True])
 def test_prefill(gu, cfg, with_cache):
@@ -211,7 +219,7 @@ def test_decode_attention_entry(gu, cfg, ctx):
     gu.assert_close(gu.to_host(z), want, cfg.dtype, "z")
 
 
-@pytest.mark.parametrize("cfg", [DSV2_P, SMALL], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [DSV2_P, SMALL, DSV2_PF, SMALL_PF], ids=lambda c: c.name)
 def test_prefill_attention_entry(gu, cfg):
     """mla_prefill_attention on oracle queries and oracle latent rows."""
     import head_latent_attention_dkv_amd as M
@@ -274,3 +282,39 @@ def test_decode_attention_score_spikes(gu, spike_at):
     M.mla_decode_attention(lay.dims, gu.to_dev(q_lat, cfg), gu.to_dev(q_rope, cfg), B, cl, max(ctx),
                            M.cache_struct(ckv, kr, B, max_seq), z, ws, nbytes)
     gu.assert_close(gu.to_host(z), want, cfg.dtype, f"z spikes at {spike_at}")
+
+
+def test_prefill_attention_exact_max_restream(gu):
+    """Scores that rise far above the first key tile's maximum (the flash kernel's fixed
+    softmax reference): the first 32 latent and rotary-key rows are zero (score 0 for every
+    query) and the queries are scaled by 20, so later keys exceed the reference by more than
+    the kernel's 64 log2-unit gap and the workgroup re-streams with the exact maximum.  The
+    oracle attends over the bf16-rounded explicit keys and values (the kernel's stored K/V)."""
+    import head_latent_attention_dkv_amd as M
+    cfg = DSV2_PF
+    gu.say(f"[prefill_attention restream] {cfg.name}")
+    lay = layer(gu, cfg)
+    d = _dims(cfg)
+    B, S_, H = cfg.batch, cfg.seq, cfg.n_heads
+    dq = cfg.d_nope + cfg.d_rope
+    pos = np.arange(S_)
+    ckv_h = np.zeros((B, S_, cfg.r_kv), np.float32)
+    kr_h = np.zeros((B, S_, cfg.d_rope), np.float32)
+    q_h = np.zeros((B, S_, H, dq), np.float32)
+    want = np.zeros((B, S_, H, cfg.d_v))
+    for b in range(B):
+        xs = S.make_x(cfg, b, S_)
+        c, kr = O.latent_rows(xs, lay.prob.weights, d, pos)
+        c[:32] = 0.0
+        kr[:32] = 0.0
+        ckv_h[b] = S.round_bf16(c.astype(np.float32))
+        kr_h[b] = S.round_bf16(kr.astype(np.float32))
+        q_h[b] = S.round_bf16((20.0 * O.queries(xs, lay.prob.weights, d, pos)).astype(np.float32))
+        k, v = O.keys_values(ckv_h[b], kr_h[b], lay.prob.weights, d, pos)
+        k, v = S.round_bf16(k.astype(np.float32)), S.round_bf16(v.astype(np.float32))
+        want[b] = O.causal_attention(q_h[b], k, v, d.scale(), pos, pos)
+    o = torch.empty((B, S_, H, cfg.d_v), dtype=gu.tdtype(cfg), device="cuda")
+    ws, nbytes = lay.workspace(M.MLA_OP_PREFILL_ATTENTION, B, S_)
+    M.mla_prefill_attention(lay.dims, lay.ws_struct, gu.to_dev(q_h, cfg), B, S_,
+                            M.cache_struct(gu.to_dev(ckv_h, cfg), gu.to_dev(kr_h, cfg), B, S_), o, ws, nbytes)
+    gu.assert_close(gu.to_host(o), want, cfg.dtype, "o with far-above-reference scores")
