@@ -217,6 +217,7 @@ hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream
     if (p.seg[i].rope == ROPE_HALFSPLIT && p.seg[i].rope_d > max_rope_d) max_rope_d = p.seg[i].rope_d;
   if (!use_bf16) return launch_tile<float, 64, 64>(p, groups, s);
   if (skinny_supported(p, groups)) return launch_skinny(p, groups, s);
+  if (gemm_big_supported(p, groups)) return launch_gemm_big(p, groups, s);
   bool big = (long long)cdiv(p.M, 128) * cdiv(N, 128) * groups >= 512;
   if (big || max_rope_d > 64) return launch_tile<bf16, 128, 128>(p, groups, s);
   return launch_tile<bf16, 64, 64>(p, groups, s);

@@ -1,0 +1,207 @@
+// Large projection GEMM for gfx950 (bf16, many rows): out[m, n] = sum_k A[m, k] W[n, k].
+//
+// Workgroup tile 256 x 256, 4 waves in a 2 x 2 grid, each wave a 128 x 128 block of
+// 32x32x16 MFMA accumulators (16 x 16 fp32 per lane, in the accumulation registers).  K
+// advances 32 at a time through NST LDS stages filled by 16-byte direct-to-LDS copies:
+// each copy instruction moves 16 rows x 64 bytes of A or of W.  Rows are 64 bytes (four
+// 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), which puts the 8 rows of
+// one LDS read phase (row stride 64 B) on 8 distinct 16-byte bank windows.  The epilogue
+// goes through LDS per wave, 32 rows at a time, into the shared output stage (rotary
+// pairs, head scatter, cache rows, head-major / transposed layouts).
+#include <type_traits>
+
+#include "common.h"
+#include "gemm_epilogue.h"
+#include "internal.h"
+#include "lds_dma.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int GBM = 256, GBN = 256, GBK = 32, GNST = 4;
+constexpr int G_AB = GBM * GBK * 2;                 // A bytes per stage (= W bytes)
+constexpr int G_STAGE = 2 * G_AB;                   // 32 KB
+constexpr int G_CPW = (G_AB / 1024) / 4;            // copies per wave per operand per stage (4)
+constexpr int G_LDC = 128 + 4;                      // epilogue LDS row stride (floats)
+constexpr size_t G_LDS = (size_t)GNST * G_STAGE;    // 128 KB
+static_assert((size_t)4 * 32 * G_LDC * 4 <= G_LDS, "epilogue chunks fit in the stages");
+
+__device__ __forceinline__ long long big_a_row(const GemmParams& p, int m) {
+  if (!p.a_cache) return m;
+  const int b = m / p.rows_per_batch;
+  return (long long)b * p.a_bstride + (m - b * p.rows_per_batch);
+}
+
+__device__ __forceinline__ int opaque_int(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int col = lane & 31, half = lane >> 5;
+  const int n0 = blockIdx.x * GBN;
+  const int m0 = blockIdx.y * GBM;
+  const int z = blockIdx.z;
+  const int zo = z / p.zdiv, zi = z - zo * p.zdiv;
+  const long long a_goff = zo * p.a_goff[0] + zi * p.a_goff[1];
+  const long long w_goff = zo * p.w_goff[0] + zi * p.w_goff[1];
+  const long long o_goff = zo * p.o_goff[0] + zi * p.o_goff[1];
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int nst = p.K / GBK;
+
+  // copy sources: copy j of wave w covers rows 16 (4 w + j) + lane / 4, physical chunk
+  // lane % 4, which holds logical chunk (lane % 4) ^ ((row >> 2) & 3)
+  const bf16* asrc[G_CPW];
+  const bf16* wsrc[G_CPW];
+#pragma unroll
+  for (int j = 0; j < G_CPW; ++j) {
+    const int t = 16 * (G_CPW * wave + j) + lane / 4;
+    const int c = (lane & 3) ^ ((t >> 2) & 3);
+    const int m = min(m0 + t, p.M - 1);
+    asrc[j] = reinterpret_cast<const bf16*>(p.a) + big_a_row(p, m) * p.a_ld + a_goff + 8 * c;
+    const int n = min(n0 + t, N - 1);
+    const int s = (n < p.seg[0].n) ? 0 : 1;
+    const int nn = n - (s ? p.seg[0].n : 0);
+    wsrc[j] = reinterpret_cast<const bf16*>(p.seg[s].w) + w_goff + (long long)nn * p.seg[s].w_ld + 8 * c;
+  }
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto issue = [&](int st) {
+    const uint32_t base = lds0 + (st % GNST) * G_STAGE;
+    const int k0 = st * GBK;
+#pragma unroll
+    for (int j = 0; j < G_CPW; ++j)
+      dma16(asrc[j] + k0, __builtin_amdgcn_readfirstlane(base + (G_CPW * wave + j) * 1024));
+#pragma unroll
+    for (int j = 0; j < G_CPW; ++j)
+      dma16(wsrc[j] + k0, __builtin_amdgcn_readfirstlane(base + G_AB + (G_CPW * wave + j) * 1024));
+  };
+
+  // operand read: row r (= 32 blk + col within the wave's block), logical chunk 2 ks + half;
+  // r mod 32 = col, so the swizzle key (r >> 2) & 3 = (col >> 2) & 3 for every block
+  const int rd_base = col * 64 | ((((col >> 2) & 3) ^ half) << 4);   // XOR (2 ks) << 4 below
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+#pragma unroll
+  for (int st = 0; st < GNST - 1; ++st)
+    if (st < nst) issue(st);
+  for (int it = 0; it < nst; ++it) {
+    const int left = nst - 1 - it;
+    if (left >= 2) wait_vmcnt<2 * 2 * G_CPW>();
+    else if (left >= 1) wait_vmcnt<2 * G_CPW>();
+    else wait_vmcnt<0>();
+    barrier_only();
+    if (it + GNST - 1 < nst) issue(it + GNST - 1);
+    const unsigned char* T = smem + (it % GNST) * G_STAGE;
+    const int rb0 = opaque_int(rd_base);
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      const int off = rb0 ^ (ks << 5);
+      Frag<bf16> fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off + (128 * wm + 32 * i) * 64));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + G_AB + off + (128 * wn + 32 * j) * 64));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma32(fa[i], fb[j], acc[i][j]);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Epilogue per wave: its 128 x 128 block in four chunks of 32 rows.  Accumulator element
+  // e of lane l in block (i, j) is out[128 wm + 32 i + 8 (e/4) + 4 (l/32) + e%4][128 wn + 32 j + l%32].
+  float* Cs = reinterpret_cast<float*>(smem) + wave * 32 * G_LDC;
+  auto stage = [&](auto I) {                    // chunk I with compile-time accumulator indices
+    constexpr int i = decltype(I)::value;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) Cs[(8 * (e >> 2) + 4 * half + (e & 3)) * G_LDC + 32 * j + col] = acc[i][j][e];
+  };
+#pragma nounroll
+  for (int i = 0; i < 4; ++i) {
+    switch (i) {
+      case 0: stage(std::integral_constant<int, 0>{}); break;
+      case 1: stage(std::integral_constant<int, 1>{}); break;
+      case 2: stage(std::integral_constant<int, 2>{}); break;
+      default: stage(std::integral_constant<int, 3>{}); break;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    if (p.fast_epilogue)
+      epilogue_block_fast<bf16>(p, Cs, G_LDC, m0 + 128 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane);
+    else
+      epilogue_block<bf16>(p, Cs, G_LDC, m0 + 128 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane, 64);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace
+
+bool gemm_big_supported(const GemmParams& p, int groups) {
+  (void)groups;
+  if (p.w_kmajor || p.M < GBM || p.K % GBK != 0 || p.a_ld % 8 != 0) return false;
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  if (N < 128) return false;
+  for (int i = 0; i < 2; ++i)
+    if (p.a_goff[i] % 8 != 0 || p.w_goff[i] % 8 != 0) return false;
+  if ((reinterpret_cast<uintptr_t>(p.a) & 15) != 0) return false;
+  int start = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    const GemmSeg& sg = p.seg[i];
+    if (sg.w_ld % 8 != 0 || (reinterpret_cast<uintptr_t>(sg.w) & 15) != 0) return false;
+    if (sg.rope == ROPE_INTERLEAVED && (start % 2 != 0 || sg.rope_d % 2 != 0)) return false;
+    if (sg.rope == ROPE_HALFSPLIT && (start % 128 != 0 || sg.rope_d > 128 || 128 % sg.rope_d != 0)) return false;
+    start += sg.n;
+  }
+  return true;
+}
+
+bool gemm_fast_epilogue_ok(const GemmParams& p, int groups) {
+  auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+  if (p.seg[0].n % 8 != 0) return false;
+  for (int i = 0; i < 2; ++i)
+    if (p.o_goff[i] % 8 != 0) return false;
+  (void)groups;
+  for (int i = 0; i < p.nseg; ++i) {
+    const GemmSeg& sg = p.seg[i];
+    if (!al16(sg.out)) return false;
+    if (sg.rope != ROPE_OFF && sg.rope_d % 8 != 0) return false;
+    if (sg.rope == ROPE_HALFSPLIT && (sg.rope_d / 2) % 8 != 0) return false;
+    if (sg.layout == OUT_ROWS) {
+      if (sg.out_hw % 8 != 0 || sg.out_hs % 8 != 0 || sg.out_ld % 8 != 0) return false;
+    } else if (sg.layout == OUT_HEAD_MAJOR) {
+      if (sg.out_hw % 8 != 0) return false;
+    } else {
+      if (sg.out_f32 || sg.out_ld % 16 != 0 || p.rows_per_batch % 32 != 0) return false;
+    }
+  }
+  return true;
+}
+
+hipError_t launch_gemm_big(const GemmParams& pin, int groups, hipStream_t s) {
+  GemmParams p = pin;
+  p.fast_epilogue = gemm_fast_epilogue_ok(p, groups) ? 1 : 0;
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  dim3 grid(cdiv(N, GBN), cdiv(p.M, GBM), groups);
+  hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(256), G_LDS, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -91,3 +91,104 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
 }
 
 }  // namespace mla
+
+namespace mla {
+
+// Vectorised form of epilogue_block for one wave and a block of `rows` (a multiple of 4,
+// inside one batch entry when a segment is transposed) x `cols` (a multiple of 8) values:
+// lane l takes the 8-column runs l % 16 (+16 ...) and rows l / 16 (+4 ...), stores 8
+// outputs at once; transposed segments are written per column in runs of 4 tokens.
+// Requires gemm_fast_epilogue_ok() on the host.
+template <typename T>
+__device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const float* Cs, int ldc, int m0,
+                                                    int rows, int n0, int cols, long long o_goff, int lane) {
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  for (int cr = lane & 15; cr < cols / 8; cr += 16) {
+    const int n = n0 + 8 * cr;
+    if (n >= N) continue;
+    const int s = (n < p.seg[0].n) ? 0 : 1;
+    const GemmSeg& sg = p.seg[s];
+    if (sg.layout == OUT_HEAD_T16) continue;
+    const int nn = n - (s ? p.seg[0].n : 0);
+    const long long cc = nn + o_goff;
+    const int hw = sg.out_hw;
+    const long long head = hw ? cc / hw : 0, j0 = hw ? cc - head * hw : cc;
+    const int hh = sg.rope != ROPE_OFF ? nn % sg.rope_d : 0;
+    const int half = sg.rope_d >> 1;
+    for (int r = lane >> 4; r < rows; r += 4) {
+      const int m = m0 + r;
+      if (m >= p.M) break;
+      const int b = m / p.rows_per_batch;
+      const int t = m - b * p.rows_per_batch;
+      const float* src = Cs + r * ldc + 8 * cr;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = src[e];
+      if (sg.rope == ROPE_INTERLEAVED) {
+        const int pos = (p.pos0 ? p.pos0[b] : 0) + t;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float sn, cs;
+          const int jj = (hh >> 1) + q;
+          rope_sincos(pos, p.rope.hi[jj], p.rope.lo[jj], &sn, &cs);
+          const float x0 = v[2 * q], x1 = v[2 * q + 1];
+          v[2 * q] = x0 * cs - x1 * sn;
+          v[2 * q + 1] = x0 * sn + x1 * cs;
+        }
+      } else if (sg.rope == ROPE_HALFSPLIT) {
+        const int pos = (p.pos0 ? p.pos0[b] : 0) + t;
+        const bool lo = hh < half;
+        const float* ps = src + (lo ? half : -half);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float sn, cs;
+          const int jj = (hh + e) % half;
+          rope_sincos(pos, p.rope.hi[jj], p.rope.lo[jj], &sn, &cs);
+          const float o = ps[e];
+          v[e] = lo ? v[e] * cs - o * sn : o * sn + v[e] * cs;
+        }
+      }
+      long long idx;
+      if (sg.layout == OUT_ROWS) {
+        const long long oc = hw ? head * sg.out_hs + j0 : cc;
+        const long long orow = sg.out_cache ? (long long)b * p.out_bstride + (p.pos0 ? p.pos0[b] : 0) + t : m;
+        idx = orow * sg.out_ld + oc;
+      } else {
+        idx = (((long long)b * sg.out_nh + head) * p.rows_per_batch + t) * hw + j0;
+      }
+      if (sg.out_f32) {
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(sg.out) + idx);
+        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sg.out) + idx) = o;
+      }
+    }
+  }
+  // transposed segments: column c, tokens in runs of 4 (perm16 keeps 4-runs contiguous)
+  for (int c = lane; c < cols; c += 64) {
+    const int n = n0 + c;
+    if (n >= N) continue;
+    const int s = (n < p.seg[0].n) ? 0 : 1;
+    const GemmSeg& sg = p.seg[s];
+    if (sg.layout != OUT_HEAD_T16) continue;
+    const long long cc = n - (s ? p.seg[0].n : 0) + o_goff;
+    const long long head = cc / sg.out_hw, j = cc - head * sg.out_hw;
+    for (int r = 0; r < rows; r += 4) {
+      const int m = m0 + r;
+      if (m >= p.M) break;
+      const int b = m / p.rows_per_batch;
+      const int t = m - b * p.rows_per_batch;
+      const long long idx = (((long long)b * sg.out_nh + head) * sg.out_hw + j) * sg.out_ld + perm16(t);
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (bf16)Cs[(r + e) * ldc + c];
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sg.out) + idx) = o;
+    }
+  }
+}
+
+}  // namespace mla

@@ -76,6 +76,7 @@ struct GemmParams {
   float* part;
   size_t part_bytes;
   int splits, kchunk;
+  int fast_epilogue;        // set by the launcher when gemm_fast_epilogue_ok()
 };
 
 hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream_t s);
@@ -85,6 +86,12 @@ bool skinny_supported(const GemmParams& p, int groups);
 hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s);
 // workspace bytes launch_skinny uses for split-K partials of an M x N x K product
 size_t skinny_ws_bytes(int M, int N, int K, int groups);
+// Many-row (M >= 256) bf16 path: 256 x 256 tiles streamed through LDS.
+bool gemm_big_supported(const GemmParams& p, int groups);
+// Vectorised epilogue preconditions: 8-element runs never straddle a segment or a head,
+// stores are 16-byte aligned, transposed segments see whole 4-token runs of one sequence.
+bool gemm_fast_epilogue_ok(const GemmParams& p, int groups);
+hipError_t launch_gemm_big(const GemmParams& p, int groups, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Split-context decode over the latent cache + log-sum-exp combine
