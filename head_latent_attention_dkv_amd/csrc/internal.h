@@ -152,6 +152,7 @@ struct FlashParams {
   void* o;                  // [B][S][H][dv]
   int B, S, H, dn, d_rope;
   float scale_log2;
+  int ntq;                  // query tiles per (sequence, head); set by the launcher
 };
 bool prefill_fast_supported(int dn, int d_rope, int dv, int S);
 hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s);

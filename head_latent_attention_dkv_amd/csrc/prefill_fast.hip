@@ -34,6 +34,9 @@ constexpr int FK = 64;           // keys per tile
 constexpr int FNST = 3;          // LDS stages
 constexpr float kFlashGap = 64.0f;    // log2 units: p <= 2^64 stays far from bf16 / fp32 overflow
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#define kOnes2 ((bf16x2){(__bf16)1.0f, (__bf16)1.0f})
+
 __device__ __forceinline__ int opaque_i(int x) {
   asm volatile("" : "+v"(x));
   return x;
@@ -68,9 +71,25 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int ntq = gridDim.x;
-  const int qt = ntq - 1 - (int)blockIdx.x;            // longest query tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Block -> (sequence, head, query tile).  Workgroups are handed to the 8 XCDs in turn
+  // (block L to XCD L % 8), so the map keeps each (sequence, head) group on one XCD: XCD x
+  // runs groups x, x + 8, ..., each as ntq consecutive blocks, longest query tile first.
+  // Every XCD then gets the same work, and a group's keys / values are reused from its
+  // XCD's L2.  (Group counts not divisible by 8 use the plain order.)
+  const int ntq = p.ntq;
+  const int L = blockIdx.x;
+  const int ngroups = p.B * p.H;
+  int g, qrev;
+  if (ngroups % 8 == 0) {
+    const int x = L & 7, slot = L >> 3;
+    g = (slot / ntq) * 8 + x;
+    qrev = slot % ntq;
+  } else {
+    g = L / ntq;
+    qrev = L % ntq;
+  }
+  const int qt = ntq - 1 - qrev;
+  const int h = g % p.H, b = g / p.H;
   const int S = p.S;
   const int q0 = qt * FQ;
   const int qw = q0 + 64 * wave;                        // this wave's first query
@@ -108,9 +127,12 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
     const int row = (wave * KNW + j) * C::KN_RPC + lane / C::CN;
     kn_src[j] = row * DN * 2 + (((lane % C::CN) ^ (row % C::CN)) << 4);
   }
-  const int r8 = lane / 8, c8 = ((lane % 8) ^ r8) << 4;
-  const int kr_src = (wave * KRW * 8 + r8) * DR * 2 + c8;      // + j * 8 rows
-  const long long v_src = (long long)(wave * VW * 8 + r8) * S * 2 + c8;   // + j * 8 rows
+  // 128-byte rows (rotary keys, transposed values): chunk c of row r sits at
+  // c ^ ((r >> 1) & 7), so the 16 rows of one 16-lane read phase (two rows per 256-byte
+  // bank line) land on distinct bank windows.  Copies cover 8 rows starting at a multiple
+  // of 8, so the key of lane row r8 = lane / 8 is (r8 >> 1) + 4 ((copy row0 / 8) & 1).
+  const int r8 = lane / 8;
+  auto c8 = [&](int row0) { return ((lane % 8) ^ (((row0 + r8) >> 1) & 7)) << 4; };
   const uint32_t lds0 = lds_addr_of(smem);
   auto issue = [&](int tile) {
     const uint32_t sbase = lds0 + (tile % FNST) * C::STAGE;
@@ -120,21 +142,25 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
       dma16(kbase + (long long)key0 * DN * 2 + kn_src[j],
             __builtin_amdgcn_readfirstlane(sbase + (wave * KNW + j) * 1024));
 #pragma unroll
-    for (int j = 0; j < KRW; ++j)
-      dma16(rbase + (long long)key0 * DR * 2 + kr_src + j * 8 * DR * 2,
+    for (int j = 0; j < KRW; ++j) {
+      const int row0 = (wave * KRW + j) * 8;
+      dma16(rbase + (long long)key0 * DR * 2 + (row0 + r8) * DR * 2 + c8(row0),
             __builtin_amdgcn_readfirstlane(sbase + C::KN_BYTES + (wave * KRW + j) * 1024));
+    }
 #pragma unroll
-    for (int j = 0; j < VW; ++j)
-      dma16(vbase + (long long)key0 * 2 + v_src + (long long)j * 8 * S * 2,
+    for (int j = 0; j < VW; ++j) {
+      const int row0 = (wave * VW + j) * 8;
+      dma16(vbase + (long long)key0 * 2 + (long long)(row0 + r8) * S * 2 + c8(row0),
             __builtin_amdgcn_readfirstlane(sbase + C::KN_BYTES + C::KR_BYTES + (wave * VW + j) * 1024));
+    }
   };
 
   // ---- operand LDS addresses: row base | (swizzled chunk << 4); the logical chunk of
   // k-step ks is 2 ks + half, and (2 ks + half) ^ key = 2 ks ^ (half ^ key), so one base per
   // region and an XOR with ks << 5 give every address ----
   const int kn_base = col * DN * 2 | (((col % C::CN) ^ half) << 4);
-  const int kr_base = C::KN_BYTES + (col * DR * 2 | (((col % 8) ^ half) << 4));
-  const int v_base = C::KN_BYTES + C::KR_BYTES + (col * FK * 2 | (((col % 8) ^ half) << 4));
+  const int kr_base = C::KN_BYTES + (col * DR * 2 | ((((col >> 1) & 7) ^ half) << 4));
+  const int v_base = C::KN_BYTES + C::KR_BYTES + (col * FK * 2 | ((((col >> 1) & 7) ^ half) << 4));
 
   f32x16 oacc[C::DB][2];
 #pragma unroll
@@ -166,61 +192,83 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
       const unsigned char* T = smem + (it % FNST) * C::STAGE;
       // per-lane address bases, kept opaque so the compiler rebuilds (not hoists) addresses
       const int kn_b = opaque_i(kn_base), kr_b = opaque_i(kr_base), v_b = opaque_i(v_base);
-      // the tile's two 32-key halves one after the other: scores for 32 keys x 64 queries
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (key0 + 32 * kb > qw + 63) break;            // this half is after all of the wave's queries
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+
+      const bool diag = key0 + 63 > qw;                 // some keys after some of this wave's queries
+      // Half kb of the tile: scores S^T[32 keys x 64 queries], causal mask, maxima (log2 units)
+      auto kfrag = [&](int kb, int ks) {
+        const int off = ks < C::KSN ? (kn_b ^ (ks << 5)) + kb * 32 * DN * 2
+                                    : (kr_b ^ ((ks - C::KSN) << 5)) + kb * 32 * DR * 2;
+        return frag_load<bf16>(reinterpret_cast<const bf16*>(T + off));
+      };
+      // operand reads run two k-steps ahead of the MFMAs that consume them
+      auto scores = [&](int kb, f32x16 (&sc)[2]) {
+        sc[0] = f32x16{};
+        sc[1] = f32x16{};
+        Frag<bf16> fa[3];
+        fa[0] = kfrag(kb, 0);
+        fa[1] = kfrag(kb, 1);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const int off = ks < C::KSN ? (kn_b ^ (ks << 5)) + kb * 32 * DN * 2
-                                      : (kr_b ^ ((ks - C::KSN) << 5)) + kb * 32 * DR * 2;
-          const Frag<bf16> fa = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off));
+          if (ks + 2 < C::KS) fa[(ks + 2) % 3] = kfrag(kb, ks + 2);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) sacc[qb] = mma32(fa, qf[qb][ks], sacc[qb]);
+          for (int qb = 0; qb < 2; ++qb) sc[qb] = mma32(fa[ks % 3], qf[qb][ks], sc[qb]);
         }
-        const int kk0 = key0 + 32 * kb;
-        const bool diag = kk0 + 31 > qw;                // some keys after some of this wave's queries
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int ks = 0; ks < C::KS - 2; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      };
+      auto mask_max = [&](int kb, f32x16 (&sc)[2], float (&mt)[2]) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int qi = qw + 32 * qb + col;
-          sacc[qb] *= p.scale_log2;
           if (diag) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (kk0 + 8 * (i >> 2) + 4 * half + (i & 3) > qi) sacc[qb][i] = -INFINITY;
+              if (key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3) > qi) sc[qb][i] = -INFINITY;
           }
+          float mx = sc[qb][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[qb][i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          mt[qb] = mx * p.scale_log2;
         }
+      };
+      auto track = [&](const float (&mt)[2], bool first) {
         if constexpr (!SECOND) {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
-            float mt = sacc[qb][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sacc[qb][i]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            m_seen[qb] = fmaxf(m_seen[qb], mt);
-            if (it == 0 && kb == 0) m_ref[qb] = mt;      // key 0 is visible to every query
-            if (__builtin_amdgcn_readfirstlane(__any(mt > m_ref[qb] + kFlashGap))) redo = true;
+            m_seen[qb] = fmaxf(m_seen[qb], mt[qb]);
+            if (first) m_ref[qb] = mt[qb];                // key 0 is visible to every query
+            if (__builtin_amdgcn_readfirstlane(__any(mt[qb] > m_ref[qb] + kFlashGap))) redo = true;
           }
-          if (redo) continue;
         }
-        Frag<bf16> pf[2][2];
+      };
+      // p = 2^(scale s - m_ref) (raw v_exp_f32: the argument stays below kFlashGap unless the
+      // wave is re-streaming anyway, and -inf gives 0)
+      auto probs = [&](const f32x16 (&sc)[2], Frag<bf16> (&pf)[2][2]) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          float ps = 0.f;
+          const float nm = -m_ref[qb];
+          float ps = l_run[qb];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             float pv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              pv[j] = exp2f(sacc[qb][8 * t + j] - m_ref[qb]);
-              ps += pv[j];
-            }
+            for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][8 * t + j], p.scale_log2, nm));
             pf[qb][t] = frag_from_f32<bf16>(pv);
+            // the denominator sums the same bf16 probabilities the products use
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              ps = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[qb][t].v[2 * j], pf[qb][t].v[2 * j + 1]}, kOnes2, ps, false);
           }
-          l_run[qb] += ps;
+          l_run[qb] = ps;
         }
-        // ---- O^T += V^T . P^T over the half's two 16-key steps ----
+      };
+      auto pv_products = [&](int kb, const Frag<bf16> (&pf)[2][2]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -230,6 +278,25 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mma32(fv, pf[qb][t], oacc[db][qb]);
           }
+      };
+
+      // Order: S0, mask/max 0, [S1 MFMAs | exponentials of half 0], mask/max 1,
+      // [P0 V products | exponentials of half 1], P1 V products.  A wave that must re-stream
+      // keeps computing scores and maxima (exact maximum) but adds nothing to O.
+      f32x16 s0[2], s1[2];
+      float mt0[2], mt1[2];
+      Frag<bf16> pf0[2][2], pf1[2][2];
+      scores(0, s0);
+      mask_max(0, s0, mt0);
+      track(mt0, it == 0);
+      probs(s0, pf0);
+      scores(1, s1);
+      mask_max(1, s1, mt1);
+      track(mt1, false);
+      if (SECOND || !redo) {
+        pv_products(0, pf0);
+        probs(s1, pf1);
+        pv_products(1, pf1);
       }
     }
   };
@@ -284,8 +351,10 @@ bool prefill_fast_supported(int dn, int d_rope, int dv, int S) {
 
 namespace {
 template <int DN, int DR>
-hipError_t launch_flash(const FlashParams& p, hipStream_t s) {
-  dim3 grid(cdiv(p.S, FQ), p.H, p.B);
+hipError_t launch_flash(const FlashParams& pin, hipStream_t s) {
+  FlashParams p = pin;
+  p.ntq = cdiv(p.S, FQ);
+  dim3 grid(p.ntq * p.H * p.B);
   constexpr size_t lds = FlashCfg<DN, DR>::LDS;
   hipLaunchKernelGGL((prefill_flash_kernel<DN, DR>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
