@@ -94,10 +94,11 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
 
 namespace mla {
 
-// Vectorised form of epilogue_block for one wave and a block of `rows` (a multiple of 4,
-// inside one batch entry when a segment is transposed) x `cols` (a multiple of 8) values:
-// lane l takes the 8-column runs l % 16 (+16 ...) and rows l / 16 (+4 ...), stores 8
-// outputs at once; transposed segments are written per column in runs of 4 tokens.
+// Vectorised form of epilogue_block for one wave and a block of `rows` (a multiple of 4;
+// a multiple of 32 starting at a multiple of 32 inside one batch entry when a segment is
+// transposed) x `cols` (a multiple of 8) values: lane l takes the 8-column runs l % 16
+// (+16 ...) and rows l / 16 (+4 ...) and stores 8 outputs at once; transposed segments are
+// written 16 bytes per lane along the token axis.
 // Requires gemm_fast_epilogue_ok() on the host.
 template <typename T>
 __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const float* Cs, int ldc, int m0,
@@ -168,25 +169,34 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
       }
     }
   }
-  // transposed segments: column c, tokens in runs of 4 (perm16 keeps 4-runs contiguous)
-  for (int c = lane; c < cols; c += 64) {
-    const int n = n0 + c;
-    if (n >= N) continue;
-    const int s = (n < p.seg[0].n) ? 0 : 1;
-    const GemmSeg& sg = p.seg[s];
-    if (sg.layout != OUT_HEAD_T16) continue;
-    const long long cc = n - (s ? p.seg[0].n : 0) + o_goff;
-    const long long head = cc / sg.out_hw, j = cc - head * sg.out_hw;
-    for (int r = 0; r < rows; r += 4) {
-      const int m = m0 + r;
-      if (m >= p.M) break;
-      const int b = m / p.rows_per_batch;
-      const int t = m - b * p.rows_per_batch;
-      const long long idx = (((long long)b * sg.out_nh + head) * sg.out_hw + j) * sg.out_ld + perm16(t);
-      bf16x4 o;
+  // transposed segments: 8 consecutive output positions (16 bytes) per lane, 4 lanes per
+  // 32-position row segment, so one store instruction fills 16 whole 64-byte segments.
+  // Positions 8 u .. 8 u + 7 of a 16-group hold tokens 4 u' .. 4 u' + 3 and 8 + 4 u' ..
+  // 8 + 4 u' + 3 (u' = u % 2) of the same group (perm16).
+  for (int base = 0; base < rows; base += 32) {
+    const int m = m0 + base;
+    if (m >= p.M) break;
+    const int b = m / p.rows_per_batch;
+    const int t0 = m - b * p.rows_per_batch;           // a multiple of 32
+    const int seg = lane & 3;                          // positions 8 seg .. 8 seg + 7
+    const int grp = seg >> 1, u = seg & 1;
+    const int ra = base + 16 * grp + 4 * u;            // local rows of the first 4 tokens
+    for (int c = lane >> 2; c < cols; c += 16) {
+      const int n = n0 + c;
+      if (n >= N) continue;
+      const int s = (n < p.seg[0].n) ? 0 : 1;
+      const GemmSeg& sg = p.seg[s];
+      if (sg.layout != OUT_HEAD_T16) continue;
+      const long long cc = n - (s ? p.seg[0].n : 0) + o_goff;
+      const long long head = cc / sg.out_hw, j = cc - head * sg.out_hw;
+      const long long idx = (((long long)b * sg.out_nh + head) * sg.out_hw + j) * sg.out_ld + t0 + 8 * seg;
+      bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (bf16)Cs[(r + e) * ldc + c];
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sg.out) + idx) = o;
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (bf16)Cs[(ra + e) * ldc + c];
+        o[4 + e] = (bf16)Cs[(ra + 8 + e) * ldc + c];
+      }
+      *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sg.out) + idx) = o;
     }
   }
 }

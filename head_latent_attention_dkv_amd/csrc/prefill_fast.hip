@@ -32,6 +32,10 @@ namespace {
 constexpr int FQ = 256;          // queries per workgroup
 constexpr int FK = 64;           // keys per tile
 constexpr int FNST = 3;          // LDS stages
+#ifndef MLA_FLASH_QB
+#define MLA_FLASH_QB 1
+#endif
+constexpr int kFlashQB = MLA_FLASH_QB;   // 32-query blocks per wave (waves per workgroup = 8 / QB)
 constexpr float kFlashGap = 64.0f;    // log2 units: p <= 2^64 stays far from bf16 / fp32 overflow
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -42,8 +46,9 @@ __device__ __forceinline__ int opaque_i(int x) {
   return x;
 }
 
-template <int DN, int DR>
+template <int DN, int DR, int QB>
 struct FlashCfg {
+  static constexpr int NWV = 8 / QB;                  // waves per workgroup (256 queries)
   static constexpr int DV = DN;
   static constexpr int KSN = DN / 16, KSR = DR / 16, KS = KSN + KSR;
   static constexpr int CN = DN / 8;                   // 16-byte chunks per key row (decompressed)
@@ -55,18 +60,19 @@ struct FlashCfg {
   static constexpr int KR_COPIES = KR_BYTES / 1024;
   static constexpr int V_COPIES = V_BYTES / 1024;
   static constexpr int COPIES = KN_COPIES + KR_COPIES + V_COPIES;
-  static constexpr int CPW = COPIES / 4;              // per wave per stage
+  static constexpr int CPW = COPIES / NWV;            // per wave per stage
   static constexpr int KN_RPC = 1024 / (DN * 2);      // key rows per copy
   static constexpr int DB = DV / 32;                  // 32-row blocks of O^T
   static constexpr size_t LDS = (size_t)FNST * STAGE;
-  static_assert(KN_COPIES % 4 == 0 && KR_COPIES % 4 == 0 && V_COPIES % 4 == 0, "copies split evenly over the waves");
+  static_assert(KN_COPIES % NWV == 0 && KR_COPIES % NWV == 0 && V_COPIES % NWV == 0, "copies split evenly over the waves");
   static_assert(DN == 64 || DN == 128, "decompressed width");
   static_assert(DR == 0 || DR == 64, "rotary width");
 };
 
-template <int DN, int DR>
-__global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
-  using C = FlashCfg<DN, DR>;
+template <int DN, int DR, int QB>
+__global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashParams p) {
+  using C = FlashCfg<DN, DR, QB>;
+  constexpr int QW = 32 * QB;                          // queries per wave
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -92,15 +98,15 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
   const int h = g % p.H, b = g / p.H;
   const int S = p.S;
   const int q0 = qt * FQ;
-  const int qw = q0 + 64 * wave;                        // this wave's first query
+  const int qw = q0 + QW * wave;                        // this wave's first query
   const int kend = min(S, q0 + FQ);                     // keys 0 .. kend-1 (multiple of 64)
   const int ntiles = kend / FK;
   const long long bh = (long long)b * p.H + h;
 
   // ---- Q^T fragments: query 32 qb + col of the wave, features 16 ks + 8 half .. +7 ----
-  Frag<bf16> qf[2][C::KS];
+  Frag<bf16> qf[QB][C::KS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int qi = min(qw + 32 * qb + col, S - 1);
     const bf16* qp = reinterpret_cast<const bf16*>(p.q) + (((long long)b * S + qi) * p.H + h) * (DN + DR) + 8 * half;
 #pragma unroll
@@ -108,7 +114,7 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
   }
   wait_vmcnt<0>();
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(qf[qb][ks].v));
 
@@ -120,7 +126,7 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
   // Every wave issues the same mix per stage: KNW decompressed-key copies, KRW rotary-key
   // copies, VW value copies (its quarter of each region).  Rotary and value rows have 8
   // chunks and 8 rows per copy, so their swizzle depends on the lane only.
-  constexpr int KNW = C::KN_COPIES / 4, KRW = C::KR_COPIES / 4, VW = C::V_COPIES / 4;
+  constexpr int KNW = C::KN_COPIES / C::NWV, KRW = C::KR_COPIES / C::NWV, VW = C::V_COPIES / C::NWV;
   int kn_src[KNW];           // lane byte offset of decompressed-key copy j of this wave
 #pragma unroll
   for (int j = 0; j < KNW; ++j) {
@@ -162,17 +168,23 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
   const int kr_base = C::KN_BYTES + (col * DR * 2 | ((((col >> 1) & 7) ^ half) << 4));
   const int v_base = C::KN_BYTES + C::KR_BYTES + (col * FK * 2 | ((((col >> 1) & 7) ^ half) << 4));
 
-  f32x16 oacc[C::DB][2];
+  f32x16 oacc[C::DB][QB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
   // Softmax reference per query column: the maximum of its first key tile.  p = 2^(s - m_ref)
   // stays exact in bf16 / fp32 while s - m_ref < kFlashGap; a wave whose scores rise
   // further stops accumulating but keeps tracking its exact maximum (m_seen), and the
   // workgroup then re-streams the keys once with that maximum as the reference.  No
   // accumulator rescale sits in the loop.
-  float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_ref[QB], m_seen[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = -INFINITY;
+    m_seen[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
   bool redo = false;
 
   auto pass = [&](auto second_pass) {
@@ -186,7 +198,7 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
       barrier_only();
       if (it + FNST - 1 < ntiles) issue(it + FNST - 1);
       const int key0 = it * FK;
-      if (key0 > qw + 63) continue;                     // every key of the tile is after this wave's queries
+      if (key0 > qw + QW - 1) continue;                     // every key of the tile is after this wave's queries
       if (SECOND && !redo) continue;
 
       const unsigned char* T = smem + (it % FNST) * C::STAGE;
@@ -201,9 +213,9 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
         return frag_load<bf16>(reinterpret_cast<const bf16*>(T + off));
       };
       // operand reads run two k-steps ahead of the MFMAs that consume them
-      auto scores = [&](int kb, f32x16 (&sc)[2]) {
-        sc[0] = f32x16{};
-        sc[1] = f32x16{};
+      auto scores = [&](int kb, f32x16 (&sc)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb] = f32x16{};
         Frag<bf16> fa[3];
         fa[0] = kfrag(kb, 0);
         fa[1] = kfrag(kb, 1);
@@ -211,7 +223,7 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
         for (int ks = 0; ks < C::KS; ++ks) {
           if (ks + 2 < C::KS) fa[(ks + 2) % 3] = kfrag(kb, ks + 2);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) sc[qb] = mma32(fa[ks % 3], qf[qb][ks], sc[qb]);
+          for (int qb = 0; qb < QB; ++qb) sc[qb] = mma32(fa[ks % 3], qf[qb][ks], sc[qb]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -221,9 +233,9 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       };
-      auto mask_max = [&](int kb, f32x16 (&sc)[2], float (&mt)[2]) {
+      auto mask_max = [&](int kb, f32x16 (&sc)[QB], float (&mt)[QB]) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           const int qi = qw + 32 * qb + col;
           if (diag) {
 #pragma unroll
@@ -237,10 +249,10 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
           mt[qb] = mx * p.scale_log2;
         }
       };
-      auto track = [&](const float (&mt)[2], bool first) {
+      auto track = [&](const float (&mt)[QB], bool first) {
         if constexpr (!SECOND) {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
+          for (int qb = 0; qb < QB; ++qb) {
             m_seen[qb] = fmaxf(m_seen[qb], mt[qb]);
             if (first) m_ref[qb] = mt[qb];                // key 0 is visible to every query
             if (__builtin_amdgcn_readfirstlane(__any(mt[qb] > m_ref[qb] + kFlashGap))) redo = true;
@@ -249,9 +261,9 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
       };
       // p = 2^(scale s - m_ref) (raw v_exp_f32: the argument stays below kFlashGap unless the
       // wave is re-streaming anyway, and -inf gives 0)
-      auto probs = [&](const f32x16 (&sc)[2], Frag<bf16> (&pf)[2][2]) {
+      auto probs = [&](const f32x16 (&sc)[QB], Frag<bf16> (&pf)[QB][2]) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           const float nm = -m_ref[qb];
           float ps = l_run[qb];
 #pragma unroll
@@ -268,7 +280,7 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
           l_run[qb] = ps;
         }
       };
-      auto pv_products = [&](int kb, const Frag<bf16> (&pf)[2][2]) {
+      auto pv_products = [&](int kb, const Frag<bf16> (&pf)[QB][2]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -276,16 +288,16 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
             const int off = (v_b ^ ((2 * kb + t) << 5)) + db * 32 * FK * 2;
             const Frag<bf16> fv = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off));
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mma32(fv, pf[qb][t], oacc[db][qb]);
+            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mma32(fv, pf[qb][t], oacc[db][qb]);
           }
       };
 
       // Order: S0, mask/max 0, [S1 MFMAs | exponentials of half 0], mask/max 1,
       // [P0 V products | exponentials of half 1], P1 V products.  A wave that must re-stream
       // keeps computing scores and maxima (exact maximum) but adds nothing to O.
-      f32x16 s0[2], s1[2];
-      float mt0[2], mt1[2];
-      Frag<bf16> pf0[2][2], pf1[2][2];
+      f32x16 s0[QB], s1[QB];
+      float mt0[QB], mt1[QB];
+      Frag<bf16> pf0[QB][2], pf1[QB][2];
       scores(0, s0);
       mask_max(0, s0, mt0);
       track(mt0, it == 0);
@@ -314,10 +326,12 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x16{};
-      m_ref[0] = m_seen[0];
-      m_ref[1] = m_seen[1];
-      l_run[0] = l_run[1] = 0.f;
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        m_ref[qb] = m_seen[qb];
+        l_run[qb] = 0.f;
+      }
     }
     pass(std::true_type{});
     wait_vmcnt<0>();
@@ -325,7 +339,7 @@ __global__ void __launch_bounds__(256, 1) prefill_flash_kernel(FlashParams p) {
 
   // ---- normalise and store o[b][q][h][:] (4 consecutive features per 8-byte store) ----
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const float inv = 1.f / lt;
     const int qi = qw + 32 * qb + col;
@@ -350,22 +364,22 @@ bool prefill_fast_supported(int dn, int d_rope, int dv, int S) {
 }
 
 namespace {
-template <int DN, int DR>
+template <int DN, int DR, int QB>
 hipError_t launch_flash(const FlashParams& pin, hipStream_t s) {
   FlashParams p = pin;
   p.ntq = cdiv(p.S, FQ);
   dim3 grid(p.ntq * p.H * p.B);
-  constexpr size_t lds = FlashCfg<DN, DR>::LDS;
-  hipLaunchKernelGGL((prefill_flash_kernel<DN, DR>), grid, dim3(256), lds, s, p);
+  constexpr size_t lds = FlashCfg<DN, DR, QB>::LDS;
+  hipLaunchKernelGGL((prefill_flash_kernel<DN, DR, QB>), grid, dim3(64 * (8 / QB)), lds, s, p);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s) {
-  if (p.dn == 128 && p.d_rope == 64) return launch_flash<128, 64>(p, s);
-  if (p.dn == 128 && p.d_rope == 0) return launch_flash<128, 0>(p, s);
-  if (p.dn == 64 && p.d_rope == 0) return launch_flash<64, 0>(p, s);
-  if (p.dn == 64 && p.d_rope == 64) return launch_flash<64, 64>(p, s);
+  if (p.dn == 128 && p.d_rope == 64) return launch_flash<128, 64, kFlashQB>(p, s);
+  if (p.dn == 128 && p.d_rope == 0) return launch_flash<128, 0, kFlashQB>(p, s);
+  if (p.dn == 64 && p.d_rope == 0) return launch_flash<64, 0, kFlashQB>(p, s);
+  if (p.dn == 64 && p.d_rope == 64) return launch_flash<64, 64, kFlashQB>(p, s);
   return hipErrorInvalidValue;
 }
 
