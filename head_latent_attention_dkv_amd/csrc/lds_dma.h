@@ -18,8 +18,26 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // 16-byte global -> LDS copy per lane (lane l writes lds_addr + 16 l).  Issued as inline
 // assembly so the compiler does not drain all outstanding copies (vmcnt(0)) before every
 // LDS read it cannot disambiguate; completion is tracked explicitly with wait_vmcnt<>.
+// The copy takes its LDS address from M0, and on this GPU family an LDS-DMA instruction
+// needs one wait state after the SALU write of M0 (the compiler cannot see into the asm to
+// insert it), hence the s_nop.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Same copy addressed as wave-uniform base (SGPR pair) + 32-bit per-lane byte offset, which
+// keeps the 64-bit address arithmetic off the vector ALU.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
+// 4-byte form (64 lanes x 4 bytes = 256 contiguous LDS bytes), for narrow rows.
+//
+// Every lane of the wave must be active for any of these copies: an LDS-DMA issued under a
+// partial exec mask still fills the LDS slots of the inactive lanes, which would overwrite
+// the neighbouring rows.
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 
 __device__ __forceinline__ int bitrev4(int x) {

@@ -49,9 +49,10 @@ float softmax_scale(const mla_dims* d) {
 }
 
 // Decode split plan: tokens per split (multiple of 32) and splits per (sequence, head).
-// The bf16 fast path covers MLA with a 512-wide latent (+ rotary 64) and MLRA with four
-// latent blocks of 128; it runs one 256-thread workgroup per CU (its LDS pipeline takes
-// most of the CU's 160 KB), so the plan aims at whole waves of 256 workgroups.
+// The bf16 fast path covers MLA with a 512-wide latent (+ rotary 64), one workgroup per
+// (sequence, split, 64 heads), and MLRA with four latent blocks of 128; either runs one
+// workgroup per CU (its LDS pipeline takes most of the CU's 160 KB), so the plan aims at
+// whole waves of 256 workgroups.
 struct SplitPlan {
   int chunk, nsplit, head_tiles, dl, dr, nw;
   int fast_variant;   // -1: generic kernel
@@ -77,7 +78,7 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
   const int ntok = max_ctx + 1;
   int chunk;
   if (sp.fast_variant >= 0) {
-    sp.fast_head_tiles = sp.fast_variant == 2 ? 1 : cdiv(hpb, 128);
+    sp.fast_head_tiles = sp.fast_variant == 2 ? 1 : cdiv(hpb, 64);
     const long long wgs = (long long)B * sp.fast_head_tiles;
     int ns = (int)((kCUs + wgs - 1) / wgs);
     chunk = round_up(cdiv(ntok, ns < 1 ? 1 : ns), 32);

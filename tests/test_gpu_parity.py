@@ -284,6 +284,49 @@ def test_decode_attention_score_spikes(gu, spike_at):
     gu.assert_close(gu.to_host(z), want, cfg.dtype, f"z spikes at {spike_at}")
 
 
+@pytest.mark.parametrize("spike", [False, True], ids=["plain", "spikes"])
+def test_decode_attention_many_tiles_per_split(gu, spike):
+    """64 sequences (few splits per sequence, so each split spans many 32-token tiles and
+    every LDS stage is reused) with mixed context lengths; random bf16 cache rows and
+    queries.  With spikes, one row per sequence aligned with the query far into the
+    context forces the exact-maximum re-stream over many tiles.  Sampled sequences are
+    compared with the oracle."""
+    import head_latent_attention_dkv_amd as M
+    cfg = DSV2
+    lay = layer(gu, cfg)
+    d = _dims(cfg)
+    rng = np.random.default_rng(21 + int(spike))
+    B, H, rb = 64, cfg.n_heads, cfg.r_kv
+    ctx = [int(c) for c in rng.integers(100, 900, B)]
+    ctx[5] = 0
+    ctx[6] = 31
+    ctx[7] = 899
+    gu.say(f"[decode_attention many tiles] spike={spike} ctx[:8]={ctx[:8]}")
+    max_seq = max(ctx) + 1
+    ckv_h = S.round_bf16(rng.standard_normal((B, max_seq, rb)).astype(np.float32))
+    kr_h = S.round_bf16(rng.standard_normal((B, max_seq, cfg.d_rope)).astype(np.float32))
+    q_lat = S.round_bf16(rng.standard_normal((B, H, rb)).astype(np.float32))
+    q_rope = S.round_bf16(rng.standard_normal((B, H, cfg.d_rope)).astype(np.float32))
+    if spike:
+        for b in range(B):
+            at = (ctx[b] * 3) // 4
+            ckv_h[b, at] = S.round_bf16(2.0 * q_lat[b, b % H])
+    ckv, kr = gu.to_dev(ckv_h, cfg), gu.to_dev(kr_h, cfg)
+    z = torch.empty((B, H, rb), dtype=gu.tdtype(cfg), device="cuda")
+    cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    ws, nbytes = lay.workspace(M.MLA_OP_DECODE_ATTENTION, B, max(ctx))
+    M.mla_decode_attention(lay.dims, gu.to_dev(q_lat, cfg), gu.to_dev(q_rope, cfg), B, cl, max(ctx),
+                           M.cache_struct(ckv, kr, B, max_seq), z, ws, nbytes)
+    z_h = gu.to_host(z)
+    for b in [0, 5, 6, 7, 40, 63]:
+        n = ctx[b] + 1
+        want = np.zeros((H, rb))
+        for h in range(H):
+            want[h] = O.latent_attention(q_lat[b, h][None], q_rope[b, h][None], ckv_h[b, :n], kr_h[b, :n],
+                                         d.scale())[0]
+        gu.assert_close(z_h[b], want, cfg.dtype, f"z b={b} ctx={ctx[b]}")
+
+
 def test_prefill_attention_exact_max_restream(gu):
     """Scores that rise far above the first key tile's maximum (the flash kernel's fixed
     softmax reference): the first 32 latent and rotary-key rows are zero (score 0 for every
