@@ -140,7 +140,8 @@ def timed(torch, fn, steps, warmup, stats=None):
 # Sources of each measured kernel unit (a stored counter measurement is valid only for them).
 UNIT_SOURCES = {
     "dsv2_decode_attention": ("decode_fast.hip", "decode.hip", "lds_dma.h", "common.h", "internal.h"),
-    "dsv2_prefill_attention": ("prefill.hip", "gemm.hip", "gemm_epilogue.h", "common.h", "internal.h"),
+    "dsv2_prefill_attention": ("prefill_fast.hip", "prefill.hip", "gemm.hip", "gemm_big.hip", "gemm_epilogue.h",
+                               "lds_dma.h", "common.h", "internal.h"),
 }
 
 
@@ -332,7 +333,7 @@ def summarize_profiles(d):
         return vals
 
     def unit_kib(sub, counter):
-        v = per_dispatch(sub, counter, lambda n: "decode_wide_kernel" in n or "combine_kernel" in n)
+        v = per_dispatch(sub, counter, lambda n: "decode_hg64_kernel" in n or "combine_kernel" in n)
         by = {}
         for (name, _), x in v.items():
             by.setdefault("combine" if "combine_kernel" in name else "split", []).append(x)
@@ -439,6 +440,27 @@ def summarize_profiles(d):
               f"Kernel sources digest: {rec['src_digest']}", ""]
     with open(os.path.join(PROFILES, "dsv2_decode_step_kernels.md"), "w") as fh:
         fh.write("\n".join(lines))
+
+    # kernel times of `bench.py --only prefill_attention` (d/prefill_stats)
+    pstats = rows("prefill_stats", "*kernel_stats.csv")
+    if pstats:
+        pl = ["# Kernel times: DeepSeek-V2-shaped prefill attention (B=4, S=4096, H=128, d_nope=128, "
+              "d_rope=64, r_kv=512)", "",
+              "Command (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
+              "```",
+              "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/prefill_stats -o run -- "
+              "python3 bench.py --only prefill_attention --steps 8 --warmup 2",
+              "python3 bench.py --summarize <dir>",
+              "```", "",
+              "mla_prefill_attention = K/V up-projection GEMM (gemm_big_kernel, writes head-major K and "
+              "token-permuted V^T) + flash causal attention (prefill_flash_kernel).", "",
+              "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+        for r in pstats[:8]:
+            pl.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        pl += ["", f"Kernel sources digest: {src_digest(*UNIT_SOURCES['dsv2_prefill_attention'])}", ""]
+        with open(os.path.join(PROFILES, "dsv2_prefill_attention_kernels.md"), "w") as fh:
+            fh.write("\n".join(pl))
 
 
 def main():
