@@ -216,6 +216,7 @@ hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream
   for (int i = 0; i < p.nseg; ++i)
     if (p.seg[i].rope == ROPE_HALFSPLIT && p.seg[i].rope_d > max_rope_d) max_rope_d = p.seg[i].rope_d;
   if (!use_bf16) return launch_tile<float, 64, 64>(p, groups, s);
+  if (kmajor_small_supported(p, groups)) return launch_kmajor_small(p, groups, s);
   if (skinny_supported(p, groups)) return launch_skinny(p, groups, s);
   if (gemm_big_supported(p, groups)) return launch_gemm_big(p, groups, s);
   bool big = (long long)cdiv(p.M, 128) * cdiv(N, 128) * groups >= 512;

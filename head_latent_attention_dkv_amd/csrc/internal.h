@@ -86,6 +86,9 @@ bool skinny_supported(const GemmParams& p, int groups);
 hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s);
 // workspace bytes launch_skinny uses for split-K partials of an M x N x K product
 size_t skinny_ws_bytes(int M, int N, int K, int groups);
+// Few-row (M <= 256) grouped product with a k-major weight (absorbed queries).
+bool kmajor_small_supported(const GemmParams& p, int groups);
+hipError_t launch_kmajor_small(const GemmParams& p, int groups, hipStream_t s);
 // Many-row (M >= 256) bf16 path: 256 x 256 tiles streamed through LDS.
 bool gemm_big_supported(const GemmParams& p, int groups);
 // Vectorised epilogue preconditions: 8-element runs never straddle a segment or a head,
