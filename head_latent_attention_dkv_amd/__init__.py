@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        # PyTorch ships its own HIP runtime under the same soname: load it first so that the
+        # library binds to the runtime that owns the tensors and streams handed to it (loaded
+        # the other way round, calls fail with MLA_ERR_HIP or launch nothing)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         D, W, C = ctypes.POINTER(mla_dims), ctypes.POINTER(mla_weights), ctypes.POINTER(mla_cache)

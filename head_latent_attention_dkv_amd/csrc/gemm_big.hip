@@ -5,9 +5,14 @@
 // advances 32 at a time through NST LDS stages filled by 16-byte direct-to-LDS copies:
 // each copy instruction moves 16 rows x 64 bytes of A or of W.  Rows are 64 bytes (four
 // 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), which puts the 8 rows of
-// one LDS read phase (row stride 64 B) on 8 distinct 16-byte bank windows.  The epilogue
-// goes through LDS per wave, 32 rows at a time, into the shared output stage (rotary
-// pairs, head scatter, cache rows, head-major / transposed layouts).
+// one LDS read phase (row stride 64 B) on 8 distinct 16-byte bank windows.
+//
+// Output stages:
+//   * the keys / values of flash prefill (every wave's 128 columns inside one head of one
+//     segment, bf16, no rotation) are written straight from the accumulators (values,
+//     transposed) or through a small bf16 transpose in LDS (keys, head-major);
+//   * everything else goes through LDS per wave, 32 rows at a time, into the shared output
+//     stage (rotary pairs, head scatter, cache rows, head-major / transposed layouts).
 #include <type_traits>
 
 #include "common.h"
@@ -26,6 +31,12 @@ constexpr int G_CPW = (G_AB / 1024) / 4;            // copies per wave per opera
 constexpr int G_LDC = 128 + 4;                      // epilogue LDS row stride (floats)
 constexpr size_t G_LDS = (size_t)GNST * G_STAGE;    // 128 KB
 static_assert((size_t)4 * 32 * G_LDC * 4 <= G_LDS, "epilogue chunks fit in the stages");
+constexpr int KV_CS = 72;                           // bf16 column stride (bytes) of the key transpose
+constexpr int KV_BUF = 128 * KV_CS;                 // one 32-row x 128-column chunk
+static_assert((size_t)4 * 2 * KV_BUF <= G_LDS, "key transpose buffers fit in the stages");
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ long long big_a_row(const GemmParams& p, int m) {
   if (!p.a_cache) return m;
@@ -38,6 +49,9 @@ __device__ __forceinline__ int opaque_int(int x) {
   return x;
 }
 
+// DIRECT: the flash-layout output stage (own instantiation: sharing one register allocation
+// with the generic stage costs spills)
+template <bool DIRECT>
 __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -104,25 +118,107 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
     if (it + GNST - 1 < nst) issue(it + GNST - 1);
     const unsigned char* T = smem + (it % GNST) * G_STAGE;
     const int rb0 = opaque_int(rd_base);
+    Frag<bf16> fa[2][4], fb[2][4];
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
       const int off = rb0 ^ (ks << 5);
-      Frag<bf16> fa[4], fb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[i] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off + (128 * wm + 32 * i) * 64));
+        fa[ks][i] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off + (128 * wm + 32 * i) * 64));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        fb[j] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + G_AB + off + (128 * wn + 32 * j) * 64));
+        fb[ks][j] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + G_AB + off + (128 * wn + 32 * j) * 64));
+    }
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mma32(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma32(fa[ks][i], fb[ks][j], acc[i][j]);
+    // issue order: the first step's 8 operand reads, then its 16 products with the second
+    // step's 8 reads slotted in after every other product, then the second step's products
+    // (one wave per SIMD: nothing else hides an LDS read issued just before its use)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
   }
   wait_vmcnt<0>();
   __syncthreads();
 
+  if constexpr (DIRECT) {
+    // Flash layouts.  The wave's columns N0 .. N0 + 127 are columns j0 .. j0 + 127 of one head.
+    const int N0 = n0 + 128 * wn;
+    if (N0 >= N) return;
+    const int s = N0 < p.seg[0].n ? 0 : 1;
+    const GemmSeg& sg = p.seg[s];
+    const int cc = N0 - (s ? p.seg[0].n : 0) + (int)o_goff;
+    const int head = cc / sg.out_hw, j0 = cc - head * sg.out_hw;
+    bf16* out = reinterpret_cast<bf16*>(sg.out);
+    if (sg.layout == OUT_HEAD_T16) {
+      // Row j of a head holds the tokens in perm16 order: positions 8 u .. 8 u + 7 of a
+      // 16-token group are tokens 4 u .. 4 u + 3 and 8 + 4 u .. 8 + 4 u + 3, i.e. the
+      // accumulator elements 8 g .. 8 g + 7 of the lanes with l / 32 = u (rows
+      // 16 g + 4 u + e % 4 and 16 g + 8 + 4 u + e % 4).  One 16-byte store per lane,
+      // 32-column block and 16-token group.
+      const long long jstride = 32LL * sg.out_ld;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 128 * wm + 32 * i;
+        if (m >= p.M) break;
+        const int b = m / p.rows_per_batch, t = m - b * p.rows_per_batch;
+        bf16* base = out + ((long long)(b * sg.out_nh + head) * sg.out_hw + j0 + col) * sg.out_ld + t + 8 * half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (bf16)acc[i][j][8 * g + e];
+            *reinterpret_cast<bf16x8*>(base + j * jstride + 16 * g) = o;
+          }
+      }
+    } else {
+      // Head-major rows: chunk i (32 rows) goes to LDS column-major as bf16 (column stride
+      // 72 B: the 16 columns of one write phase fall on distinct bank pairs); the LDS
+      // transpose load then hands lane x of a 16-lane group 4 consecutive columns of row
+      // r0 + x, and two loads make one 16-byte store.
+      unsigned char* ct = smem + wave * 2 * KV_BUF;
+      const int g16 = lane >> 4, x16 = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 128 * wm + 32 * i;
+        if (m >= p.M) break;
+        const int b = m / p.rows_per_batch, t = m - b * p.rows_per_batch;
+        unsigned char* buf = ct + (i & 1) * KV_BUF;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[i][j][4 * q + e];
+            *reinterpret_cast<bf16x4*>(buf + (32 * j + col) * KV_CS + (8 * q + 4 * half) * 2) = o;
+          }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        bf16* base = out + ((long long)(b * sg.out_nh + head) * p.rows_per_batch + t) * sg.out_hw + j0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r0 = 16 * (u & 1), c0 = 32 * (u >> 1) + 8 * g16;
+          const unsigned char* rd = buf + (c0 + (x16 >> 2)) * KV_CS + (r0 + 4 * (x16 & 3)) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(rd));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(rd + 4 * KV_CS));
+          const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          *reinterpret_cast<s16x8*>(base + (r0 + x16) * sg.out_hw + c0) = v;
+        }
+      }
+    }
+  } else {
   // Epilogue per wave: its 128 x 128 block in four chunks of 32 rows.  Accumulator element
   // e of lane l in block (i, j) is out[128 wm + 32 i + 8 (e/4) + 4 (l/32) + e%4][128 wn + 32 j + l%32].
   float* Cs = reinterpret_cast<float*>(smem) + wave * 32 * G_LDC;
@@ -149,6 +245,7 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
       epilogue_block<bf16>(p, Cs, G_LDC, m0 + 128 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane, 64);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
+  }
   }
 }
 
@@ -195,12 +292,30 @@ bool gemm_fast_epilogue_ok(const GemmParams& p, int groups) {
   return true;
 }
 
+// Flash-layout output stage: bf16 head-major / transposed segments without rotation, every
+// 128-column block inside one head of one segment, 32-row chunks inside one sequence.
+static bool kv_direct_ok(const GemmParams& p) {
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  if (N % 128 != 0 || p.rows_per_batch % 32 != 0 || p.M % 32 != 0) return false;
+  for (int i = 0; i < 2; ++i)
+    if (p.o_goff[i] % 128 != 0) return false;
+  for (int i = 0; i < p.nseg; ++i) {
+    const GemmSeg& sg = p.seg[i];
+    if (sg.layout == OUT_ROWS || sg.out_f32 || sg.rope != ROPE_OFF) return false;
+    if (sg.n % 128 != 0 || sg.out_hw % 128 != 0) return false;
+  }
+  return true;
+}
+
 hipError_t launch_gemm_big(const GemmParams& pin, int groups, hipStream_t s) {
   GemmParams p = pin;
-  p.fast_epilogue = gemm_fast_epilogue_ok(p, groups) ? 1 : 0;
+  p.fast_epilogue = gemm_fast_epilogue_ok(p, groups) ? (kv_direct_ok(p) ? 2 : 1) : 0;
   const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
   dim3 grid(cdiv(N, GBN), cdiv(p.M, GBM), groups);
-  hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(256), G_LDS, s, p);
+  if (p.fast_epilogue == 2)
+    hipLaunchKernelGGL(gemm_big_kernel<true>, grid, dim3(256), G_LDS, s, p);
+  else
+    hipLaunchKernelGGL(gemm_big_kernel<false>, grid, dim3(256), G_LDS, s, p);
   return hipGetLastError();
 }
 

@@ -76,7 +76,7 @@ struct GemmParams {
   float* part;
   size_t part_bytes;
   int splits, kchunk;
-  int fast_epilogue;        // set by the launcher when gemm_fast_epilogue_ok()
+  int fast_epilogue;        // set by the launcher: 0 generic, 1 vectorised, 2 flash layouts direct
 };
 
 hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream_t s);
