@@ -20,6 +20,7 @@
 // the two lane halves) against a fixed reference maximum (see the pass below).  16-byte
 // chunks are XOR-swizzled per row so that operand reads of 8 rows hit distinct LDS banks.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "internal.h"
@@ -37,9 +38,16 @@ constexpr int FNST = 3;          // LDS stages
 #endif
 constexpr int kFlashQB = MLA_FLASH_QB;   // 32-query blocks per wave (waves per workgroup = 8 / QB)
 constexpr float kFlashGap = 64.0f;    // log2 units: p <= 2^64 stays far from bf16 / fp32 overflow
+constexpr float kFlashLimit = 0x1p64f;  // 2^kFlashGap
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define kOnes2 ((bf16x2){(__bf16)1.0f, (__bf16)1.0f})
+
+// f(integral_constant<LO + i>) for i in the sequence, in order, fully unrolled
+template <int LO, typename F, int... I>
+__device__ __forceinline__ void unroll_from(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, LO + I>{}), ...);
+}
 
 __device__ __forceinline__ int opaque_i(int x) {
   asm volatile("" : "+v"(x));
@@ -173,22 +181,180 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
-  // Softmax reference per query column: the maximum of its first key tile.  p = 2^(s - m_ref)
-  // stays exact in bf16 / fp32 while s - m_ref < kFlashGap; a wave whose scores rise
-  // further stops accumulating but keeps tracking its exact maximum (m_seen), and the
-  // workgroup then re-streams the keys once with that maximum as the reference.  No
-  // accumulator rescale sits in the loop.
-  float m_ref[QB], m_seen[QB], l_run[QB];
+  // Softmax reference per query column: the maximum of its first key tile (key 0 is visible
+  // to every query, so the reference never exceeds the exact maximum and the denominator is
+  // at least 1).  p = 2^(s - m_ref) is exact in bf16 / fp32 while s - m_ref < kFlashGap.
+  // Every p is non-negative and so bounded by its lane's running sum: one test of the sums
+  // after the pass tells whether a score rose further.  The workgroup then finds the exact
+  // maximum (scores only) and runs the pass again with it as the reference.  No accumulator
+  // rescale and no per-tile maximum sit in the loop.
+  float m_ref[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_ref[qb] = -INFINITY;
-    m_seen[qb] = -INFINITY;
     l_run[qb] = 0.f;
   }
   bool redo = false;
 
-  auto pass = [&](auto second_pass) {
-    constexpr bool SECOND = decltype(second_pass)::value;
+  // One key tile of one wave.  MODE 0: accumulate against the first tile's maximum (first:
+  // this is that tile); MODE 1: exact maximum only; MODE 2: accumulate against the exact
+  // maximum.  diag: the tile holds keys after some of the wave's queries (causal mask).
+  // first / diag are wave-uniform run-time flags: one instruction stream serves all tiles.
+  auto tile = [&](const unsigned char* T, int key0, auto mode_c, bool first, bool diag) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr bool STREAM = MODE != 1;
+    // per-lane address bases, kept opaque so the compiler rebuilds (not hoists) addresses
+    const int kn_b = opaque_i(kn_base), kr_b = opaque_i(kr_base), v_b = opaque_i(v_base);
+    auto kfrag = [&](int kb, int ks) {
+      const int off = ks < C::KSN ? (kn_b ^ (ks << 5)) + kb * 32 * DN * 2
+                                  : (kr_b ^ ((ks - C::KSN) << 5)) + kb * 32 * DR * 2;
+      return frag_load<bf16>(reinterpret_cast<const bf16*>(T + off));
+    };
+    // scores S^T[32 keys x QW queries] of tile half kb (K index = feature)
+    auto scores = [&](int kb, f32x16 (&sc)[QB]) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const Frag<bf16> fa = kfrag(kb, ks);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb] = mma32(fa, qf[qb][ks], sc[qb]);
+      }
+    };
+    auto mask = [&](int kb, f32x16 (&sc)[QB]) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qi = qw + 32 * qb + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3) > qi) sc[qb][i] = -INFINITY;
+      }
+    };
+    // scaled maximum over both halves of the tile, both lane halves (log2 units)
+    auto tile_max = [&](const f32x16 (&a)[QB], const f32x16 (&c)[QB], int qb) {
+      float mx = fmaxf(a[qb][0], c[qb][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(a[qb][i], c[qb][i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      return mx * p.scale_log2;
+    };
+    f32x16 s0[QB], s1[QB];
+    Frag<bf16> pf0[QB][2], pf1[QB][2];
+    if constexpr (STREAM) {
+      // Accumulating tile, one explicit instruction stream: operand n (K fragments of both
+      // halves, then V^T fragments of both halves) is read 4 steps before its products (one
+      // per 32-query block); the exponentials of half 0 ride between the products of half
+      // 1's scores, those of half 1 between the first half's value products.  sched_barrier
+      // keeps every step in place.  The first tile takes the reference maximum from its
+      // first half (keys 0..31, key 0 visible to every query: still at most the exact
+      // maximum); diagonal tiles mask each half before its exponentials.
+      constexpr int KS = C::KS, NV = 2 * C::DB, NOP = 2 * KS + 2 * NV, PF = 4, NE = 16 * QB;
+      auto operand = [&](int n) {
+        if (n < 2 * KS) return kfrag(n / KS, n % KS);
+        const int r = n - 2 * KS, kb = r / NV, t = (r % NV) / C::DB, db = r % C::DB;
+        return frag_load<bf16>(reinterpret_cast<const bf16*>(T + (v_b ^ ((2 * kb + t) << 5)) + db * 32 * FK * 2));
+      };
+      float nm[QB], ps[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ps[qb] = l_run[qb];
+      float pv0[QB][16], pv1[QB][16];
+      // probability x = 16 qb + e of a half: exponential, and on every odd e the bf16 pair
+      // and its contribution to the denominator
+      auto prob = [&](const f32x16 (&sc)[QB], float (&pv)[QB][16], Frag<bf16> (&pf)[QB][2], int x) {
+        const int qb = x >> 4, e = x & 15;
+        pv[qb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][e], p.scale_log2, nm[qb]));
+        if (e & 1) {
+          pf[qb][e >> 3].v[(e & 7) - 1] = (bf16)pv[qb][e - 1];
+          pf[qb][e >> 3].v[e & 7] = (bf16)pv[qb][e];
+          ps[qb] = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[qb][e >> 3].v[(e & 7) - 1], pf[qb][e >> 3].v[e & 7]},
+                                                   kOnes2, ps[qb], false);
+        }
+      };
+      Frag<bf16> ring[PF + 1];
+#pragma unroll
+      for (int n = 0; n < PF; ++n) ring[n] = operand(n);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s0[qb] = f32x16{};
+        s1[qb] = f32x16{};
+      }
+      // step n: its products, the read of operand n + PF, and its share of exponentials
+      auto step = [&](auto n_c) {
+        constexpr int n = decltype(n_c)::value;
+        const Frag<bf16>& op = ring[n % (PF + 1)];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          if constexpr (n < KS) {
+            s0[qb] = mma32(op, qf[qb][n], s0[qb]);
+          } else if constexpr (n < 2 * KS) {
+            s1[qb] = mma32(op, qf[qb][n - KS], s1[qb]);
+          } else {
+            constexpr int r = n - 2 * KS, kb = r / NV, t = (r % NV) / C::DB, db = r % C::DB;
+            oacc[db][qb] = mma32(op, kb ? pf1[qb][t] : pf0[qb][t], oacc[db][qb]);
+          }
+        }
+        if constexpr (n + PF < NOP) ring[(n + PF) % (PF + 1)] = operand(n + PF);
+        if constexpr (n >= KS && n < 2 * KS) {
+          constexpr int k = n - KS;
+#pragma unroll
+          for (int x = (NE * k) / KS; x < (NE * (k + 1)) / KS; ++x) prob(s0, pv0, pf0, x);
+        } else if constexpr (n >= 2 * KS && n < 2 * KS + NV) {
+          constexpr int k = n - 2 * KS;
+#pragma unroll
+          for (int x = (NE * k) / NV; x < (NE * (k + 1)) / NV; ++x) prob(s1, pv1, pf1, x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto steps = [&](auto lo_c, auto hi_c) {
+        constexpr int lo = decltype(lo_c)::value, hi = decltype(hi_c)::value;
+        unroll_from<lo>(step, std::make_integer_sequence<int, hi - lo>{});
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using IK = std::integral_constant<int, KS>;
+      using I2K = std::integral_constant<int, 2 * KS>;
+      using IN = std::integral_constant<int, NOP>;
+      __builtin_amdgcn_sched_barrier(0);
+      steps(I0{}, IK{});                       // half 0 scores
+      if (diag) {
+        asm volatile("; diagonal tile");        // keeps these branches
+        mask(0, s0);
+      }
+      if (MODE == 0 && first) {
+        asm volatile("; first tile");
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float mx = s0[qb][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[qb][i]);
+          m_ref[qb] = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) nm[qb] = -m_ref[qb];
+      __builtin_amdgcn_sched_barrier(0);
+      steps(IK{}, I2K{});                      // half 1 scores | half 0 exponentials
+      if (diag) {
+        asm volatile("; diagonal tile");
+        mask(1, s1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      steps(I2K{}, IN{});                      // value products | half 1 exponentials
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] = ps[qb];
+      return;
+    }
+    // exact-maximum pass: scores only
+    scores(0, s0);
+    if (diag) mask(0, s0);
+    scores(1, s1);
+    if (diag) mask(1, s1);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = fmaxf(m_ref[qb], tile_max(s0, s1, qb));
+  };
+
+  auto pass = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    using M0 = std::integral_constant<int, MODE>;
 #pragma unroll
     for (int s = 0; s < FNST - 1; ++s)
       if (s < ntiles) issue(s);
@@ -199,122 +365,18 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
       if (it + FNST - 1 < ntiles) issue(it + FNST - 1);
       const int key0 = it * FK;
       if (key0 > qw + QW - 1) continue;                     // every key of the tile is after this wave's queries
-      if (SECOND && !redo) continue;
-
+      if (MODE != 0 && !redo) continue;
       const unsigned char* T = smem + (it % FNST) * C::STAGE;
-      // per-lane address bases, kept opaque so the compiler rebuilds (not hoists) addresses
-      const int kn_b = opaque_i(kn_base), kr_b = opaque_i(kr_base), v_b = opaque_i(v_base);
-
-      const bool diag = key0 + 63 > qw;                 // some keys after some of this wave's queries
-      // Half kb of the tile: scores S^T[32 keys x 64 queries], causal mask, maxima (log2 units)
-      auto kfrag = [&](int kb, int ks) {
-        const int off = ks < C::KSN ? (kn_b ^ (ks << 5)) + kb * 32 * DN * 2
-                                    : (kr_b ^ ((ks - C::KSN) << 5)) + kb * 32 * DR * 2;
-        return frag_load<bf16>(reinterpret_cast<const bf16*>(T + off));
-      };
-      // operand reads run two k-steps ahead of the MFMAs that consume them
-      auto scores = [&](int kb, f32x16 (&sc)[QB]) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb] = f32x16{};
-        Frag<bf16> fa[3];
-        fa[0] = kfrag(kb, 0);
-        fa[1] = kfrag(kb, 1);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          if (ks + 2 < C::KS) fa[(ks + 2) % 3] = kfrag(kb, ks + 2);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sc[qb] = mma32(fa[ks % 3], qf[qb][ks], sc[qb]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int ks = 0; ks < C::KS - 2; ++ks) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      };
-      auto mask_max = [&](int kb, f32x16 (&sc)[QB], float (&mt)[QB]) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qi = qw + 32 * qb + col;
-          if (diag) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3) > qi) sc[qb][i] = -INFINITY;
-          }
-          float mx = sc[qb][0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[qb][i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          mt[qb] = mx * p.scale_log2;
-        }
-      };
-      auto track = [&](const float (&mt)[QB], bool first) {
-        if constexpr (!SECOND) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            m_seen[qb] = fmaxf(m_seen[qb], mt[qb]);
-            if (first) m_ref[qb] = mt[qb];                // key 0 is visible to every query
-            if (__builtin_amdgcn_readfirstlane(__any(mt[qb] > m_ref[qb] + kFlashGap))) redo = true;
-          }
-        }
-      };
-      // p = 2^(scale s - m_ref) (raw v_exp_f32: the argument stays below kFlashGap unless the
-      // wave is re-streaming anyway, and -inf gives 0)
-      auto probs = [&](const f32x16 (&sc)[QB], Frag<bf16> (&pf)[QB][2]) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float nm = -m_ref[qb];
-          float ps = l_run[qb];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            float pv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][8 * t + j], p.scale_log2, nm));
-            pf[qb][t] = frag_from_f32<bf16>(pv);
-            // the denominator sums the same bf16 probabilities the products use
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              ps = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[qb][t].v[2 * j], pf[qb][t].v[2 * j + 1]}, kOnes2, ps, false);
-          }
-          l_run[qb] = ps;
-        }
-      };
-      auto pv_products = [&](int kb, const Frag<bf16> (&pf)[QB][2]) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const int off = (v_b ^ ((2 * kb + t) << 5)) + db * 32 * FK * 2;
-            const Frag<bf16> fv = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off));
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mma32(fv, pf[qb][t], oacc[db][qb]);
-          }
-      };
-
-      // Order: S0, mask/max 0, [S1 MFMAs | exponentials of half 0], mask/max 1,
-      // [P0 V products | exponentials of half 1], P1 V products.  A wave that must re-stream
-      // keeps computing scores and maxima (exact maximum) but adds nothing to O.
-      f32x16 s0[QB], s1[QB];
-      float mt0[QB], mt1[QB];
-      Frag<bf16> pf0[QB][2], pf1[QB][2];
-      scores(0, s0);
-      mask_max(0, s0, mt0);
-      track(mt0, it == 0);
-      probs(s0, pf0);
-      scores(1, s1);
-      mask_max(1, s1, mt1);
-      track(mt1, false);
-      if (SECOND || !redo) {
-        pv_products(0, pf0);
-        probs(s1, pf1);
-        pv_products(1, pf1);
-      }
+      const bool diag = key0 + 63 > qw;                     // some keys after some of this wave's queries
+      tile(T, key0, M0{}, it == 0, diag);
     }
   };
 
-  pass(std::false_type{});
-  // workgroup-wide vote: does any wave need the exact-maximum pass?
+  pass(std::integral_constant<int, 0>{});
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    if (__builtin_amdgcn_readfirstlane(__any(!(l_run[qb] <= kFlashLimit)))) redo = true;
+  // workgroup-wide vote: does any wave need the exact-maximum passes?
   __shared__ int redo_flag;
   wait_vmcnt<0>();
   if (threadIdx.x == 0) redo_flag = 0;
@@ -329,11 +391,14 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        m_ref[qb] = m_seen[qb];
+        m_ref[qb] = -INFINITY;
         l_run[qb] = 0.f;
       }
     }
-    pass(std::true_type{});
+    pass(std::integral_constant<int, 1>{});
+    wait_vmcnt<0>();
+    __syncthreads();
+    pass(std::integral_constant<int, 2>{});
     wait_vmcnt<0>();
   }
 
