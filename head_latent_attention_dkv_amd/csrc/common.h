@@ -17,7 +17,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace mla {
+
+// f(integral_constant<LO + i>) for i in the sequence, in order, fully unrolled
+template <int LO, typename F, int... I>
+__device__ __forceinline__ void unroll_from(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, LO + I>{}), ...);
+}
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

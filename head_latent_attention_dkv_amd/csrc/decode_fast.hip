@@ -598,6 +598,283 @@ __global__ void __launch_bounds__(512, 1) decode_hg64_kernel(DecodeParams p) {
   }
 }
 
+// 128-head variant for the latent-512 case (MLA with one latent block): one workgroup per
+// (sequence, split) streams each cache tile once for all heads.  4 waves, one per SIMD;
+// wave w owns heads 32w..32w+31 for both products, so a head's softmax never leaves its wave:
+//   scores  S^T[32 tokens x 32 heads] = C_tile[32 x (512+VR)] . Q^T   (32x32x16 MFMA, K =
+//           feature; the k-steps alternate between two accumulators so that a single wave
+//           does not wait on one dependent chain);
+//   values  Z^T[512 x 32 heads] += C_tile^T[512 x 32 tokens] . P^T   (16 column blocks x 2
+//           k-steps of 16 tokens; C^T comes from the LDS transpose load).
+// Score lane l holds head l%32 at tokens 8(e/4) + 4(l/32) + e%4; read as a k-step of 16
+// tokens, those are tokens {4h..4h+3, 8+4h..8+4h+3} (h = l/32), which the transpose load
+// hands the value MFMA in the same order, so P^T is the B operand straight from registers.
+// Each tile runs as one explicit instruction stream: score operands read 4 steps ahead of
+// their products, the value operands of the first column blocks in flight during the
+// exponentials, then the value products with their operands read ahead.
+// Registers: Q (32 heads x 576 bf16) 144, z accumulators (512 x 32 fp32) 256 per wave.
+template <int VR, int NSTAGE>
+__global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
+  constexpr int VL = 512, NWV = 4;
+  using C = FastCfg<VL, VR, NWV, NSTAGE>;
+  constexpr int KSL = VL / 16, KSR = VR / 16, KS = KSL + KSR;   // 16-wide k-steps (36 or 32)
+  constexpr int RPW = TT / NWV;                       // latent rows per wave per tile (8)
+  constexpr int DMA_PER_WAVE = RPW + (VR ? 1 : 0);    // + one 8-row rotary copy
+  constexpr int MBS = VL / 32;                        // 32-column blocks of z (16)
+  constexpr int SPF = 4, VPF = 4;                     // score / value operands read ahead
+  static_assert(NSTAGE == 4, "three tiles in flight");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  int* const vote = reinterpret_cast<int*>(smem_raw + C::LDS);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int i16 = lane & 15, g16 = lane >> 4;
+
+  const int hg = blockIdx.x % p.head_tiles;
+  const int pair = blockIdx.x / p.head_tiles;
+  const int b = pair / p.nsplit;
+  const int split = pair - b * p.nsplit;
+  const int n_tok = p.ctx_len[b] + 1;
+  const int tok_begin = split * p.chunk;
+  if (tok_begin >= n_tok) return;
+  const int tok_end = min(n_tok, tok_begin + p.chunk);
+  const int ntiles = (tok_end - tok_begin + TT - 1) / TT;
+
+  const int head = hg * 128 + 32 * wave + col;
+  const bool head_ok = head < p.hpb;
+
+  // ---- copies: latent row t of a tile is one wave-wide 1 KB load at chunk ln ^ bitrev4(t);
+  // the wave's 8 rotary rows are one 1 KB load (lane -> row 8 wave + ln/8, chunk ln%8) ----
+  const unsigned char* ckv_seq = reinterpret_cast<const unsigned char*>(p.ckv) + (long long)b * p.cache_bstride * (VL * 2);
+  const unsigned char* kr_seq = reinterpret_cast<const unsigned char*>(p.kr) + (long long)b * p.cache_bstride * (VR * 2);
+  const uint32_t lds_base = lds_addr_of(smem_raw);
+  auto issue_tile = [&](int tile, int stage) {
+    const int t0 = tok_begin + tile * TT;
+    const uint32_t sbase = lds_base + stage * C::STAGE_BYTES;
+    const int ln = opaque(lane);
+    const uint32_t ln16 = (uint32_t)ln << 4;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int t = wave * RPW + i;                    // wave-uniform
+      const int tok = min(t0 + t, tok_end - 1);
+      const uint32_t key16 = (uint32_t)bitrev4(t & 15) << 4;
+      dma16_s(ckv_seq + (long long)tok * (VL * 2), ln16 ^ key16, __builtin_amdgcn_readfirstlane(sbase + t * 1024));
+    }
+    if constexpr (VR > 0) {
+      const int t = wave * RPW + (ln >> 3);
+      const int tok = min(t0 + t, tok_end - 1);
+      const uint32_t c = (uint32_t)(((ln & 7) ^ ((t >> 1) & 7)) << 4);
+      dma16_s(kr_seq, (uint32_t)tok * (VR * 2) + c, __builtin_amdgcn_readfirstlane(sbase + C::LAT_BYTES + wave * RPW * 128));
+    }
+  };
+
+  // ---- Q^T (B operand): lane holds head col, k = 16 ks + 8 half + [0..7]; all loads land
+  // before the first tile copy is issued ----
+  const int head_ld = head_ok ? head : 0;
+  const bf16* qlp = reinterpret_cast<const bf16*>(p.q_lat) + ((long long)b * p.H + head_ld) * p.q_lat_hs + 8 * half;
+  const bf16* qrp = reinterpret_cast<const bf16*>(p.q_rope) + ((long long)b * p.H + head_ld) * p.q_rope_hs + 8 * half;
+  Frag<bf16> qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_load<bf16>(ks < KSL ? qlp + 16 * ks : qrp + 16 * (ks - KSL));
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (!head_ok) qf[ks] = frag_zero<bf16>();
+    asm volatile("" ::"v"(qf[ks].v));
+  }
+
+  // ---- per-lane LDS byte offsets inside a stage.  The XOR swizzle only touches the low 4
+  // bits of a chunk index, so for a step index n = 8 j + r (scores) or 4 j + r (values) the
+  // address is base[r] + 256 j: a few base registers plus instruction offsets ----
+  // score operand (row = token col, logical chunk 2 ks + half of its latent row; rotary
+  // k-step ks' = ks - KSL at chunk 2 ks' + half of its 128-byte row)
+  int s_base[8], r_base[KSR ? KSR : 1];
+  {
+    const int f = bitrev4(col & 15), fr = (col >> 1) & 7;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s_base[r] = col * 1024 + (((2 * r + half) ^ f) << 4);
+#pragma unroll
+    for (int r = 0; r < (KSR ? KSR : 1); ++r) r_base[r] = C::LAT_BYTES + col * 128 + (((2 * r + half) ^ fr) << 4);
+  }
+  // value operand (transpose load): lane i16 of group g16 reads token row
+  // 16 kt + 8 hi + 4 half + i16/4, 8 bytes at latent column 32 mb + 16 (g16 % 2) + 4 (i16 % 4),
+  // i.e. logical chunk 4 mb + x: for mb = 4 j + r, v_base[hi][r] + 256 j + 16 KB kt
+  int v_base[2][4];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const int rr = 8 * hi + 4 * half + (i16 >> 2);
+    const int x = 2 * (g16 & 1) + ((i16 & 3) >> 1), f = bitrev4(rr);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v_base[hi][r] = rr * 1024 + 8 * (i16 & 1) + (((4 * r + x) ^ f) << 4);
+  }
+
+  f32x16 acc[MBS];
+#pragma unroll
+  for (int mb = 0; mb < MBS; ++mb) acc[mb] = f32x16{};
+  float m_ref = -INFINITY;   // reference maximum of this lane's head (log2 units)
+  float l_run = 0.f;         // this lane's share of the head's sum of p
+  bool redo = false;
+
+  // One tile.  MODE 0: accumulate against the first tile's maximum; MODE 1: exact maximum
+  // only; MODE 2: accumulate against the exact maximum.
+  auto tile = [&](int stage_off, int t0, bool first, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    // this stage's bases (one add each); every read is base + an instruction offset
+    int sb[8], rbs[KSR ? KSR : 1], vb[2][4];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sb[r] = s_base[r] + stage_off;
+#pragma unroll
+    for (int r = 0; r < (KSR ? KSR : 1); ++r) rbs[r] = r_base[r] + stage_off;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vb[hi][r] = v_base[hi][r] + stage_off;
+    auto sread = [&](int n) {
+      const unsigned char* src = n < KSL ? smem_raw + sb[n % 8] + 256 * (n / 8) : smem_raw + rbs[n - KSL];
+      return *reinterpret_cast<const bf16x8*>(src);
+    };
+    auto vread = [&](int n) {              // value operand n = 16 kt + mb
+      const int kt = n / MBS, mb = n % MBS;
+      const unsigned char* a0 = smem_raw + vb[0][mb % 4] + 256 * (mb / 4) + 16384 * kt;
+      const unsigned char* a1 = smem_raw + vb[1][mb % 4] + 256 * (mb / 4) + 16384 * kt;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a1);
+      const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    // scores: two accumulator chains over alternating k-steps
+    f32x16 sa = f32x16{}, sc = f32x16{};
+    bf16x8 sring[SPF + 1];
+#pragma unroll
+    for (int n = 0; n < SPF; ++n) sring[n] = sread(n);
+    __builtin_amdgcn_sched_barrier(0);
+    // (an empty asm reading one element of every fourth product of a chain keeps the pure
+    // MFMAs in their steps: without it the products sink to their first use and every
+    // operand read stays live at once)
+    auto sstep = [&](auto n_c) {
+      constexpr int n = decltype(n_c)::value;
+      if constexpr (n % 2 == 0) {
+        mma32_acc(sa, sring[n % (SPF + 1)], qf[n].v);
+        if constexpr (n % 8 == 6) asm volatile("" ::"v"(sa[0]));
+      } else {
+        mma32_acc(sc, sring[n % (SPF + 1)], qf[n].v);
+        if constexpr (n % 8 == 7) asm volatile("" ::"v"(sc[0]));
+      }
+      if constexpr (n + SPF < KS) sring[(n + SPF) % (SPF + 1)] = sread(n + SPF);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    unroll_from<0>(sstep, std::make_integer_sequence<int, KS>{});
+    // value operands of the first steps go out before the exponentials
+    bf16x8 vring[VPF + 1];
+    if constexpr (MODE != 1) {
+#pragma unroll
+      for (int n = 0; n < VPF; ++n) vring[n] = vread(n);
+    }
+    f32x16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = sa[e] + sc[e];
+    if (t0 + TT > tok_end) {                          // the ragged last tile only
+      asm volatile("; ragged tile");                  // keeps this a branch
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (t0 + 8 * (e >> 2) + 4 * half + (e & 3) >= tok_end) s[e] = -INFINITY;
+    }
+    if (MODE == 1 || first) {
+      float mx = s[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1])) * p.scale_log2;
+      m_ref = MODE == 1 ? fmaxf(m_ref, mx) : mx;
+    }
+    if constexpr (MODE == 1) return;
+    bf16x8 pf[2];
+    {
+      const float nm = -m_ref;
+      float ps = l_run;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kt + j], p.scale_log2, nm));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[kt][j] = (bf16)pv[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ps = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[kt][2 * j], pf[kt][2 * j + 1]}, kOnes2, ps, false);
+      }
+      l_run = ps;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto vstep = [&](auto n_c) {
+      constexpr int n = decltype(n_c)::value;
+      constexpr int kt = n / MBS, mb = n % MBS;
+      mma32_acc(acc[mb], vring[n % (VPF + 1)], pf[kt]);
+      if constexpr (n + VPF < 2 * MBS) vring[(n + VPF) % (VPF + 1)] = vread(n + VPF);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    unroll_from<0>(vstep, std::make_integer_sequence<int, 2 * MBS>{});
+  };
+
+  auto pass = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 1; ++st)
+      if (st < ntiles) issue_tile(st, st);
+    for (int it = 0; it < ntiles; ++it) {
+      const int left = ntiles - 1 - it;
+      if (left >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
+      else if (left >= 1) wait_vmcnt<DMA_PER_WAVE>();
+      else wait_vmcnt<0>();
+      barrier_only();
+      if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+      if (MODE != 0 && !redo) continue;
+      tile((it % NSTAGE) * C::STAGE_BYTES, tok_begin + it * TT, MODE == 0 && it == 0, mode_c);
+    }
+  };
+
+  pass(std::integral_constant<int, 0>{});
+  // p >= 0, so a p above 2^kRestartGap shows in its lane's sum
+  if (__builtin_amdgcn_readfirstlane(__any(!(l_run <= 0x1p64f)))) redo = true;
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) *vote = 0;
+  __syncthreads();
+  if (redo && lane == 0) *vote = 1;
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(*vote)) {
+    if (redo) {
+#pragma unroll
+      for (int mb = 0; mb < MBS; ++mb) acc[mb] = f32x16{};
+      m_ref = -INFINITY;
+      l_run = 0.f;
+    }
+    pass(std::integral_constant<int, 1>{});
+    wait_vmcnt<0>();
+    __syncthreads();
+    pass(std::integral_constant<int, 2>{});
+    wait_vmcnt<0>();
+  }
+
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  if (!head_ok) return;
+  const long long pidx = ((long long)b * p.H + head) * p.nsplit + split;
+  if (half == 0) {
+    p.part_ml[pidx * 2 + 0] = m_ref;
+    p.part_ml[pidx * 2 + 1] = l_tot;
+  }
+  // accumulator element e of lane l in block mb: latent column 32 mb + 8 (e/4) + 4 (l/32) + e%4
+  float* pz = p.part_z + pidx * VL + 4 * half;
+#pragma unroll
+  for (int mb = 0; mb < MBS; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(pz + 32 * mb + 8 * q) =
+          (f32x4){acc[mb][4 * q + 0], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
+}
+
 }  // namespace
 
 // Shapes served by the fast path: bf16; MLA with latent 512 (+ rotary 64 or none) and a
@@ -615,22 +892,21 @@ bool decode_fast_supported(const DecodeParams& p, int* variant) {
   return false;
 }
 
-int decode_fast_head_tile(int variant) { return variant == 2 ? 16 : 64; }
+int decode_fast_head_tile(int variant) { return variant == 2 ? 16 : 128; }
 
 hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s) {
   dim3 grid(p.nsplit, p.head_tiles, p.B);
   switch (variant) {
     case 3:
     case 4: {
-      // 1-D grid over (sequence, split, 64-head group)
+      // 1-D grid over (sequence, split, 128-head group)
       const dim3 g1((unsigned)(p.B * p.nsplit * p.head_tiles));
-      constexpr size_t extra = 2 * 2 * 64 * 16 + 4 * 2 * 16 * 4 + 16;
       if (variant == 3) {
-        constexpr size_t lds = FastCfg<512, 64, 8, 4>::LDS + extra;
-        hipLaunchKernelGGL((decode_hg64_kernel<64, 4>), g1, dim3(512), lds, s, p);
+        constexpr size_t lds = FastCfg<512, 64, 4, 4>::LDS + 16;
+        hipLaunchKernelGGL((decode_h128_kernel<64, 4>), g1, dim3(256), lds, s, p);
       } else {
-        constexpr size_t lds = FastCfg<512, 0, 8, 4>::LDS + extra;
-        hipLaunchKernelGGL((decode_hg64_kernel<0, 4>), g1, dim3(512), lds, s, p);
+        constexpr size_t lds = FastCfg<512, 0, 4, 4>::LDS + 16;
+        hipLaunchKernelGGL((decode_h128_kernel<0, 4>), g1, dim3(256), lds, s, p);
       }
       break;
     }

@@ -1,7 +1,7 @@
 // Large projection GEMM for gfx950 (bf16, many rows): out[m, n] = sum_k A[m, k] W[n, k].
 //
-// Workgroup tile 256 x 256, 4 waves in a 2 x 2 grid, each wave a 128 x 128 block of
-// 32x32x16 MFMA accumulators (16 x 16 fp32 per lane, in the accumulation registers).  K
+// Workgroup tile 256 x 256, 8 waves (two per SIMD) in a 4 x 2 grid, each wave a 64 x 128
+// block of 32x32x16 MFMA accumulators (8 x 16 fp32 per lane, in the accumulation registers).  K
 // advances 32 at a time through NST LDS stages filled by 16-byte direct-to-LDS copies:
 // each copy instruction moves 16 rows x 64 bytes of A or of W.  Rows are 64 bytes (four
 // 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), which puts the 8 rows of
@@ -24,16 +24,16 @@ namespace mla {
 
 namespace {
 
-constexpr int GBM = 256, GBN = 256, GBK = 32, GNST = 4;
+constexpr int GBM = 256, GBN = 256, GBK = 32, GNST = 4, GNW = 8;
 constexpr int G_AB = GBM * GBK * 2;                 // A bytes per stage (= W bytes)
 constexpr int G_STAGE = 2 * G_AB;                   // 32 KB
-constexpr int G_CPW = (G_AB / 1024) / 4;            // copies per wave per operand per stage (4)
+constexpr int G_CPW = (G_AB / 1024) / GNW;          // copies per wave per operand per stage (2)
 constexpr int G_LDC = 128 + 4;                      // epilogue LDS row stride (floats)
-constexpr size_t G_LDS = (size_t)GNST * G_STAGE;    // 128 KB
-static_assert((size_t)4 * 32 * G_LDC * 4 <= G_LDS, "epilogue chunks fit in the stages");
+constexpr size_t G_EPI = (size_t)GNW * 32 * G_LDC * 4;   // per-wave 32-row epilogue chunks
+constexpr size_t G_LDS = (size_t)GNST * G_STAGE > G_EPI ? (size_t)GNST * G_STAGE : G_EPI;
 constexpr int KV_CS = 72;                           // bf16 column stride (bytes) of the key transpose
 constexpr int KV_BUF = 128 * KV_CS;                 // one 32-row x 128-column chunk
-static_assert((size_t)4 * 2 * KV_BUF <= G_LDS, "key transpose buffers fit in the stages");
+static_assert((size_t)GNW * KV_BUF <= G_LDS, "key transpose buffers fit in the stages");
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -52,12 +52,12 @@ __device__ __forceinline__ int opaque_int(int x) {
 // DIRECT: the flash-layout output stage (own instantiation: sharing one register allocation
 // with the generic stage costs spills)
 template <bool DIRECT>
-__global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
+__global__ void __launch_bounds__(64 * GNW, 1) gemm_big_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;             // 64-row block wm, 128-column block wn
   const int col = lane & 31, half = lane >> 5;
   const int n0 = blockIdx.x * GBN;
   const int m0 = blockIdx.y * GBM;
@@ -100,9 +100,9 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
   // r mod 32 = col, so the swizzle key (r >> 2) & 3 = (col >> 2) & 3 for every block
   const int rd_base = col * 64 | ((((col >> 2) & 3) ^ half) << 4);   // XOR (2 ks) << 4 below
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
@@ -118,13 +118,13 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
     if (it + GNST - 1 < nst) issue(it + GNST - 1);
     const unsigned char* T = smem + (it % GNST) * G_STAGE;
     const int rb0 = opaque_int(rd_base);
-    Frag<bf16> fa[2][4], fb[2][4];
+    Frag<bf16> fa[2][2], fb[2][4];
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
       const int off = rb0 ^ (ks << 5);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[ks][i] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off + (128 * wm + 32 * i) * 64));
+      for (int i = 0; i < 2; ++i)
+        fa[ks][i] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off + (64 * wm + 32 * i) * 64));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         fb[ks][j] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + G_AB + off + (128 * wn + 32 * j) * 64));
@@ -132,19 +132,18 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mma32(fa[ks][i], fb[ks][j], acc[i][j]);
-    // issue order: the first step's 8 operand reads, then its 16 products with the second
-    // step's 8 reads slotted in after every other product, then the second step's products
-    // (one wave per SIMD: nothing else hides an LDS read issued just before its use)
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // issue order: the first step's 6 operand reads, then its 8 products with the second
+    // step's 6 reads slotted in after the first 6, then the second step's products
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    for (int k = 0; k < 6; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -166,8 +165,8 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
       // 32-column block and 16-token group.
       const long long jstride = 32LL * sg.out_ld;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 128 * wm + 32 * i;
+      for (int i = 0; i < 2; ++i) {
+        const int m = m0 + 64 * wm + 32 * i;
         if (m >= p.M) break;
         const int b = m / p.rows_per_batch, t = m - b * p.rows_per_batch;
         bf16* base = out + ((long long)(b * sg.out_nh + head) * sg.out_hw + j0 + col) * sg.out_ld + t + 8 * half;
@@ -186,14 +185,14 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
       // 72 B: the 16 columns of one write phase fall on distinct bank pairs); the LDS
       // transpose load then hands lane x of a 16-lane group 4 consecutive columns of row
       // r0 + x, and two loads make one 16-byte store.
-      unsigned char* ct = smem + wave * 2 * KV_BUF;
+      // (one buffer per wave: a wave's LDS accesses complete in issue order)
+      unsigned char* buf = smem + wave * KV_BUF;
       const int g16 = lane >> 4, x16 = lane & 15;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 128 * wm + 32 * i;
+      for (int i = 0; i < 2; ++i) {
+        const int m = m0 + 64 * wm + 32 * i;
         if (m >= p.M) break;
         const int b = m / p.rows_per_batch, t = m - b * p.rows_per_batch;
-        unsigned char* buf = ct + (i & 1) * KV_BUF;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -219,8 +218,8 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
       }
     }
   } else {
-  // Epilogue per wave: its 128 x 128 block in four chunks of 32 rows.  Accumulator element
-  // e of lane l in block (i, j) is out[128 wm + 32 i + 8 (e/4) + 4 (l/32) + e%4][128 wn + 32 j + l%32].
+  // Epilogue per wave: its 64 x 128 block in two chunks of 32 rows.  Accumulator element
+  // e of lane l in block (i, j) is out[64 wm + 32 i + 8 (e/4) + 4 (l/32) + e%4][128 wn + 32 j + l%32].
   float* Cs = reinterpret_cast<float*>(smem) + wave * 32 * G_LDC;
   auto stage = [&](auto I) {                    // chunk I with compile-time accumulator indices
     constexpr int i = decltype(I)::value;
@@ -230,19 +229,15 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(GemmParams p) {
       for (int e = 0; e < 16; ++e) Cs[(8 * (e >> 2) + 4 * half + (e & 3)) * G_LDC + 32 * j + col] = acc[i][j][e];
   };
 #pragma nounroll
-  for (int i = 0; i < 4; ++i) {
-    switch (i) {
-      case 0: stage(std::integral_constant<int, 0>{}); break;
-      case 1: stage(std::integral_constant<int, 1>{}); break;
-      case 2: stage(std::integral_constant<int, 2>{}); break;
-      default: stage(std::integral_constant<int, 3>{}); break;
-    }
+  for (int i = 0; i < 2; ++i) {
+    if (i == 0) stage(std::integral_constant<int, 0>{});
+    else stage(std::integral_constant<int, 1>{});
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
     if (p.fast_epilogue)
-      epilogue_block_fast<bf16>(p, Cs, G_LDC, m0 + 128 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane);
+      epilogue_block_fast<bf16>(p, Cs, G_LDC, m0 + 64 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane);
     else
-      epilogue_block<bf16>(p, Cs, G_LDC, m0 + 128 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane, 64);
+      epilogue_block<bf16>(p, Cs, G_LDC, m0 + 64 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane, 64);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
   }
@@ -313,9 +308,9 @@ hipError_t launch_gemm_big(const GemmParams& pin, int groups, hipStream_t s) {
   const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
   dim3 grid(cdiv(N, GBN), cdiv(p.M, GBM), groups);
   if (p.fast_epilogue == 2)
-    hipLaunchKernelGGL(gemm_big_kernel<true>, grid, dim3(256), G_LDS, s, p);
+    hipLaunchKernelGGL(gemm_big_kernel<true>, grid, dim3(64 * GNW), G_LDS, s, p);
   else
-    hipLaunchKernelGGL(gemm_big_kernel<false>, grid, dim3(256), G_LDS, s, p);
+    hipLaunchKernelGGL(gemm_big_kernel<false>, grid, dim3(64 * GNW), G_LDS, s, p);
   return hipGetLastError();
 }
 

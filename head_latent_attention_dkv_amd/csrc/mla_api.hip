@@ -78,7 +78,7 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
   const int ntok = max_ctx + 1;
   int chunk;
   if (sp.fast_variant >= 0) {
-    sp.fast_head_tiles = sp.fast_variant == 2 ? 1 : cdiv(hpb, 64);
+    sp.fast_head_tiles = sp.fast_variant == 2 ? 1 : cdiv(hpb, 128);
     const long long wgs = (long long)B * sp.fast_head_tiles;
     int ns = (int)((kCUs + wgs - 1) / wgs);
     chunk = round_up(cdiv(ntok, ns < 1 ? 1 : ns), 32);

@@ -43,12 +43,6 @@ constexpr float kFlashLimit = 0x1p64f;  // 2^kFlashGap
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define kOnes2 ((bf16x2){(__bf16)1.0f, (__bf16)1.0f})
 
-// f(integral_constant<LO + i>) for i in the sequence, in order, fully unrolled
-template <int LO, typename F, int... I>
-__device__ __forceinline__ void unroll_from(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, LO + I>{}), ...);
-}
-
 __device__ __forceinline__ int opaque_i(int x) {
   asm volatile("" : "+v"(x));
   return x;
