@@ -221,8 +221,12 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 }
 
 // z[b][h] = sum_s 2^(m_s - M) z_s / sum_s 2^(m_s - M) l_s over the splits of sequence b.
+// One 64-lane workgroup per (head, sequence); lane c owns CPT consecutive columns (vector
+// loads), the split weights are formed once per split, and the split loop is unrolled so
+// that several partial rows are in flight at once.
 template <typename T, int DL>
 __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
+  constexpr int CPT = DL >= 64 ? DL / 64 : 1;
   const int head = blockIdx.x;
   const int b = blockIdx.y;
   const int n_tok = p.ctx_len[b] + 1;
@@ -233,13 +237,30 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   float Lsum = 0.f;
   for (int s = 0; s < ns; ++s) Lsum += exp2f(p.part_ml[(base + s) * 2] - M) * p.part_ml[(base + s) * 2 + 1];
   const float inv = 1.f / Lsum;
-  T* z = reinterpret_cast<T*>(p.z) + ((long long)b * p.H + head) * p.rb;
-  for (int c = threadIdx.x; c < p.rb; c += 64) {
-    float a = 0.f;
-    for (int s = 0; s < ns; ++s)
-      a += exp2f(p.part_ml[(base + s) * 2] - M) * p.part_z[(base + s) * DL + c];
-    z[c] = from_f32<T>(a * inv);
+  const int c0 = threadIdx.x * CPT;
+  if (c0 >= p.rb) return;
+  float a[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) a[j] = 0.f;
+  const float* zs = p.part_z + base * DL + c0;
+#pragma unroll 4
+  for (int s = 0; s < ns; ++s) {
+    const float w = exp2f(p.part_ml[(base + s) * 2] - M);
+    float v[CPT];
+    if constexpr (CPT % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < CPT; j += 4) *reinterpret_cast<f32x4*>(v + j) = *reinterpret_cast<const f32x4*>(zs + (long long)s * DL + j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) v[j] = zs[(long long)s * DL + j];
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) a[j] += w * v[j];
   }
+  T* z = reinterpret_cast<T*>(p.z) + ((long long)b * p.H + head) * p.rb + c0;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+    if (c0 + j < p.rb) z[j] = from_f32<T>(a[j] * inv);
 }
 
 template <typename T, int DL>

@@ -11,10 +11,10 @@
 //     32x32x16 MFMA whose k index is the token;
 //   * 16-byte chunks are XOR-swizzled inside groups of 8 per token row so that both read
 //     patterns hit distinct LDS banks.
-// Workgroup = 4 waves.  MLA (one latent block): wave w owns heads 32w..32w+31 of a
-// 128-head tile and reads the whole row.  MLRA (4 latent blocks): wave w owns latent
-// block w (its heads padded to 32) and reads its own quarter of the row; the tile is
-// still streamed once for all blocks.
+// Workgroup = 4 waves, one per SIMD, and the tile is streamed once for all heads.  MLA
+// (one latent block of 512): wave w owns heads 32w..32w+31 and reads the whole row
+// (decode_h128_kernel).  MLRA (4 latent blocks of 128): wave w owns latent block w and
+// reads its own quarter of the row (decode_fast_kernel).
 #include <type_traits>
 
 #include "common.h"
@@ -26,9 +26,9 @@ namespace mla {
 namespace {
 
 constexpr int TT = 32;
-constexpr int kSPF = 4;                          // score operand reads in flight per wave
 constexpr float kLazyRescale = 8.0f;
 constexpr float kRestartGap = 64.0f;       // log2 units: p <= 2^64 keeps bf16 / fp32 far from overflow
+constexpr float kRestartLimit = 0x1p64f;   // 2^kRestartGap
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -277,327 +277,6 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   for (int mb = 0; mb < C::MB; ++mb) *reinterpret_cast<f32x4*>(pz + 16 * mb) = acc[mb];
 }
 
-// 64-head variant for the latent-512 case (MLA with one latent block): 8 waves, two per SIMD,
-// so that each SIMD has a second wave to issue LDS reads and vector work while the other
-// waits or multiplies.  One workgroup covers 64 heads of one sequence over one split;
-// the two 64-head groups of a (sequence, split) pair run on the same XCD (consecutive
-// blocks of that XCD), so the second reader of each cache tile finds it in L2.
-//   scores: wave w = (head block hb = w % 4 of 16 heads, token half th = w / 4),
-//           S^T[16 tokens x 16 heads] = C_tile[16 x 576] . Q^T  (16x16x32 MFMA, 18 k-steps);
-//   values: wave w owns latent columns 64w..64w+63 for all 64 heads,
-//           Z^T[64 x 64 heads] += C_tile^T[64 x 32] . P^T  (2 x 2 blocks of 32x32x16, K = 32).
-// P moves between the roles through a 4 KB LDS buffer laid out as the value MFMA's B
-// operand, so the tile is transpose-read once per workgroup.  Score lane l holds head
-// l%16 and tokens 16 th + 4(l/16) + i; the transpose load hands the value MFMA lane
-// (column, g) the tokens {4g..4g+3, 8+4g..8+4g+3} of each 16-token k-step.
-// Registers: Q (16 heads x 576 bf16) 72, z accumulators (64 x 64 fp32) 64 per wave.
-template <int VR, int NSTAGE>
-__global__ void __launch_bounds__(512, 1) decode_hg64_kernel(DecodeParams p) {
-  constexpr int VL = 512, NWV = 8;
-  using C = FastCfg<VL, VR, NWV, NSTAGE>;            // stage: 32 latent rows + 32 rotary rows
-  constexpr int KSL = VL / 32, KSR = VR / 32, KS = KSL + KSR;   // 32-wide k-steps
-  constexpr int RPW = TT / NWV;                       // latent rows per wave per tile (4)
-  constexpr int DMA_PER_WAVE = RPW + (VR ? 2 : 0);    // + two 2-row rotary copies
-  constexpr int PB_BYTES = 2 * 2 * 64 * 16;           // [head block j][k-step][lane] x 16 B
-  static_assert(NSTAGE == 4, "three tiles in flight");
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
-  unsigned char* const pbuf = smem_raw + C::LDS;
-  float* const xbuf = reinterpret_cast<float*>(pbuf + PB_BYTES);   // [hb][th][16] maxima / sums
-  int* const vote = reinterpret_cast<int*>(xbuf + 4 * 2 * 16);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hb = wave & 3, th = wave >> 2;
-  const int c16 = lane & 15, g = lane >> 4;
-
-  // work item: (sequence, split, 64-head group); the two head groups of a pair share an XCD
-  int u = blockIdx.x;
-  if (p.head_tiles == 2 && (gridDim.x & 15) == 0) {
-    const int x = u & 7, slot = u >> 3;
-    u = (((slot >> 1) << 3) + x) * 2 + (slot & 1);
-  }
-  const int hg = u % p.head_tiles;
-  const int pair = u / p.head_tiles;
-  const int b = pair / p.nsplit;
-  const int split = pair - b * p.nsplit;
-
-  const int n_tok = p.ctx_len[b] + 1;
-  const int tok_begin = split * p.chunk;
-  if (tok_begin >= n_tok) return;
-  const int tok_end = min(n_tok, tok_begin + p.chunk);
-  const int ntiles = (tok_end - tok_begin + TT - 1) / TT;
-
-  const int hbase = hg * 64;
-  const int head = hbase + 16 * hb + c16;            // score-role head of this lane
-  const bool head_ok = head < p.hpb;
-
-  // ---- copies: latent row t of a tile is one wave-wide 1 KB load (scalar sequence base +
-  // 32-bit lane offset); each wave also moves its 4 rotary rows as two 256-byte copies of
-  // 2 rows (4 bytes per lane, all lanes active) ----
-  const unsigned char* ckv_seq = reinterpret_cast<const unsigned char*>(p.ckv) + (long long)b * p.cache_bstride * (VL * 2);
-  const unsigned char* kr_seq = reinterpret_cast<const unsigned char*>(p.kr) + (long long)b * p.cache_bstride * (VR * 2);
-  const uint32_t lds_base = lds_addr_of(smem_raw);
-  auto issue_tile = [&](int tile, int stage) {
-    const int t0 = tok_begin + tile * TT;
-    const uint32_t sbase = lds_base + stage * C::STAGE_BYTES;
-    const int ln = opaque(lane);
-    const uint32_t ln16 = (uint32_t)ln << 4;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int t = wave * RPW + i;                    // wave-uniform
-      const int tok = min(t0 + t, tok_end - 1);
-      const uint32_t key16 = (uint32_t)bitrev4(t & 15) << 4;
-      dma16_s(ckv_seq + (long long)tok * (VL * 2), ln16 ^ key16, __builtin_amdgcn_readfirstlane(sbase + t * 1024));
-    }
-    if constexpr (VR > 0) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {                    // lane -> (row wave*4 + 2k + lane/32, dword lane%32)
-        const int t = wave * RPW + 2 * k + (ln >> 5);
-        const int tok = min(t0 + t, tok_end - 1);
-        const uint32_t c = (uint32_t)((((ln & 31) >> 2) ^ ((t >> 1) & 7)) << 4) + 4 * (ln & 3);
-        dma4_s(kr_seq, (uint32_t)tok * (VR * 2) + c,
-               __builtin_amdgcn_readfirstlane(sbase + C::LAT_BYTES + (wave * RPW + 2 * k) * 128));
-      }
-    }
-  };
-
-  // ---- Q^T (B operand of the 16x16x32 MFMA): lane holds head c16, k = 32 ks + 8 g + [0..7];
-  // loaded while the first tiles are in flight ----
-  const bf16* ql = reinterpret_cast<const bf16*>(p.q_lat);
-  const bf16* qr = reinterpret_cast<const bf16*>(p.q_rope);
-  const int head_ld = head_ok ? head : 0;
-  const bf16* qlp = ql + ((long long)b * p.H + head_ld) * p.q_lat_hs + 8 * g;
-  const bf16* qrp = qr + ((long long)b * p.H + head_ld) * p.q_rope_hs + 8 * g;
-  Frag<bf16> qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_load<bf16>(ks < KSL ? qlp + ks * 32 : qrp + (ks - KSL) * 32);
-  // Only tile 0 is copied together with the Q loads; tiles 1 and 2 follow at the top of the
-  // first iteration.  (With tiles 1 and 2 also issued here, behind the 18 Q loads, later
-  // tiles came out wrong on the GPU although the staged bytes checked out; the cause was
-  // not pinned down, and this order is the one verified at every tile count.)
-  issue_tile(0, 0);
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (!head_ok) qf[ks] = frag_zero<bf16>();
-    asm volatile("" ::"v"(qf[ks].v));
-  }
-
-  // ---- per-lane LDS byte offsets inside a stage ----
-  // score operand: token row t = 16 th + c16, 16-byte chunk 4 ks + g (XOR key bitrev4(c16))
-  int qk_off[4];
-  {
-    const int t = 16 * th + c16;
-    const int f = bitrev4(c16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) qk_off[q] = t * 1024 + (((4 * q + g) ^ f) << 4);
-  }
-  int rope_off[VR ? KSR : 1];
-  {
-    const int t = 16 * th + c16;
-#pragma unroll
-    for (int ks = 0; ks < (VR ? KSR : 1); ++ks) rope_off[ks] = C::LAT_BYTES + t * 128 + (((4 * ks + g) ^ ((t >> 1) & 7)) << 4);
-  }
-  // value operand via the transpose load: lane k of 16-lane group g16 reads token row
-  // 4 half + k/4 (+ 8 for the second read, + 16 ks), 8 bytes at latent column
-  // 64 wave + 32 mb + 16 (g16 % 2) + 4 (k % 4)
-  int pv_off[2][2];
-  {
-    const int k16 = lane & 15, g16 = lane >> 4, half = lane >> 5;
-    const int r0 = 4 * half + (k16 >> 2);
-    const int x = 2 * (g16 & 1) + ((k16 & 3) >> 1);
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const int r = r0 + 8 * hi;
-      const int f = bitrev4(r);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        pv_off[hi][mb] = r * 1024 + 8 * (k16 & 1) + ((((8 * (wave & 1) + 4 * mb + x) ^ f) + 16 * (wave >> 1)) << 4);
-    }
-  }
-  // P^T written by this score lane: block j = hb / 2, k-step th, B-operand lane
-  // 32 (g % 2) + 16 (hb % 2) + c16, 8-byte half g / 2
-  const int pw_off = ((2 * (hb >> 1) + th) * 64 + 32 * (g & 1) + 16 * (hb & 1) + c16) * 16 + 8 * (g >> 1);
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mb][j][i] = 0.f;
-  float m_ref = -INFINITY;   // reference maximum of this lane's head (log2 units), shared by both token halves
-  float m_seen = -INFINITY;  // largest maximum over this wave's tokens
-  float l_run = 0.f;         // this lane's share of the head's sum of p
-  unsigned long long ovf = 0;   // lanes whose tile exceeded the reference by kRestartGap
-
-  // max / sum over the four lanes c16 + 16 g' holding the same head
-  auto head_max = [](float v) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-  };
-  auto head_sum = [](float v) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-  };
-  // value of the other token half's wave for this lane's head (after a barrier)
-  // (LDS waits only: the tile copies stay in flight)
-  auto exchange = [&](float v, auto reduce) {
-    if (g == 0) xbuf[(hb * 2 + th) * 16 + c16] = v;
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    barrier_only();
-    const float o = xbuf[(hb * 2 + (th ^ 1)) * 16 + c16];
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    barrier_only();
-    return reduce(v, o);
-  };
-
-  // Pass 1 uses each head's first-tile maximum as a fixed reference: p = 2^(s - m_ref) is
-  // exact in bf16 / fp32 while s - m_ref < kRestartGap.  If any head of the workgroup goes
-  // beyond that (never for ordinary attention scores), the accumulators are unusable; the
-  // scores still run to the end so that m_seen is each head's exact maximum, and pass 2
-  // re-streams the split for the whole workgroup with that reference.  No per-register
-  // rescale sits in either loop.
-  auto pass = [&](auto second_pass) {
-    constexpr bool SECOND = decltype(second_pass)::value;
-    if constexpr (SECOND) issue_tile(0, 0);          // pass 1 copied tile 0 with the Q loads
-    for (int it = 0; it < ntiles; ++it) {
-      const int left = ntiles - 1 - it;
-      if (it == 0) wait_vmcnt<0>();                    // only tile 0 is in flight
-      else if (left >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
-      else if (left >= 1) wait_vmcnt<DMA_PER_WAVE>();
-      else wait_vmcnt<0>();
-      barrier_only();
-      if (it == 0) {
-        if (1 < ntiles) issue_tile(1, 1);
-        if (2 < ntiles) issue_tile(2, 2);
-      }
-      if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
-
-      const unsigned char* T = smem_raw + (it % NSTAGE) * C::STAGE_BYTES;
-      const int t0 = tok_begin + it * TT;
-
-      // scores: one 16-byte LDS read per k-step feeds one MFMA, kSPF reads ahead
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      {
-        auto aread = [&](int ks) {
-          const unsigned char* src = (ks < KSL) ? T + qk_off[ks & 3] + 256 * (ks >> 2)
-                                                : T + rope_off[(ks - KSL) & (KSR ? KSR - 1 : 0)];
-          return *reinterpret_cast<const bf16x8*>(src);
-        };
-        bf16x8 abuf[KS];
-#pragma unroll
-        for (int ks = 0; ks < kSPF; ++ks) abuf[ks] = aread(ks);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + kSPF < KS) abuf[ks + kSPF] = aread(ks + kSPF);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[ks], qf[ks].v, s, 0, 0, 0);
-        }
-      }
-      // probabilities of this lane's head at tokens 16 th + 4 g + i
-      if (t0 + TT > tok_end) {                         // the ragged last tile only
-        asm volatile("; ragged tile");                 // keeps this a branch (no selects on every tile)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 16 * th + 4 * g + i >= tok_end) s[i] = -INFINITY;
-      }
-      if constexpr (!SECOND) {
-        const float mt = head_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * p.scale_log2;
-        m_seen = fmaxf(m_seen, mt);
-        if (it == 0) m_ref = exchange(mt, [](float a, float o) { return fmaxf(a, o); });
-        ovf |= __ballot(mt > m_ref + kRestartGap);
-      }
-      {
-        const float nm = -m_ref;
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, nm));   // 2^x, x <= kRestartGap
-        const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(p01, kOnes2, l_run, false);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(p23, kOnes2, l_run, false);
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<bf16x4*>(pbuf + pw_off) = (bf16x4){p01[0], p01[1], p23[0], p23[1]};
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only: the tile copies stay in flight
-      barrier_only();
-
-      // values: latent columns 64 wave .. + 63 for both 32-head blocks
-      {
-        auto tread = [&](int mb, int ks) {
-          const unsigned char* a0 = T + pv_off[0][mb] + 16 * 1024 * ks;
-          const unsigned char* a1 = T + pv_off[1][mb] + 16 * 1024 * ks;
-          s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a0);
-          s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a1);
-          s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          return __builtin_bit_cast(bf16x8, v);
-        };
-        bf16x8 pb[2][2], av[2][2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) pb[ks][j] = *reinterpret_cast<const bf16x8*>(pbuf + ((2 * j + ks) * 64 + lane) * 16);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) av[ks][mb] = tread(mb, ks);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mma32_acc(acc[mb][j], av[ks][mb], pb[ks][j]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  pass(std::false_type{});
-  // workgroup-wide vote: does any head need the exact-maximum pass?
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) *vote = 0;
-  __syncthreads();
-  if (ovf != 0 && lane == 0) *vote = 1;
-  __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(*vote)) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][j][i] = 0.f;
-    m_ref = exchange(m_seen, [](float a, float o) { return fmaxf(a, o); });   // exact maximum of the head
-    l_run = 0.f;
-    pass(std::true_type{});
-    wait_vmcnt<0>();
-  }
-
-  const float l_tot = exchange(head_sum(l_run), [](float a, float o) { return a + o; });
-  if (head_ok && th == 0 && g == 0) {
-    const long long pidx = ((long long)b * p.H + head) * p.nsplit + split;
-    p.part_ml[pidx * 2 + 0] = m_ref;
-    p.part_ml[pidx * 2 + 1] = l_tot;
-  }
-  // accumulator element e of lane l in block (mb, j): latent column
-  // 64 wave + 32 mb + 8 (e/4) + 4 (l/32) + e%4 of head 32 j + l%32
-  const int half = lane >> 5, col = lane & 31;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int hj = hbase + 32 * j + col;
-    if (hj >= p.hpb) continue;
-    float* pz = p.part_z + (((long long)b * p.H + hj) * p.nsplit + split) * VL + 64 * wave;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(pz + mb * 32 + 8 * q + 4 * half) =
-            (f32x4){acc[mb][j][4 * q + 0], acc[mb][j][4 * q + 1], acc[mb][j][4 * q + 2], acc[mb][j][4 * q + 3]};
-  }
-}
-
 // 128-head variant for the latent-512 case (MLA with one latent block): one workgroup per
 // (sequence, split) streams each cache tile once for all heads.  4 waves, one per SIMD;
 // wave w owns heads 32w..32w+31 for both products, so a head's softmax never leaves its wave:
@@ -836,7 +515,7 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
 
   pass(std::integral_constant<int, 0>{});
   // p >= 0, so a p above 2^kRestartGap shows in its lane's sum
-  if (__builtin_amdgcn_readfirstlane(__any(!(l_run <= 0x1p64f)))) redo = true;
+  if (__builtin_amdgcn_readfirstlane(__any(!(l_run <= kRestartLimit)))) redo = true;
   wait_vmcnt<0>();
   __syncthreads();
   if (threadIdx.x == 0) *vote = 0;
