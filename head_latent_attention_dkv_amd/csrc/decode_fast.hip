@@ -26,7 +26,6 @@ namespace mla {
 namespace {
 
 constexpr int TT = 32;
-constexpr float kLazyRescale = 8.0f;
 constexpr float kRestartGap = 64.0f;       // log2 units: p <= 2^64 keeps bf16 / fp32 far from overflow
 constexpr float kRestartLimit = 0x1p64f;   // 2^kRestartGap
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -71,14 +70,17 @@ __device__ __forceinline__ int opaque(int x) {
 //   Z^T[VL x 16 heads]       += C_tile^T[VL x 32] . P^T    (VL/16 row blocks, K = 32 tokens)
 // Lane l owns head l%16; its 8 scores of a tile sit at tokens 4(l/16)+i and 16+4(l/16)+i,
 // which is exactly its slice of P^T as the B operand, so P never leaves registers.
+// Softmax against a fixed reference per head (the maximum of its first tile), with the
+// overflow test on the row sums and the rare exact-maximum re-stream of decode_h128_kernel.
 template <int VL, int VR, int NW, int NSTAGE>
 __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   using C = FastCfg<VL, VR, NW, NSTAGE>;
   static_assert(VR == 0, "latent blocks without a rotary key (the copies below move latent rows only)");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  int* const vote = reinterpret_cast<int*>(smem_raw + C::LDS);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;        // k-group of the MFMA operands / row group of results
   const int hl = lane & 15;         // head within the wave
   const int split = blockIdx.x;
@@ -122,32 +124,22 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(qf[ks].v));
 
-  const bf16* ckv = reinterpret_cast<const bf16*>(p.ckv);
-  const bf16* kr = reinterpret_cast<const bf16*>(p.kr);
-  const long long row0 = (long long)b * p.cache_bstride;
-  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) unsigned char*)smem_raw);
-
-  // DMA: latent row t of the tile is one wave-wide 1 KB load (lane = physical chunk);
-  // each wave also loads TT/NW rotary rows (lanes 0..8*(TT/NW)-1: 8 chunks per row).
+  // DMA: latent row t of the tile is one wave-wide 1 KB load (scalar row base, 32-bit lane
+  // offset: physical chunk ln holds logical chunk ln ^ bitrev4(t))
+  const unsigned char* ckv_seq = reinterpret_cast<const unsigned char*>(p.ckv) + (long long)b * p.cache_bstride * p.r_kv * 2;
+  const uint32_t lds_base = lds_addr_of(smem_raw);
   auto issue_tile = [&](int tile, int stage) {
     const int t0 = tok_begin + tile * TT;
     const uint32_t sbase = lds_base + stage * C::STAGE_BYTES;
-    const int ln = opaque(lane);
+    const uint32_t ln16 = (uint32_t)opaque(lane) << 4;
 #pragma unroll
     for (int i = 0; i < C::RPW; ++i) {
       const int t = wave * C::RPW + i;
       const int tok = min(t0 + t, tok_end - 1);
-      const int c = ln ^ bitrev4(t & 15);
-      const bf16* src = ckv + (row0 + tok) * p.r_kv + c * 8;
-      dma16(src, __builtin_amdgcn_readfirstlane(sbase + t * 1024));
+      dma16_s(ckv_seq + (long long)tok * p.r_kv * 2, ln16 ^ ((uint32_t)bitrev4(t & 15) << 4),
+              __builtin_amdgcn_readfirstlane(sbase + t * 1024));
     }
   };
-
-  f32x4 acc[C::MB];
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
 
   // Per-lane LDS byte offsets inside a stage (see the swizzle above).
   int qk_off[4];
@@ -155,13 +147,6 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
     const int f = bitrev4(hl);
 #pragma unroll
     for (int q = 0; q < 4; ++q) qk_off[q] = hl * 1024 + (((vc0 + 4 * q + grp) ^ f) << 4);
-  }
-  int rope_off[2][VR ? C::KSR : 1];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int t = 16 * rb + hl;
-#pragma unroll
-    for (int ks = 0; ks < (VR ? C::KSR : 1); ++ks) rope_off[rb][ks] = t * 128 + (((4 * ks + grp) ^ ((t >> 1) & 7)) << 4);
   }
   int pv_off[8];
   {
@@ -173,21 +158,31 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
     for (int q = 0; q < 8; ++q) pv_off[q] = r0 * 1024 + 8 * (k16 & 1) + (((vc0 + 2 * q + x) ^ f0) << 4);
   }
 
+  f32x4 acc[C::MB];
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < ntiles) issue_tile(s, s);
+  for (int mb = 0; mb < C::MB; ++mb) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;   // reference maximum of this lane's head (log2 units)
+  float l_run = 0.f;         // this lane's share of the head's sum of p
+  bool redo = false;
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int left = ntiles - 1 - it;
-    if (NSTAGE >= 4 && left >= 2) wait_vmcnt<2 * C::DMA_PER_WAVE>();
-    else if (NSTAGE >= 3 && left >= 1) wait_vmcnt<C::DMA_PER_WAVE>();
-    else wait_vmcnt<0>();
-    barrier_only();
-    if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+  // max / sum over the four lanes hl + 16 g' holding the same head
+  auto head_max = [](float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  };
+  auto head_sum = [](float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  };
 
-    const unsigned char* T = smem_raw + (it % NSTAGE) * C::STAGE_BYTES;
-    const int t0 = tok_begin + it * TT;
-
+  // One tile.  MODE 0: accumulate against the first tile's maximum; MODE 1: exact maximum
+  // only; MODE 2: accumulate against the exact maximum.
+  auto tile = [&](const unsigned char* T, int t0, bool first, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
     // S^T: row block rb covers tokens 16 rb .. 16 rb + 15; lane reads token 16 rb + hl at
     // logical chunk vc0 + 4 ks + grp.  With f = bitrev4(hl) only the low 4 bits of the
     // chunk are permuted, so the byte offset is qk_off[ks % 4] + 256 (ks / 4) + 16 KB rb.
@@ -200,51 +195,31 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
             T + qk_off[ks & 3] + 256 * (ks >> 2) + 16 * 1024 * rb));
         s[rb] = mma16(a, qf[ks], s[rb]);
       }
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (VR > 0) {
-#pragma unroll
-      for (int ks = 0; ks < C::KSR; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          Frag<bf16> a = frag_load<bf16>(reinterpret_cast<const bf16*>(T + C::LAT_BYTES + rope_off[rb][ks]));
-          s[rb] = mma16(a, qf[C::KSL + ks], s[rb]);
-        }
-    }
-    float pv[8];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[4 * rb + i] = s[rb][i] * p.scale_log2;
     if (t0 + TT > tok_end) {                                // ragged last tile only
+      asm volatile("; ragged tile");                        // keeps this a branch
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t0 + 16 * rb + 4 * grp + i >= tok_end) pv[4 * rb + i] = -INFINITY;
+          if (t0 + 16 * rb + 4 * grp + i >= tok_end) s[rb][i] = -INFINITY;
     }
-    float mt = fmaxf(fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3])),
-                     fmaxf(fmaxf(pv[4], pv[5]), fmaxf(pv[6], pv[7])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // The running maximum is raised only when a tile exceeds it by more than 2^8
-    // (always on the first tile); the branch is wave-uniform and rarely taken.
-    if (__builtin_amdgcn_readfirstlane(__any(mt > m_run + kLazyRescale))) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
+    if (MODE == 1 || first) {
+      const float mt = head_max(fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])))) * p.scale_log2;
+      m_ref = MODE == 1 ? fmaxf(m_ref, mt) : mt;
+    }
+    if constexpr (MODE == 1) return;
+    const float nm = -m_ref;
+    float pv[8];
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) acc[mb] *= alpha;
-    }
-    float ps = 0.f;
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = exp2f(pv[i] - m_run);
-      ps += pv[i];
-    }
-    l_run += ps;
+      for (int i = 0; i < 4; ++i) pv[4 * rb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][i], p.scale_log2, nm));
     const Frag<bf16> pf = frag_from_f32<bf16>(pv);
+    // the denominator sums the same bf16 probabilities the products use
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_run = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf.v[2 * j], pf.v[2 * j + 1]}, kOnes2, l_run, false);
     __builtin_amdgcn_sched_barrier(0);
 
     // Z^T += C^T . P^T with the A operand from the LDS transpose load: lane k of 16-lane
@@ -260,16 +235,54 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
       Frag<bf16> a;
       a.v = __builtin_bit_cast(bf16x8, v);
       acc[mb] = mma16(a, pf, acc[mb]);
-      if ((mb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  auto pass = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 1; ++st)
+      if (st < ntiles) issue_tile(st, st);
+    for (int it = 0; it < ntiles; ++it) {
+      const int left = ntiles - 1 - it;
+      if (NSTAGE >= 4 && left >= 2) wait_vmcnt<2 * C::DMA_PER_WAVE>();
+      else if (NSTAGE >= 3 && left >= 1) wait_vmcnt<C::DMA_PER_WAVE>();
+      else wait_vmcnt<0>();
+      barrier_only();
+      if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+      if (MODE != 0 && !redo) continue;
+      tile(smem_raw + (it % NSTAGE) * C::STAGE_BYTES, tok_begin + it * TT, MODE == 0 && it == 0, mode_c);
+    }
+  };
+
+  pass(std::integral_constant<int, 0>{});
+  // p >= 0, so a p above 2^kRestartGap shows in its lane's sum
+  if (__builtin_amdgcn_readfirstlane(__any(!(l_run <= kRestartLimit)))) redo = true;
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) *vote = 0;
+  __syncthreads();
+  if (redo && lane == 0) *vote = 1;
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(*vote)) {
+    if (redo) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      m_ref = -INFINITY;
+      l_run = 0.f;
+    }
+    pass(std::integral_constant<int, 1>{});
+    wait_vmcnt<0>();
+    __syncthreads();
+    pass(std::integral_constant<int, 2>{});
+    wait_vmcnt<0>();
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = head_sum(l_run);
   if (!head_ok) return;
   const long long pidx = ((long long)b * p.H + head) * p.nsplit + split;
   if (grp == 0) {
-    p.part_ml[pidx * 2 + 0] = m_run;
+    p.part_ml[pidx * 2 + 0] = m_ref;
     p.part_ml[pidx * 2 + 1] = l_tot;
   }
   float* pz = p.part_z + pidx * VL + 4 * grp;
@@ -591,7 +604,7 @@ hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s)
     }
     case 2: {
       using C = FastCfg<128, 0, 4, 4>;
-      hipLaunchKernelGGL((decode_fast_kernel<128, 0, 4, 4>), grid, dim3(256), C::LDS, s, p);
+      hipLaunchKernelGGL((decode_fast_kernel<128, 0, 4, 4>), grid, dim3(256), C::LDS + 16, s, p);
       break;
     }
     default:
