@@ -82,7 +82,9 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
     const long long wgs = (long long)B * sp.fast_head_tiles;
     int ns = (int)((kCUs + wgs - 1) / wgs);
     chunk = round_up(cdiv(ntok, ns < 1 ? 1 : ns), 32);
-    if (sp.fast_variant == 2 && chunk > 512) chunk = 512;   // ragged contexts: many small splits
+    // MLRA (latent blocks): splits of at most 1024 tokens keep ragged batches balanced over
+    // the CUs while each workgroup streams long enough to amortise its start
+    if (sp.fast_variant == 2 && chunk > 1024) chunk = 1024;
   } else {
     const long long wgs = (long long)B * L * sp.head_tiles;
     const int wg_per_cu = sp.nw == 4 ? 1 : 8;

@@ -382,8 +382,13 @@ SkinnyPlan plan_stream(int M, int N, int K, int groups) {
   double best_cost = 1e300;
   int best_blocks = 0;
   const int max_s = K / (kStreamKT * kMinStagesPerSlab) > 0 ? K / (kStreamKT * kMinStagesPerSlab) : 1;
+  // Wide outputs (512 or more 32-row tiles) take 32-row tiles without split: three blocks fit
+  // on a CU, so the blocks land evenly on the compute units (64-row tiles leave half of
+  // them with one block and half with two).
+  const bool wide = (long long)cdiv(N, 32) * groups >= 512;
   for (int rows : {128, 64, 32}) {
     if (M > 64 && rows == 128) continue;                 // accumulator budget
+    if (wide && rows != 32) continue;
     const long long tiles = (long long)cdiv(N, rows) * groups;
     int s = (int)((kMinBlocks + tiles - 1) / tiles);
     s = s < 1 ? 1 : (s > max_s ? max_s : s);
