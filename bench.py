@@ -142,6 +142,7 @@ UNIT_SOURCES = {
     "dsv2_decode_attention": ("decode_fast.hip", "decode.hip", "lds_dma.h", "common.h", "internal.h"),
     "dsv2_prefill_attention": ("prefill_fast.hip", "prefill.hip", "gemm.hip", "gemm_big.hip", "gemm_epilogue.h",
                                "lds_dma.h", "common.h", "internal.h"),
+    "mlra_decode_attention": ("decode_fast.hip", "decode.hip", "lds_dma.h", "common.h", "internal.h"),
 }
 
 
@@ -333,7 +334,7 @@ def summarize_profiles(d):
         return vals
 
     def unit_kib(sub, counter):
-        v = per_dispatch(sub, counter, lambda n: "decode_hg64_kernel" in n or "combine_kernel" in n)
+        v = per_dispatch(sub, counter, lambda n: "decode_h128_kernel" in n or "combine_kernel" in n)
         by = {}
         for (name, _), x in v.items():
             by.setdefault("combine" if "combine_kernel" in name else "split", []).append(x)
@@ -371,7 +372,9 @@ def summarize_profiles(d):
                     "_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi128ELi128EEEvNS_10GemmParamsE":
                         "gemm_kernel<bf16,128,128>",
                     "_ZN3mla12_GLOBAL__N_114combine_kernelIDF16bLi512EEEvNS_12DecodeParamsE":
-                        "combine_kernel<bf16,512>"}.get(name, name)
+                        "combine_kernel<bf16,512>",
+                    "_ZN3mla12_GLOBAL__N_114combine_kernelIDF16bLi128EEEvNS_12DecodeParamsE":
+                        "combine_kernel<bf16,128>"}.get(name, name)
         return name[:70]
 
     lines = ["# Kernel times: DeepSeek-V2-shaped decode step (B=64, 4096 cached tokens, H=128)", "",
@@ -461,6 +464,27 @@ def summarize_profiles(d):
         pl += ["", f"Kernel sources digest: {src_digest(*UNIT_SOURCES['dsv2_prefill_attention'])}", ""]
         with open(os.path.join(PROFILES, "dsv2_prefill_attention_kernels.md"), "w") as fh:
             fh.write("\n".join(pl))
+
+    # kernel times of `bench.py --only mlra` (d/mlra_stats)
+    mstats = rows("mlra_stats", "*kernel_stats.csv")
+    if mstats:
+        ml = ["# Kernel times: MLRA decode (B=128, contexts U[512, 16384], 4 latent blocks x rank 128, "
+              "H=16, d_model=2048)", "",
+              "Command (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
+              "```",
+              "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/mlra_stats -o run -- "
+              "python3 bench.py --only mlra --steps 20 --warmup 5",
+              "python3 bench.py --summarize <dir>",
+              "```", "",
+              "mla_decode_attention = split kernel (decode_fast_kernel) + combine kernel; the call also runs "
+              "the few-row projections and the cache append.", "",
+              "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+        for r in mstats[:10]:
+            ml.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        ml += ["", f"Kernel sources digest: {src_digest(*UNIT_SOURCES['mlra_decode_attention'])}", ""]
+        with open(os.path.join(PROFILES, "mlra_decode_attention_kernels.md"), "w") as fh:
+            fh.write("\n".join(ml))
 
 
 def main():
