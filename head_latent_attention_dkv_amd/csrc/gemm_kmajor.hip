@@ -45,21 +45,35 @@ __global__ void __launch_bounds__(256) kmajor_small_kernel(GemmParams p) {
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   for (int k0 = 0; k0 < p.K; k0 += KM_KC) {
     const int kc = min(KM_KC, p.K - k0);           // a multiple of 16
-    // A chunk: 64 rows x kc, 16-byte pieces (rows beyond M repeat row M-1)
-    for (int i = tid; i < KM_BM * (KM_KC / 8); i += 256) {
+    // A chunk (64 rows x kc; rows beyond M repeat row M-1) and W chunk (kc rows x 128
+    // columns) in 16-byte pieces: all of a thread's 12 loads are issued before the first
+    // LDS store, so they are in flight together
+    constexpr int NA = KM_BM * (KM_KC / 8) / 256, NW = KM_KC * (KM_BN / 8) / 256;
+    bf16x8 va[NA], vw[NW];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + 256 * j;
       const int r = i / (KM_KC / 8), c = (i % (KM_KC / 8)) * 8;
-      if (c < kc) {
-        const int m = min(m0 + r, p.M - 1);
-        *reinterpret_cast<bf16x8*>(&As[r * KM_ALD + c]) =
-            *reinterpret_cast<const bf16x8*>(A + (long long)m * p.a_ld + k0 + c);
-      }
+      const int m = min(m0 + r, p.M - 1);
+      if (c < kc) va[j] = *reinterpret_cast<const bf16x8*>(A + (long long)m * p.a_ld + k0 + c);
     }
-    // W chunk: kc rows x 128 columns
-    for (int i = tid; i < KM_KC * (KM_BN / 8); i += 256) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int i = tid + 256 * j;
       const int r = i / (KM_BN / 8), c = (i % (KM_BN / 8)) * 8;
-      if (r < kc)
-        *reinterpret_cast<bf16x8*>(&Ws[r * KM_WLD + c]) =
-            *reinterpret_cast<const bf16x8*>(W + (long long)(k0 + r) * sg.w_ld + n0 + c);
+      if (r < kc) vw[j] = *reinterpret_cast<const bf16x8*>(W + (long long)(k0 + r) * sg.w_ld + n0 + c);
+    }
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + 256 * j;
+      const int r = i / (KM_KC / 8), c = (i % (KM_KC / 8)) * 8;
+      if (c < kc) *reinterpret_cast<bf16x8*>(&As[r * KM_ALD + c]) = va[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int i = tid + 256 * j;
+      const int r = i / (KM_BN / 8), c = (i % (KM_BN / 8)) * 8;
+      if (r < kc) *reinterpret_cast<bf16x8*>(&Ws[r * KM_WLD + c]) = vw[j];
     }
     __syncthreads();
     for (int ks = 0; ks < kc / 16; ++ks) {
