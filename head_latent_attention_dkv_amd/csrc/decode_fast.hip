@@ -603,8 +603,10 @@ hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s)
       break;
     }
     case 2: {
-      using C = FastCfg<128, 0, 4, 4>;
-      hipLaunchKernelGGL((decode_fast_kernel<128, 0, 4, 4>), grid, dim3(256), C::LDS + 16, s, p);
+      // two stages (64 KB): two workgroups share a CU, so one's start and tail overlap the
+      // other's stream
+      using C = FastCfg<128, 0, 4, 2>;
+      hipLaunchKernelGGL((decode_fast_kernel<128, 0, 4, 2>), grid, dim3(256), C::LDS + 16, s, p);
       break;
     }
     default:
