@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the computation runs in the library's HIP
 kernels.  PyTorch supplies device memory (tensor data pointers) and the current HIP
 stream.  The entry points keep the C names: mla_validate, mla_workspace_bytes,
-mla_cache_append, mla_prefill, mla_decode, mla_decode_attention,
+mla_cache_append, mla_prefill, mla_prefill_chunk, mla_decode, mla_decode_attention,
 mla_prefill_attention, mla_status_str.
 
 If the shared library is missing, loading raises -- there is no fallback path.
@@ -24,7 +24,7 @@ MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 4, 5, 6
 MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 MLA_ROPE_NONE, MLA_ROPE_DECOUPLED_INTERLEAVED, MLA_ROPE_FULL_HALFSPLIT = 0, 1, 2
 MLA_OP_CACHE_APPEND, MLA_OP_PREFILL, MLA_OP_DECODE = 0, 1, 2
-MLA_OP_DECODE_ATTENTION, MLA_OP_PREFILL_ATTENTION = 3, 4
+MLA_OP_DECODE_ATTENTION, MLA_OP_PREFILL_ATTENTION, MLA_OP_PREFILL_CHUNK = 3, 4, 5
 
 
 class MLAError(RuntimeError):
@@ -53,7 +53,8 @@ class mla_cache(ctypes.Structure):
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ("mla_status_str", "mla_validate", "mla_workspace_bytes", "mla_cache_append",
-           "mla_prefill", "mla_decode", "mla_decode_attention", "mla_prefill_attention")
+           "mla_prefill", "mla_decode", "mla_decode_attention", "mla_prefill_attention",
+           "mla_prefill_chunk")
 
 
 def lib() -> ctypes.CDLL:
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_attention.argtypes = [D, vp, vp, i32, vp, i32, C, vp, vp, sz, vp]
         L.mla_prefill_attention.restype = ctypes.c_int
         L.mla_prefill_attention.argtypes = [D, W, vp, i32, i32, C, vp, vp, sz, vp]
+        L.mla_prefill_chunk.restype = ctypes.c_int
+        L.mla_prefill_chunk.argtypes = [D, W, vp, i32, i32, i32, C, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -162,6 +165,13 @@ def mla_prefill(dims, weights: mla_weights, x, B: int, S: int, cache: Optional[m
     _check(lib().mla_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, S,
                              ctypes.byref(cache) if cache is not None else None, _ptr(y),
                              _ptr(workspace), int(ws_bytes), _stream(stream)), "mla_prefill")
+
+
+def mla_prefill_chunk(dims, weights: mla_weights, x, B: int, T: int, start_pos: int, cache: mla_cache,
+                      y, workspace, ws_bytes: int, stream=None) -> None:
+    _check(lib().mla_prefill_chunk(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                                   int(start_pos), ctypes.byref(cache), _ptr(y), _ptr(workspace),
+                                   int(ws_bytes), _stream(stream)), "mla_prefill_chunk")
 
 
 def mla_decode(dims, weights: mla_weights, x, B: int, ctx_len, max_ctx: int, cache: mla_cache,

@@ -133,13 +133,14 @@ hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s)
 // Flash-style causal prefill
 // ---------------------------------------------------------------------------
 struct PrefillParams {
-  const void* q;            // [B][S][H][dq]
+  const void* q;            // [B][T][H][dq]: T queries per sequence at positions q_off .. q_off+T-1
   const void* k;            // decompressed keys [B*S][H*dn] (head h at columns h*dn)
   const void* kr;           // rotated shared key rows: kr + (b*kr_bstride + t)*d_rope, or NULL
   long long kr_bstride;
   const void* v;            // values [B*S][H*dv]
-  void* o;                  // [B][S][H][dv]
-  int B, S, H, dn, d_rope, dv;
+  void* o;                  // [B][T][H][dv]
+  int B, S, H, dn, d_rope, dv;   // S keys per sequence (positions 0 .. S-1)
+  int T, q_off;             // queries per sequence and the position of the first (T = S, 0: prefill)
   float scale_log2;
 };
 
@@ -147,13 +148,14 @@ hipError_t launch_prefill(const PrefillParams& p, bool use_bf16, int dq_pad, int
 
 // bf16 flash prefill over head-major keys and transposed values (see prefill_fast.hip).
 struct FlashParams {
-  const void* q;            // [B][S][H][dn + d_rope]
+  const void* q;            // [B][T][H][dn + d_rope]: T queries at positions q_off .. q_off+T-1
   const void* k;            // decompressed keys, head-major [B][H][S][dn]
   const void* kr;           // rotated shared key rows: kr + (b*kr_bstride + t)*d_rope, or NULL
   long long kr_bstride;
   const void* vt;           // values, per head transposed [B][H][dv][S] (perm16 token order)
-  void* o;                  // [B][S][H][dv]
-  int B, S, H, dn, d_rope;
+  void* o;                  // [B][T][H][dv]
+  int B, S, H, dn, d_rope;  // S keys per sequence (positions 0 .. S-1)
+  int T, q_off;             // queries per sequence and the position of the first (T = S, 0: prefill)
   float scale_log2;
   int ntq;                  // query tiles per (sequence, head); set by the launcher
 };

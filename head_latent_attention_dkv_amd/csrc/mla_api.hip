@@ -413,7 +413,7 @@ hipError_t run_out_proj(const mla_dims* d, const mla_weights* w, const void* o, 
 }
 
 hipError_t run_flash(const mla_dims* d, const void* q, const void* k, const void* kr, long long kr_bstride,
-                     const void* vt, void* o, int B, int S, hipStream_t st) {
+                     const void* vt, void* o, int B, int S, int T, int q_off, hipStream_t st) {
   FlashParams fp;
   memset(&fp, 0, sizeof(fp));
   fp.q = q;
@@ -424,6 +424,8 @@ hipError_t run_flash(const mla_dims* d, const void* q, const void* k, const void
   fp.o = o;
   fp.B = B;
   fp.S = S;
+  fp.T = T;
+  fp.q_off = q_off;
   fp.H = d->n_heads;
   fp.dn = d->d_nope;
   fp.d_rope = d->d_rope;
@@ -454,6 +456,12 @@ DecodeParams decode_params(const mla_dims* d, const mla_cache* cache, const int3
   p.part_z = reinterpret_cast<float*>(at(ws, lay.part_z));
   p.part_ml = reinterpret_cast<float*>(at(ws, lay.part_ml));
   return p;
+}
+
+// v[i] = value for i < n (a device array of per-sequence start positions)
+__global__ void fill_i32_kernel(int32_t* v, int n, int32_t value) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) v[i] = value;
 }
 
 }  // namespace
@@ -516,6 +524,7 @@ size_t mla_workspace_bytes(const mla_dims* d, int op, int32_t batch, int32_t seq
     case MLA_OP_CACHE_APPEND: return 0;
     case MLA_OP_PREFILL: return seq > 0 ? prefill_layout(d, batch, seq, false).total : 0;
     case MLA_OP_PREFILL_ATTENTION: return seq > 0 ? prefill_layout(d, batch, seq, true).total : 0;
+    case MLA_OP_PREFILL_CHUNK: return seq > 0 ? prefill_layout(d, batch, seq, false).total + align_up((size_t)batch * 4) : 0;
     case MLA_OP_DECODE:
       if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) return 0;
       return decode_layout(d, batch, seq, false).total;
@@ -555,7 +564,7 @@ mla_status mla_prefill_attention(const mla_dims* d, const mla_weights* w, const 
   const bool flash = use_flash(d, S);
   hipError_t e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st, flash);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  if (flash) return hip_status(run_flash(d, q, k, cache->kr, cache->max_seq, v, o, B, S, st));
+  if (flash) return hip_status(run_flash(d, q, k, cache->kr, cache->max_seq, v, o, B, S, S, 0, st));
   int dqp, dvp;
   prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp);
   PrefillParams pp;
@@ -568,6 +577,8 @@ mla_status mla_prefill_attention(const mla_dims* d, const mla_weights* w, const 
   pp.o = o;
   pp.B = B;
   pp.S = S;
+  pp.T = S;
+  pp.q_off = 0;
   pp.H = d->n_heads;
   pp.dn = d->d_nope;
   pp.d_rope = d->d_rope;
@@ -607,7 +618,7 @@ mla_status mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, i
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (flash) {
     void* o = at(ws, lay.o);
-    e = run_flash(d, q, k, cache ? cache->kr : latr, cache ? cache->max_seq : S, v, o, B, S, st);
+    e = run_flash(d, q, k, cache ? cache->kr : latr, cache ? cache->max_seq : S, v, o, B, S, S, 0, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
     return hip_status(run_out_proj(d, w, o, B * S, y, st));
   }
@@ -623,6 +634,8 @@ mla_status mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, i
   pp.o = at(ws, lay.o);
   pp.B = B;
   pp.S = S;
+  pp.T = S;
+  pp.q_off = 0;
   pp.H = d->n_heads;
   pp.dn = d->d_nope;
   pp.d_rope = d->d_rope;
@@ -631,6 +644,63 @@ mla_status mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, i
   e = launch_prefill(pp, is_bf16(d), dqp, dvp, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   return hip_status(run_out_proj(d, w, pp.o, B * S, y, st));
+}
+
+mla_status mla_prefill_chunk(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t T,
+                             int32_t start_pos, const mla_cache* cache, float* y, void* ws, size_t ws_bytes,
+                             void* stream) {
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (!x || !y || B <= 0 || T <= 0 || start_pos < 0) return MLA_ERR_INVALID_ARG;
+  if ((s = check_weights(d, w, true, true, true)) != MLA_OK) return s;
+  if ((s = check_cache(d, cache)) != MLA_OK) return s;
+  if (B > cache->max_batch || (long long)start_pos + T > cache->max_seq) return MLA_ERR_CAPACITY;
+  const int S = start_pos + T;                      // keys per sequence: cached + new
+  PrefillWs lay = prefill_layout(d, B, S, false);
+  const size_t pos_off = lay.total;
+  if (!ws || ws_bytes < pos_off + align_up((size_t)B * 4)) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  // per-sequence start rows for the append and the query rotation
+  int32_t* pos = reinterpret_cast<int32_t*>(at(ws, pos_off));
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(cdiv(B, 256)), dim3(256), 0, st, pos, B, start_pos);
+  if ((e = hipGetLastError()) != hipSuccess) return MLA_ERR_HIP;
+  void* q = at(ws, lay.q);
+  if ((e = run_queries(d, w, x, B * T, T, pos, at(ws, lay.cq), q, st)) != hipSuccess) return MLA_ERR_HIP;
+  if ((e = run_latent(d, w, x, B, T, pos, cache, nullptr, nullptr, st)) != hipSuccess) return MLA_ERR_HIP;
+  // keys and values of every cached row 0..S-1, then the new queries over them
+  void* k = at(ws, lay.k);
+  void* v = at(ws, lay.v);
+  void* o = at(ws, lay.o);
+  const bool flash = use_flash(d, S) && start_pos % 64 == 0;
+  if ((e = run_kv_up(d, w, cache->ckv, true, cache->max_seq, B, S, k, v, st, flash)) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (flash) {
+    e = run_flash(d, q, k, cache->kr, cache->max_seq, v, o, B, S, T, start_pos, st);
+  } else {
+    int dqp, dvp;
+    prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp);
+    PrefillParams pp;
+    memset(&pp, 0, sizeof(pp));
+    pp.q = q;
+    pp.k = k;
+    pp.kr = cache->kr;
+    pp.kr_bstride = cache->max_seq;
+    pp.v = v;
+    pp.o = o;
+    pp.B = B;
+    pp.S = S;
+    pp.T = T;
+    pp.q_off = start_pos;
+    pp.H = d->n_heads;
+    pp.dn = d->d_nope;
+    pp.d_rope = d->d_rope;
+    pp.dv = d->d_v;
+    pp.scale_log2 = softmax_scale(d) * kLog2e;
+    e = launch_prefill(pp, is_bf16(d), dqp, dvp, st);
+  }
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return hip_status(run_out_proj(d, w, o, B * T, y, st));
 }
 
 mla_status mla_decode_attention(const mla_dims* d, const void* q_lat, const void* q_rope, int32_t B,

@@ -50,13 +50,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int n_qt = (p.S + BQ - 1) / BQ;
+  const int n_qt = (p.T + BQ - 1) / BQ;
   const int qt = n_qt - 1 - blockIdx.x;          // heaviest (latest) query tiles first
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int q0 = qt * BQ;
-  const int qw0 = q0 + wave * 32;                 // this wave's first query
+  const int qw0 = q0 + wave * 32;                 // this wave's first query (index among the T)
   const int query = qw0 + col;
+  const int qa0 = p.q_off + qw0, qabs = p.q_off + query;   // their positions
   const int dq = p.dn + p.d_rope;
 
   const T* Q = reinterpret_cast<const T*>(p.q);
@@ -71,7 +72,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int d = ks * 16 + 8 * half + j;
-      v[j] = (query < p.S && d < dq) ? to_f32(Q[(((long long)b * p.S + query) * p.H + h) * dq + d]) : 0.f;
+      v[j] = (query < p.T && d < dq) ? to_f32(Q[(((long long)b * p.T + query) * p.H + h) * dq + d]) : 0.f;
     }
     qf[ks] = frag_from_f32<T>(v);
   }
@@ -142,14 +143,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     }
   };
 
-  const int kend = min(p.S, q0 + BQ);            // keys beyond the tile's last query are masked
+  const int kend = min(p.S, p.q_off + q0 + BQ);  // keys beyond the tile's last query are masked
   load_tile(0);
   for (int k0 = 0; k0 < kend; k0 += BKEY) {
     store_tile();
     __syncthreads();
     if (k0 + BKEY < kend) load_tile(k0 + BKEY);
 
-    if (k0 <= qw0 + 31) {                         // some key of the tile is visible to this wave
+    if (k0 <= qa0 + 31) {                         // some key of the tile is visible to this wave
       f32x16 s[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -162,14 +163,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
       }
       float pv[32];
       float mt = -INFINITY;
-      const bool diag = (k0 + BKEY - 1 > qw0) || (k0 + BKEY > p.S);
+      const bool diag = (k0 + BKEY - 1 > qa0) || (k0 + BKEY > p.S);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           int key = k0 + mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
           float x = s[mb][i] * p.scale_log2;
-          if (diag && (key > query || key >= p.S)) x = -INFINITY;
+          if (diag && (key > qabs || key >= p.S)) x = -INFINITY;
           pv[mb * 16 + i] = x;
           mt = fmaxf(mt, x);
         }
@@ -208,9 +209,9 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
   }
 
   const float l_tot = wave_sum32(l_run);
-  if (query >= p.S) return;
+  if (query >= p.T) return;
   const float inv = 1.f / l_tot;
-  T* O = reinterpret_cast<T*>(p.o) + (((long long)b * p.S + query) * p.H + h) * p.dv;
+  T* O = reinterpret_cast<T*>(p.o) + (((long long)b * p.T + query) * p.H + h) * p.dv;
 #pragma unroll
   for (int mb = 0; mb < DVP / 32; ++mb)
 #pragma unroll
@@ -223,7 +224,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
 template <typename T, int DQP, int DVP>
 hipError_t launch_impl(const PrefillParams& p, hipStream_t s) {
   using C = PrefillCfg<T, DQP, DVP>;
-  dim3 grid((p.S + BQ - 1) / BQ, p.H, p.B);
+  dim3 grid((p.T + BQ - 1) / BQ, p.H, p.B);
   hipLaunchKernelGGL((prefill_kernel<T, DQP, DVP>), grid, dim3(256), C::LDS, s, p);
   return hipGetLastError();
 }

@@ -98,10 +98,11 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
   }
   const int qt = ntq - 1 - qrev;
   const int h = g % p.H, b = g / p.H;
-  const int S = p.S;
+  const int S = p.S;                                    // keys per sequence
   const int q0 = qt * FQ;
-  const int qw = q0 + QW * wave;                        // this wave's first query
-  const int kend = min(S, q0 + FQ);                     // keys 0 .. kend-1 (multiple of 64)
+  const int qw = q0 + QW * wave;                        // this wave's first query (index among the T)
+  const int qwa = p.q_off + qw;                         // its position
+  const int kend = min(S, p.q_off + q0 + FQ);           // keys 0 .. kend-1 (multiple of 64)
   const int ntiles = kend / FK;
   const long long bh = (long long)b * p.H + h;
 
@@ -109,8 +110,8 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
   Frag<bf16> qf[QB][C::KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = min(qw + 32 * qb + col, S - 1);
-    const bf16* qp = reinterpret_cast<const bf16*>(p.q) + (((long long)b * S + qi) * p.H + h) * (DN + DR) + 8 * half;
+    const int qi = min(qw + 32 * qb + col, p.T - 1);
+    const bf16* qp = reinterpret_cast<const bf16*>(p.q) + (((long long)b * p.T + qi) * p.H + h) * (DN + DR) + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = frag_load<bf16>(qp + 16 * ks);
   }
@@ -218,7 +219,7 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
     auto mask = [&](int kb, f32x16 (&sc)[QB]) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw + 32 * qb + col;
+        const int qi = qwa + 32 * qb + col;             // query position
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3) > qi) sc[qb][i] = -INFINITY;
@@ -358,10 +359,10 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
       barrier_only();
       if (it + FNST - 1 < ntiles) issue(it + FNST - 1);
       const int key0 = it * FK;
-      if (key0 > qw + QW - 1) continue;                     // every key of the tile is after this wave's queries
+      if (key0 > qwa + QW - 1) continue;                    // every key of the tile is after this wave's queries
       if (MODE != 0 && !redo) continue;
       const unsigned char* T = smem + (it % FNST) * C::STAGE;
-      const bool diag = key0 + 63 > qw;                     // some keys after some of this wave's queries
+      const bool diag = key0 + 63 > qwa;                    // some keys after some of this wave's queries
       tile(T, key0, M0{}, it == 0, diag);
     }
   };
@@ -402,8 +403,8 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const float inv = 1.f / lt;
     const int qi = qw + 32 * qb + col;
-    if (qi >= S) continue;
-    bf16* op = reinterpret_cast<bf16*>(p.o) + (((long long)b * S + qi) * p.H + h) * C::DV + 4 * half;
+    if (qi >= p.T) continue;
+    bf16* op = reinterpret_cast<bf16*>(p.o) + (((long long)b * p.T + qi) * p.H + h) * C::DV + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -426,7 +427,7 @@ namespace {
 template <int DN, int DR, int QB>
 hipError_t launch_flash(const FlashParams& pin, hipStream_t s) {
   FlashParams p = pin;
-  p.ntq = cdiv(p.S, FQ);
+  p.ntq = cdiv(p.T, FQ);
   dim3 grid(p.ntq * p.H * p.B);
   constexpr size_t lds = FlashCfg<DN, DR, QB>::LDS;
   hipLaunchKernelGGL((prefill_flash_kernel<DN, DR, QB>), grid, dim3(64 * (8 / QB)), lds, s, p);

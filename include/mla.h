@@ -71,7 +71,8 @@ typedef enum {
   MLA_OP_PREFILL = 1,
   MLA_OP_DECODE = 2,
   MLA_OP_DECODE_ATTENTION = 3,
-  MLA_OP_PREFILL_ATTENTION = 4
+  MLA_OP_PREFILL_ATTENTION = 4,
+  MLA_OP_PREFILL_CHUNK = 5
 } mla_op;
 
 /* Layer dimensions.
@@ -123,8 +124,9 @@ const char* mla_status_str(mla_status s);
 mla_status mla_validate(const mla_dims* dims);
 
 /* Bytes of device workspace entry point `op` needs for `batch` sequences of
- * `seq_or_max_ctx` tokens (prefill: S; decode: the largest ctx_len).  Returns 0 for
- * invalid arguments and for ops that need none (MLA_OP_CACHE_APPEND).  Host only. */
+ * `seq_or_max_ctx` tokens (prefill: S; decode: the largest ctx_len; chunked prefill:
+ * start_pos + T).  Returns 0 for invalid arguments and for ops that need none
+ * (MLA_OP_CACHE_APPEND).  Host only. */
 size_t mla_workspace_bytes(const mla_dims* dims, int op, int32_t batch, int32_t seq_or_max_ctx);
 
 /* Fused down-projection + RoPE + cache write ([DSV2 page] ``forward`` cached path:
@@ -192,6 +194,23 @@ mla_status mla_decode_attention(const mla_dims* dims, const void* q_lat, const v
 mla_status mla_prefill_attention(const mla_dims* dims, const mla_weights* w, const void* q,
                                  int32_t B, int32_t S, const mla_cache* cache, void* o,
                                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Continued (chunked) prefill: T new tokens per sequence at positions start_pos ..
+ * start_pos+T-1 over a cache whose rows 0..start_pos-1 already hold the earlier tokens'
+ * latents ([DSV2 page] ``forward`` with start_pos > 0: the new latents and rotary keys are
+ * written at rows start_pos.., the keys and values of rows 0..start_pos+T-1 are
+ * up-projected, and new token i attends to the keys at positions <= start_pos + i).
+ * start_pos = 0 gives mla_prefill with a cache.
+ *   x          [B][T][d_model]
+ *   start_pos  host int32, the same for every sequence (the page's start_pos)
+ *   cache      rows start_pos .. start_pos+T-1 of each sequence are written; rows
+ *              0..start_pos-1 are read and must hold the earlier tokens
+ *   y          [B][T][d_model] float32, fully overwritten
+ * Workspace: mla_workspace_bytes(dims, MLA_OP_PREFILL_CHUNK, B, start_pos + T).
+ * Errors: CAPACITY if B > max_batch or start_pos + T > max_seq. */
+mla_status mla_prefill_chunk(const mla_dims* dims, const mla_weights* w, const void* x,
+                             int32_t B, int32_t T, int32_t start_pos, const mla_cache* cache,
+                             float* y, void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

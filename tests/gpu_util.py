@@ -116,6 +116,14 @@ class Layer:
         M.mla_prefill(self.dims, self.ws_struct, x, B, S_, cache_struct, y, ws, n)
         return y
 
+    def prefill_chunk(self, x: torch.Tensor, start_pos: int, cache_struct) -> torch.Tensor:
+        """Continued prefill of x [B][T] at positions start_pos.. over the cached rows below."""
+        B, T = x.shape[0], x.shape[1]
+        y = torch.empty((B, T, self.cfg.d_model), dtype=torch.float32, device="cuda")
+        ws, n = self.workspace(M.MLA_OP_PREFILL_CHUNK, B, start_pos + T)
+        M.mla_prefill_chunk(self.dims, self.ws_struct, x, B, T, int(start_pos), cache_struct, y, ws, n)
+        return y
+
     def decode(self, x: torch.Tensor, ctx_len: Sequence[int], cache_struct) -> torch.Tensor:
         B = x.shape[0]
         y = torch.empty((B, self.cfg.d_model), dtype=torch.float32, device="cuda")

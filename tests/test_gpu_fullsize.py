@@ -142,3 +142,25 @@ def test_prefill_full(gu, name, sample_b, rows):
         gu.assert_close(got, want, cfg.dtype, f"y b={b} sampled rows together")
         c, _ = O.latent_rows(xs[b][:64], lay.prob.weights, d, np.arange(64))
         gu.assert_close(gu.to_host(ckv[b, :64]), c, cfg.dtype, f"cache rows 0..63 b={b}")
+
+
+def test_prefill_chunk_full(gu):
+    """Continued prefill at the DeepSeek-V2 prefill shape: 3072 cached tokens, 1024 new."""
+    cfg = S.CONFIGS["dsv2_prefill"]
+    B, start, T = cfg.batch, 3072, 1024
+    gu.say(f"[prefill-chunk-full] B={B} start={start} T={T}")
+    lay = gu.Layer(cfg)
+    ckv, kr = lay.new_cache(B, start + T, fill=3.0)
+    lay.fill_cache(ckv, kr, [start] * B, threads=S.host_threads())
+    xs = S.make_x_batch(cfg, [start + T] * B, threads=S.host_threads())
+    x = gu.to_dev(np.stack([xb[start:] for xb in xs]), cfg)
+    y = gu.to_host(lay.prefill_chunk(x, start, lay.cache_view(ckv, kr, 0, B)))
+    assert np.all(np.isfinite(y))
+    d = O.Dims.from_cfg(cfg)
+    rows = [0, 1, 63, 64, 511, 1023]
+    for b in [0, B - 1]:
+        want = O.forward(xs[b], lay.prob.weights, d, q_rows=[start + r for r in rows])
+        got = y[b][rows]
+        for i, r in enumerate(rows):
+            gu.assert_close(got[i], want[i], cfg.dtype, f"y b={b} row={start + r}")
+        gu.assert_close(got, want, cfg.dtype, f"y b={b} sampled rows together")

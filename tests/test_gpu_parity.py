@@ -116,6 +116,51 @@ def test_prefill(gu, cfg, with_cache):
 
 
 # ---------------------------------------------------------------------------
+# mla_prefill_chunk: continued prefill over an existing latent cache
+# ---------------------------------------------------------------------------
+CHUNK_CASES = [
+    (DSV2_PF, 128, 192),     # flash path: key offset and key count multiples of 64
+    (SMALL_PF, 64, 256),     # flash path, full-RoPE family (keys rotated after up-projection)
+    (MLRA_PF, 192, 128),     # flash path, latent blocks
+    (DSV2_P, 37, 50),        # generic path (offset not a multiple of 64), ragged tiles
+    (DSV2_PF, 0, 320),       # start 0: the same as mla_prefill with a cache
+    (TINY, 5, 3),            # fp32 workload
+]
+
+
+@pytest.mark.parametrize("cfg,start,T", CHUNK_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_prefill_chunk(gu, cfg, start, T):
+    gu.say(f"[prefill-chunk] {cfg.name} start={start} T={T}")
+    lay = layer(gu, cfg)
+    B = cfg.batch
+    max_seq = start + T + 7
+    ckv, kr = lay.new_cache(B, max_seq, fill=SENTINEL)
+    lay.fill_cache(ckv, kr, [start] * B)
+    xs = [S.make_x(cfg, b, start + T) for b in range(B)]
+    x = gu.to_dev(np.stack([xb[start:] for xb in xs]), cfg)
+    y = gu.to_host(lay.prefill_chunk(x, start, lay.cache_view(ckv, kr, 0, B)))
+    d = _dims(cfg)
+    ckv_h = gu.to_host(ckv)
+    for b in range(B):
+        want = O.forward(xs[b], lay.prob.weights, d, q_rows=np.arange(start, start + T))
+        gu.assert_close(y[b], want, cfg.dtype, f"y b={b}")
+        c, _ = O.latent_rows(xs[b][start:], lay.prob.weights, d, np.arange(start, start + T))
+        gu.assert_close(ckv_h[b, start:start + T], c, cfg.dtype, f"appended rows b={b}")
+        assert np.all(ckv_h[b, start + T:] == SENTINEL), "rows after the chunk changed"
+
+
+def test_prefill_chunk_capacity(gu):
+    import head_latent_attention_dkv_amd as M
+    cfg = DSV2_PF
+    lay = layer(gu, cfg)
+    ckv, kr = lay.new_cache(1, 100)
+    x = gu.to_dev(np.stack([S.make_x(cfg, 0, 64)]), cfg)
+    with pytest.raises(M.MLAError) as e:
+        lay.prefill_chunk(x, 40, lay.cache_view(ckv, kr, 0, 1))     # 40 + 64 > 100 rows
+    assert e.value.status == M.MLA_ERR_CAPACITY
+
+
+# ---------------------------------------------------------------------------
 # mla_decode: absorbed decode over the latent cache
 # ---------------------------------------------------------------------------
 DECODE_CASES = [
