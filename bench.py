@@ -273,6 +273,27 @@ def bench_prefill(cfg, steps, warmup):
         "attention_ms": ms_att, "attention_flop": core + kvup,
         "attention_TFLOPs": (core + kvup) / ms_att / 1e9,
     }
+    # continued prefill: the last quarter of each sequence over the cached first three
+    # quarters (the cache already holds every row; the call rewrites rows start.. with the
+    # same values)
+    start, T = (3 * S_ // 4) // 64 * 64, S_ - (3 * S_ // 4) // 64 * 64
+    if 0 < start < S_:
+        xc = x[:, start:].contiguous()
+        yc = torch.empty((B, T, cfg.d_model), dtype=torch.float32, device="cuda")
+        wsc, nwsc = d.workspace(M.MLA_OP_PREFILL_CHUNK, B, S_)
+
+        def chunk(i):
+            M.mla_prefill_chunk(d.dims, d.wst, xc, B, T, start, cs, yc, wsc, nwsc)
+
+        log(f"[bench] {cfg.name}: timing mla_prefill_chunk (start {start}, {T} new tokens)")
+        st_chunk = {}
+        ms_chunk = timed(torch, chunk, steps, warmup, st_chunk)
+        core_c = 2.0 * B * H * ((S_ * (S_ + 1) - start * (start + 1)) / 2) * (dn + dr + dv)
+        proj_c = 2.0 * B * T * sum(v.size for k, v in w.items() if k not in ("w_uk", "w_uv"))
+        flop_c = core_c + kvup + proj_c
+        res["chunk"] = {"start": start, "new_tokens": T, "ms_per_call": ms_chunk, "stats": st_chunk,
+                        "flop": flop_c, "TFLOPs": flop_c / ms_chunk / 1e9,
+                        "new_tokens_per_s": B * T / ms_chunk * 1e3}
     return res
 
 
@@ -597,6 +618,14 @@ def main():
                      "algorithmic_flop_per_launch": pre["attention_flop"], "ms_per_launch": pre["attention_ms"],
                      "timing": pre["attention_stats"]},
     }
+    if "chunk" in pre:
+        ch = pre["chunk"]
+        line["prefill_chunk"] = {
+            "workload": f"DeepSeek-V2-shaped continued prefill B=4: {ch['new_tokens']} new tokens over "
+                        f"{ch['start']} cached (mla_prefill_chunk)",
+            "ms_per_call": ch["ms_per_call"], "timing": ch["stats"], "TFLOPs": ch["TFLOPs"],
+            "frac_of_mfma_peak": ch["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, "new_tokens_per_s": ch["new_tokens_per_s"],
+            "algorithmic_flop_per_call": ch["flop"]}
     ml = out["mlra"]
     line["mlra_decode"] = {
         "workload": "MLRA decode B=128, ctx ~ U[512,16384], 4 latent heads x rank 128, H=16, d_model=2048",
