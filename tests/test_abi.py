@@ -123,6 +123,16 @@ def test_entry_points_report_errors_before_launch():
     assert L.mla_decode(by(d), by(w), FAKE, 2, FAKE, 8, by(cache), FAKE, None, need, None) == M.MLA_ERR_WORKSPACE
     need = M.mla_workspace_bytes(d, M.MLA_OP_PREFILL, 2, 16)
     assert L.mla_prefill(by(d), by(w), FAKE, 2, 16, None, FAKE, FAKE, need - 1, None) == M.MLA_ERR_WORKSPACE
+    # continued prefill: capacity (start_pos + T beyond max_seq, batch beyond max_batch),
+    # null pointers, negative start, workspace sized for start_pos + T
+    assert L.mla_prefill_chunk(by(d), by(w), FAKE, 2, 4, 13, by(cache), FAKE, FAKE, 1 << 30, None) == M.MLA_ERR_CAPACITY
+    assert L.mla_prefill_chunk(by(d), by(w), FAKE, 3, 4, 0, by(cache), FAKE, FAKE, 1 << 30, None) == M.MLA_ERR_CAPACITY
+    assert L.mla_prefill_chunk(by(d), by(w), None, 2, 4, 0, by(cache), FAKE, FAKE, 1 << 30, None) == M.MLA_ERR_INVALID_ARG
+    assert L.mla_prefill_chunk(by(d), by(w), FAKE, 2, 4, -1, by(cache), FAKE, FAKE, 1 << 30, None) == M.MLA_ERR_INVALID_ARG
+    assert L.mla_prefill_chunk(by(d), by(w), FAKE, 2, 4, 8, None, FAKE, FAKE, 1 << 30, None) == M.MLA_ERR_INVALID_ARG
+    need = M.mla_workspace_bytes(d, M.MLA_OP_PREFILL_CHUNK, 2, 12)
+    assert need > M.mla_workspace_bytes(d, M.MLA_OP_PREFILL, 2, 12)
+    assert L.mla_prefill_chunk(by(d), by(w), FAKE, 2, 4, 8, by(cache), FAKE, FAKE, need - 1, None) == M.MLA_ERR_WORKSPACE
     # decode of the half-split family is not absorbable
     dr = _dims(family="fullrope", d_rope=0, d_nope=16)
     assert L.mla_decode(by(dr), by(w), FAKE, 2, FAKE, 8, by(cache), FAKE, FAKE, 1 << 30, None) == M.MLA_ERR_UNSUPPORTED
