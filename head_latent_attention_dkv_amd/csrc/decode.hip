@@ -220,11 +220,11 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     }
 }
 
-// z[b][h] = sum_s 2^(m_s - M) z_s / sum_s 2^(m_s - M) l_s over the splits of sequence b.
-// One 64-lane workgroup per (head, sequence); lane c owns CPT consecutive columns (vector
+// z[b][h] = sum_s 2^(m_s - M) z_s / sum_s 2^(m_s - M) l_s over the splits of sequence b
+// (PB: the splits stored y_s = z_s / l_s in bf16, so z_s = l_s y_s).  One 64-lane workgroup per (head, sequence); lane c owns CPT consecutive columns (vector
 // loads), the split weights are formed once per split, and the split loop is unrolled so
 // that several partial rows are in flight at once.
-template <typename T, int DL>
+template <typename T, int DL, bool PB>
 __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   constexpr int CPT = DL >= 64 ? DL / 64 : 1;
   const int head = blockIdx.x;
@@ -242,12 +242,24 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   float a[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) a[j] = 0.f;
+  // PB: split s holds z_s / l_s in bf16 and weighs l_s 2^(m_s - M); otherwise z_s in fp32
+  // with weight 2^(m_s - M)
   const float* zs = p.part_z + base * DL + c0;
+  const bf16* ys = reinterpret_cast<const bf16*>(p.part_z) + base * DL + c0;
 #pragma unroll 4
   for (int s = 0; s < ns; ++s) {
-    const float w = exp2f(p.part_ml[(base + s) * 2] - M);
+    float w = exp2f(p.part_ml[(base + s) * 2] - M);
     float v[CPT];
-    if constexpr (CPT % 4 == 0) {
+    if constexpr (PB) {
+      static_assert(CPT % 8 == 0, "16-byte partial loads");
+      w *= p.part_ml[(base + s) * 2 + 1];
+#pragma unroll
+      for (int j = 0; j < CPT; j += 8) {
+        const bf16x8 y = *reinterpret_cast<const bf16x8*>(ys + (long long)s * DL + j);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j + e] = (float)y[e];
+      }
+    } else if constexpr (CPT % 4 == 0) {
 #pragma unroll
       for (int j = 0; j < CPT; j += 4) *reinterpret_cast<f32x4*>(v + j) = *reinterpret_cast<const f32x4*>(zs + (long long)s * DL + j);
     } else {
@@ -263,9 +275,9 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
     if (c0 + j < p.rb) z[j] = from_f32<T>(a[j] * inv);
 }
 
-template <typename T, int DL>
+template <typename T, int DL, bool PB = false>
 hipError_t launch_combine_impl(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<T, DL>), dim3(p.H, p.B), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((combine_kernel<T, DL, PB>), dim3(p.H, p.B), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -296,6 +308,8 @@ bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, i
 
 hipError_t launch_combine(const DecodeParams& p, bool use_bf16, int dl, hipStream_t s) {
   if (use_bf16) {
+    if (dl == 512 && p.part_bf16) return launch_combine_impl<bf16, 512, true>(p, s);
+    if (p.part_bf16) return hipErrorInvalidValue;
     if (dl == 512) return launch_combine_impl<bf16, 512>(p, s);
     if (dl == 128) return launch_combine_impl<bf16, 128>(p, s);
   } else {

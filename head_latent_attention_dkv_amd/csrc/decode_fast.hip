@@ -515,9 +515,9 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
     for (int st = 0; st < NSTAGE - 1; ++st)
       if (st < ntiles) issue_tile(st, st);
     for (int it = 0; it < ntiles; ++it) {
-      const int left = ntiles - 1 - it;
-      if (left >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
-      else if (left >= 1) wait_vmcnt<DMA_PER_WAVE>();
+      // wait until only the newest tile is outstanding: two tiles in flight per CU while a
+      // tile computes (a third in flight measured slower: more concurrent DRAM streams)
+      if (ntiles - 1 - it >= 1) wait_vmcnt<DMA_PER_WAVE>();
       else wait_vmcnt<0>();
       barrier_only();
       if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
@@ -557,14 +557,19 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
     p.part_ml[pidx * 2 + 0] = m_ref;
     p.part_ml[pidx * 2 + 1] = l_tot;
   }
+  // The split's result is stored normalised (z / l, bf16, like the output z itself); the
+  // combine weights it by l 2^(m - M) in fp32.  l >= 1: the reference maximum is a score of
+  // this split, whose p is 1.
   // accumulator element e of lane l in block mb: latent column 32 mb + 8 (e/4) + 4 (l/32) + e%4
-  float* pz = p.part_z + pidx * VL + 4 * half;
+  const float inv_l = 1.f / l_tot;
+  bf16* pz = reinterpret_cast<bf16*>(p.part_z) + pidx * VL + 4 * half;
 #pragma unroll
   for (int mb = 0; mb < MBS; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4*>(pz + 32 * mb + 8 * q) =
-          (f32x4){acc[mb][4 * q + 0], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
+      *reinterpret_cast<bf16x4*>(pz + 32 * mb + 8 * q) =
+          (bf16x4){(bf16)(acc[mb][4 * q + 0] * inv_l), (bf16)(acc[mb][4 * q + 1] * inv_l),
+                   (bf16)(acc[mb][4 * q + 2] * inv_l), (bf16)(acc[mb][4 * q + 3] * inv_l)};
 }
 
 }  // namespace
@@ -585,6 +590,8 @@ bool decode_fast_supported(const DecodeParams& p, int* variant) {
 }
 
 int decode_fast_head_tile(int variant) { return variant == 2 ? 16 : 128; }
+
+bool decode_fast_bf16_partials(int variant) { return variant == 3 || variant == 4; }
 
 hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s) {
   dim3 grid(p.nsplit, p.head_tiles, p.B);

@@ -113,8 +113,9 @@ struct DecodeParams {
   int nsplit;               // splits allocated per (b, head)
   int head_tiles;           // head tiles per latent block
   float scale_log2;         // softmax scale * log2(e)
-  float* part_z;            // [B][H][nsplit][DLP]
+  float* part_z;            // [B][H][nsplit][DLP]: fp32 z, or bf16 z / l when part_bf16
   float* part_ml;           // [B][H][nsplit][2]  (running max in log2 units, sum)
+  int part_bf16;            // set by the launcher for the split kernel that stores bf16 z / l
   void* z;                  // [B][H][rb] output
 };
 
@@ -127,6 +128,8 @@ hipError_t launch_combine(const DecodeParams& p, bool use_bf16, int dl_pad, hipS
 // heads one workgroup covers, and the launch (split kernel only; combine separately).
 bool decode_fast_supported(const DecodeParams& p, int* variant);
 int decode_fast_head_tile(int variant);
+// whether the variant's split kernel stores its partial results as bf16 z / l
+bool decode_fast_bf16_partials(int variant);
 hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s);
 
 // ---------------------------------------------------------------------------

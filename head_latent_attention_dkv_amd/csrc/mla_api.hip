@@ -107,8 +107,10 @@ hipError_t run_decode_attention(const mla_dims* d, DecodeParams p, const SplitPl
                     aligned16(p.q_lat) && (p.q_lat_hs % 8 == 0) && aligned16(p.ckv) &&
                     (p.d_rope == 0 || (aligned16(p.q_rope) && p.q_rope_hs % 8 == 0 && aligned16(p.kr)));
   hipError_t e;
+  p.part_bf16 = 0;
   if (fast) {
     p.head_tiles = sp.fast_head_tiles;
+    p.part_bf16 = decode_fast_bf16_partials(variant) ? 1 : 0;
     e = launch_decode_fast(p, variant, st);
   } else {
     p.head_tiles = sp.head_tiles;
