@@ -371,7 +371,11 @@ bool use_stream(int K) { return K % kStreamKT == 0; }
 
 struct SkinnyPlan {
   int rows, splits, kchunk;
+  bool deep = false;   // one block per CU: 128-row tiles take four stages instead of three
 };
+
+constexpr int kCUs = 256;                 // compute units of one MI355X
+constexpr int kLongSlab = 2048;           // K per block from which one block per CU pays
 
 // Streaming plan: the weight-row tile (32, 64 or 128 rows) and the number of K slabs that
 // reach kMinBlocks blocks (or as many as the shape allows) with the least extra traffic:
@@ -405,6 +409,20 @@ SkinnyPlan plan_stream(int M, int N, int K, int groups) {
       best_blocks = (int)blocks;
     }
   }
+  // Between one and two blocks per CU, the CUs holding two set the time.  When every block's
+  // K slab stays long, fewer slabs that give one block per CU are faster (the decode step's
+  // output projection, 5120 x 16384 at 64 rows: 128 rows x 10 slabs 46 us, x 6 slabs 40 us).
+  if (best_blocks > kCUs && best_blocks < 2 * kCUs) {
+    const long long tiles = (long long)cdiv(N, best.rows) * groups;
+    const int s = (int)(kCUs / tiles);
+    if (s >= 1) {
+      int kc = round_up(cdiv(K, s), kStreamKT);
+      if (kc >= kLongSlab) {
+        const int s2 = cdiv(K, kc);
+        best = {best.rows, s2, s2 <= 1 ? K : kc, true};
+      }
+    }
+  }
   return best;
 }
 
@@ -418,9 +436,8 @@ SkinnyPlan plan(int M, int N, int K, int groups) {
   return use_stream(K) ? plan_stream(M, N, K, groups) : plan_direct(M, N, K, groups);
 }
 
-template <int CB, int ROWS>
+template <int CB, int ROWS, int NST = ROWS == 128 ? 3 : 4>
 hipError_t launch_stream(const GemmParams& p, int groups, hipStream_t s) {
-  constexpr int NST = ROWS == 128 ? 3 : 4;
   using C = StreamCfg<CB, ROWS, kStreamKT, NST>;
   const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
   dim3 grid(cdiv(N, ROWS), p.splits, groups);
@@ -429,10 +446,13 @@ hipError_t launch_stream(const GemmParams& p, int groups, hipStream_t s) {
 }
 
 template <int CB>
-hipError_t launch_stream_rows(const GemmParams& p, int rows, int groups, hipStream_t s) {
-  if (rows == 32) return launch_stream<CB, 32>(p, groups, s);
-  if (rows == 64) return launch_stream<CB, 64>(p, groups, s);
-  if constexpr (CB <= 2) return launch_stream<CB, 128>(p, groups, s);
+hipError_t launch_stream_rows(const GemmParams& p, const SkinnyPlan& pl, int groups, hipStream_t s) {
+  if (pl.rows == 32) return launch_stream<CB, 32>(p, groups, s);
+  if (pl.rows == 64) return launch_stream<CB, 64>(p, groups, s);
+  if constexpr (CB <= 2) {
+    if (pl.deep) return launch_stream<CB, 128, 4>(p, groups, s);
+    return launch_stream<CB, 128>(p, groups, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -469,14 +489,15 @@ hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s) {
   if (pl.splits > 1 && (p.part == nullptr || p.part_bytes < need)) {
     pl.splits = 1;
     pl.kchunk = p.K;
+    pl.deep = false;
   }
   p.splits = pl.splits;
   p.kchunk = pl.kchunk;
   hipError_t e;
   if (use_stream(p.K)) {
-    if (p.M <= 32) e = launch_stream_rows<1>(p, pl.rows, groups, s);
-    else if (p.M <= 64) e = launch_stream_rows<2>(p, pl.rows, groups, s);
-    else e = launch_stream_rows<4>(p, pl.rows, groups, s);
+    if (p.M <= 32) e = launch_stream_rows<1>(p, pl, groups, s);
+    else if (p.M <= 64) e = launch_stream_rows<2>(p, pl, groups, s);
+    else e = launch_stream_rows<4>(p, pl, groups, s);
   } else {
     dim3 grid(cdiv(N, kCols), p.splits, groups);
     if (p.M <= 32)
