@@ -289,6 +289,130 @@ hipError_t launch_impl(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Decode step only: the combine of the 128-head split kernel's bf16 partials fused with the
+// per-head value up-projection o[b][h] = W_UV,h z[b][h] (W_UV,h = rows h*DV .. h*DV+DV-1 of
+// w_uv, [DV][512]), so z never leaves the workgroup.  One workgroup per (head, 32 sequences):
+//   1. wave w combines sequences 8w .. 8w+7 (lane: 8 consecutive latent columns; split
+//      weights l_s 2^(m_s - M) / sum; the loads of all splits of four sequences are in
+//      flight together) and leaves z in LDS as bf16 (the precision the separate combine
+//      hands the product); the wave's weight rows for step 2 are loaded before all this;
+//   2. O^T[DV x 32 sequences] = W_UV,h[DV x 512] . Z^T: wave w takes rows 32w .. 32w+31 with
+//      32x32x16 MFMAs, A straight from global memory, B from LDS.  The contraction index is
+//      relabelled (k-step ks, lane half hk <-> latent columns 256 hk + 8 ks ..) identically on
+//      both operands, so every lane reads one contiguous 512-byte run of its weight row.
+template <int DV>
+__global__ void __launch_bounds__(64 * (DV / 32)) combine_uv_kernel(DecodeParams p, const bf16* __restrict__ w_uv,
+                                                                    bf16* __restrict__ o) {
+  constexpr int DL = 512, SEQ = 32, NWV = DV / 32, SPW = SEQ / NWV, LDZ = DL + 8, MAXS = 4;
+  __shared__ __attribute__((aligned(16))) bf16 zs[SEQ * LDZ];
+  const int h = blockIdx.x, b0 = blockIdx.y * SEQ;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bf16* part = reinterpret_cast<const bf16*>(p.part_z);
+  // this wave's W_UV,h rows go out first; their latency overlaps the combine
+  const int col = lane & 31, hk = lane >> 5;
+  const bf16* wrow = w_uv + ((long long)h * DV + 32 * wave + col) * DL + 256 * hk;
+  bf16x8 af[32];
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(wrow + 8 * ks);
+
+  // 1. combine.  Split weights first: thread (sequence t/8, lane t%8) scans splits t%8,
+  // t%8 + 8, ..; the eight lanes of a sequence meet through lane shuffles.
+  __shared__ float wts[SEQ][MAXS], smx[SEQ], sinv[SEQ];
+  __shared__ int sns[SEQ];
+  __shared__ long long sbase[SEQ];
+  {
+    const int sl = threadIdx.x >> 3, j = threadIdx.x & 7;
+    const int b = b0 + sl;
+    const int ns = b < p.B ? (p.ctx_len[b] + 1 + p.chunk - 1) / p.chunk : 0;
+    const long long base = ((long long)min(b, p.B - 1) * p.H + h) * p.nsplit;
+    float mx = -INFINITY;
+    for (int s = j; s < ns; s += 8) mx = fmaxf(mx, p.part_ml[(base + s) * 2]);
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    float L = 0.f;
+    for (int s = j; s < ns; s += 8) L += exp2f(p.part_ml[(base + s) * 2] - mx) * p.part_ml[(base + s) * 2 + 1];
+    L += __shfl_xor(L, 1);
+    L += __shfl_xor(L, 2);
+    L += __shfl_xor(L, 4);
+    const float inv = ns > 0 ? 1.f / L : 0.f;
+    if (j < MAXS) wts[sl][j] = j < ns ? exp2f(p.part_ml[(base + j) * 2] - mx) * p.part_ml[(base + j) * 2 + 1] * inv : 0.f;
+    if (j == 0) {
+      smx[sl] = mx;
+      sinv[sl] = inv;
+      sns[sl] = ns;
+      sbase[sl] = base;
+    }
+  }
+  __syncthreads();
+  long long rowb[SPW];
+  int nsb[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    rowb[i] = sbase[wave * SPW + i];
+    nsb[i] = sns[wave * SPW + i];
+  }
+  constexpr int SH = SPW / 2;                             // sequences per half
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    float a[SH][8];
+#pragma unroll
+    for (int i = 0; i < SH; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[i][e] = 0.f;
+    for (int s0 = 0; s0 < p.nsplit; s0 += MAXS) {
+      bf16x8 y[SH][MAXS];
+#pragma unroll
+      for (int i = 0; i < SH; ++i)
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+          const int ii = hh * SH + i;
+          const int sc = min(s0 + s, max(nsb[ii] - 1, 0));  // past the last split: a valid row, weight 0
+          y[i][s] = *reinterpret_cast<const bf16x8*>(part + (rowb[ii] + sc) * DL + 8 * lane);
+        }
+#pragma unroll
+      for (int i = 0; i < SH; ++i)
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+          const int ii = hh * SH + i, sl = wave * SPW + ii;
+          float w = wts[sl][s];
+          if (s0 > 0) {                                   // splits beyond the first MAXS
+            const int sg = s0 + s;
+            w = sg < nsb[ii] ? exp2f(p.part_ml[(rowb[ii] + sg) * 2] - smx[sl]) * p.part_ml[(rowb[ii] + sg) * 2 + 1] * sinv[sl] : 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[i][e] += w * (float)y[i][s][e];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SH; ++i) {
+      bf16x8 zz;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zz[e] = (bf16)a[i][e];
+      *reinterpret_cast<bf16x8*>(zs + (wave * SPW + hh * SH + i) * LDZ + 8 * lane) = zz;
+    }
+  }
+  __syncthreads();
+
+  // 2. O^T = W_UV,h . Z^T
+  const bf16* zrow = zs + col * LDZ + 256 * hk;
+  f32x16 c0 = f32x16{}, c1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 32; ks += 2) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], *reinterpret_cast<const bf16x8*>(zrow + 8 * ks), c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks + 1], *reinterpret_cast<const bf16x8*>(zrow + 8 * ks + 8), c1, 0, 0, 0);
+  }
+  // lane: sequence b0 + col, rows 32 wave + 8 q + 4 hk + 0..3
+  const int b = b0 + col;
+  if (b >= p.B) return;
+  bf16* orow = o + ((long long)b * p.H + h) * DV + 32 * wave + 4 * hk;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<bf16x4*>(orow + 8 * q) =
+        (bf16x4){(bf16)(c0[4 * q] + c1[4 * q]), (bf16)(c0[4 * q + 1] + c1[4 * q + 1]),
+                 (bf16)(c0[4 * q + 2] + c1[4 * q + 2]), (bf16)(c0[4 * q + 3] + c1[4 * q + 3])};
+}
+
 }  // namespace
 
 bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, int* dr_pad, int* nw) {
@@ -317,6 +441,18 @@ hipError_t launch_combine(const DecodeParams& p, bool use_bf16, int dl, hipStrea
     if (dl == 128) return launch_combine_impl<float, 128>(p, s);
   }
   return hipErrorInvalidValue;
+}
+
+bool combine_uv_supported(const DecodeParams& p, int d_v, const void* w_uv) {
+  return p.part_bf16 && p.rb == 512 && p.r_kv == 512 && d_v == 128 &&
+         (reinterpret_cast<uintptr_t>(w_uv) & 15) == 0;
+}
+
+hipError_t launch_combine_uv(const DecodeParams& p, int d_v, const void* w_uv, void* o, hipStream_t s) {
+  if (!combine_uv_supported(p, d_v, w_uv)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_uv_kernel<128>, dim3(p.H, (p.B + 31) / 32), dim3(256), 0, s, p,
+                     reinterpret_cast<const bf16*>(w_uv), reinterpret_cast<bf16*>(o));
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& p, bool use_bf16, int dl, int dr, int nw, hipStream_t s) {

@@ -123,6 +123,10 @@ hipError_t launch_decode(const DecodeParams& p, bool use_bf16, int dl_pad, int d
                          hipStream_t s);
 bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, int* dr_pad, int* nw);
 hipError_t launch_combine(const DecodeParams& p, bool use_bf16, int dl_pad, hipStream_t s);
+// Decode step: combine of bf16 partials (part_bf16) fused with o[b][h] = W_UV,h z[b][h]
+// (latent 512, d_v 128; o bf16 [B][H][d_v]).
+bool combine_uv_supported(const DecodeParams& p, int d_v, const void* w_uv);
+hipError_t launch_combine_uv(const DecodeParams& p, int d_v, const void* w_uv, void* o, hipStream_t s);
 
 // bf16 fast path (direct-to-LDS staging, LDS transpose loads): shapes it serves, the
 // heads one workgroup covers, and the launch (split kernel only; combine separately).

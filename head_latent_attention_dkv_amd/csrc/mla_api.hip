@@ -100,8 +100,11 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Split kernel (fast path when shapes and alignment allow) followed by the combine.
-hipError_t run_decode_attention(const mla_dims* d, DecodeParams p, const SplitPlan& sp, hipStream_t st) {
+// Split kernel (fast path when shapes and alignment allow) followed by the combine.  Given
+// w_uv and o (the decode step), the combine also applies the value up-projection when a
+// fused kernel serves the shape; *fused_uv says whether it did (z is then not written).
+hipError_t run_decode_attention(const mla_dims* d, DecodeParams p, const SplitPlan& sp, hipStream_t st,
+                                const void* w_uv = nullptr, void* o = nullptr, bool* fused_uv = nullptr) {
   int variant = -1;
   const bool fast = sp.fast_variant >= 0 && decode_fast_supported(p, &variant) &&
                     aligned16(p.q_lat) && (p.q_lat_hs % 8 == 0) && aligned16(p.ckv) &&
@@ -117,6 +120,10 @@ hipError_t run_decode_attention(const mla_dims* d, DecodeParams p, const SplitPl
     e = launch_decode(p, is_bf16(d), sp.dl, sp.dr, sp.nw, st);
   }
   if (e != hipSuccess) return e;
+  if (fused_uv && w_uv && o && combine_uv_supported(p, d->d_v, w_uv)) {
+    *fused_uv = true;
+    return launch_combine_uv(p, d->d_v, w_uv, o, st);
+  }
   return launch_combine(p, is_bf16(d), sp.dl, st);
 }
 
@@ -767,13 +774,16 @@ mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, in
   void* z = at(ws, lay.z);
   p.z = z;
   SplitPlan sp = plan_decode(d, B, max_ctx);
-  e = run_decode_attention(d, p, sp, st);
-  if (e != hipSuccess) return MLA_ERR_HIP;
-  // 5. o[b][h] = W_UV,h z[b][h], then y = W_O o
   void* o = at(ws, lay.o);
-  e = run_per_head(d, z, (long long)H * rb, rb, rb, w->w_uv, false, d->d_v, o,
-                   (long long)H * d->d_v, d->d_v, B, st, sw);
+  bool fused_uv = false;
+  e = run_decode_attention(d, p, sp, st, w->w_uv, o, &fused_uv);
   if (e != hipSuccess) return MLA_ERR_HIP;
+  // 5. o[b][h] = W_UV,h z[b][h] (unless fused into the combine), then y = W_O o
+  if (!fused_uv) {
+    e = run_per_head(d, z, (long long)H * rb, rb, rb, w->w_uv, false, d->d_v, o,
+                     (long long)H * d->d_v, d->d_v, B, st, sw);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
   return hip_status(run_out_proj(d, w, o, B, y, st, sw));
 }
 
