@@ -3,7 +3,7 @@
 One "step" is one whole mla_decode call of the DeepSeek-V2-shaped decode workload
 (B=64 sequences, 4096 cached tokens + 1 new token each, H=128, latent 512 + rotary 64,
 query latent 1536, d_model 5120, absorbed form): append, query path, absorbed query,
-split-context latent attention + combine, W_UV and W_O.  `value` is the latent-cache
+split-context latent attention, the combine fused with W_UV, and W_O.  `value` is the latent-cache
 bytes that step streams (sum over sequences of (ctx+1) * (512+64) * 2 B = 302.06 MB)
 divided by the measured step time.  The latent cache rotates between two copies
 (604 MB > the 256 MB Infinity Cache) so that every step reads it from HBM.  All inputs
@@ -32,6 +32,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -389,13 +390,13 @@ def summarize_profiles(d):
         name = name.replace("mla::(anonymous namespace)::", "").replace("(mla::GemmParams)", "")
         name = name.replace("(mla::DecodeParams)", "").replace("void ", "")
         if name.startswith("_ZN3mla"):
+            m = re.match(r"_ZN3mla12_GLOBAL__N_114combine_kernelIDF16bLi(\d+)ELb([01])E", name)
+            if m:
+                return f"combine_kernel<bf16,{m.group(1)}{',bf16 partials' if m.group(2) == '1' else ''}>"
             name = {"_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi64ELi64EEEvNS_10GemmParamsE": "gemm_kernel<bf16,64,64>",
                     "_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi128ELi128EEEvNS_10GemmParamsE":
-                        "gemm_kernel<bf16,128,128>",
-                    "_ZN3mla12_GLOBAL__N_114combine_kernelIDF16bLi512EEEvNS_12DecodeParamsE":
-                        "combine_kernel<bf16,512>",
-                    "_ZN3mla12_GLOBAL__N_114combine_kernelIDF16bLi128EEEvNS_12DecodeParamsE":
-                        "combine_kernel<bf16,128>"}.get(name, name)
+                        "gemm_kernel<bf16,128,128>"}.get(name, name)
+        name = re.sub(r"\(.*$", "", name)             # argument list
         return name[:70]
 
     lines = ["# Kernel times: DeepSeek-V2-shaped decode step (B=64, 4096 cached tokens, H=128)", "",
@@ -417,22 +418,19 @@ def summarize_profiles(d):
     if trace:
         trace.sort(key=lambda r: int(r["Start_Timestamp"]))
         # one timed mla_decode step.  Launch order inside the call: W_DQ (+reduce), queries
-        # (+reduce), latent (+reduce), absorbed query, attention, combine, W_UV (+reduce),
-        # W_O (+reduce); the first timing loop runs whole calls, so a step ends after the
-        # W_O product that follows a combine, and starts after the previous step's end.
+        # (+reduce), latent (+reduce), absorbed query, attention, the combine fused with W_UV,
+        # W_O (+reduce); the first timing loop runs whole calls, so a step ends after the W_O
+        # product that follows the fused combine, and starts after the previous step's end.
         names = [short(r["Kernel_Name"]) for r in trace]
 
         def step_end(c):
-            j = c + 1                                   # W_UV
-            if j + 1 < len(names) and names[j + 1] == "split_reduce_kernel":
-                j += 1
-            j += 1                                      # W_O
+            j = c + 1                                   # W_O
             if j + 1 < len(names) and names[j + 1] == "split_reduce_kernel":
                 j += 1
             return j
 
-        combines = [i for i, n in enumerate(names) if n.startswith("combine_kernel")]
-        ends = [step_end(c) for c in combines if c + 2 < len(names) and names[c + 1].startswith("skinny")]
+        combines = [i for i, n in enumerate(names) if n.startswith("combine_uv_kernel")]
+        ends = [step_end(c) for c in combines if c + 1 < len(names) and names[c + 1].startswith("skinny")]
         step = (ends[-2] + 1, ends[-1]) if len(ends) >= 2 else None
         if step:
             lines += ["One timed mla_decode step (kernel trace):", "",
