@@ -1,9 +1,10 @@
 // Large projection GEMM for gfx950 (bf16, many rows): out[m, n] = sum_k A[m, k] W[n, k].
 //
-// Workgroup tile 256 x 256, 8 waves (two per SIMD) in a 4 x 2 grid, each wave a 64 x 128
-// block of 32x32x16 MFMA accumulators (8 x 16 fp32 per lane, in the accumulation registers).  K
-// advances 32 at a time through NST LDS stages filled by 16-byte direct-to-LDS copies:
-// each copy instruction moves 16 rows x 64 bytes of A or of W.  Rows are 64 bytes (four
+// Workgroup tile 256 x 256, 8 waves (two per SIMD) in a 4 x 2 grid, or 256 x 128 with 4 waves
+// in a 4 x 1 grid and two workgroups per CU (one's output stage overlaps the other's main
+// loop); each wave a 64 x 128 block of 32x32x16 MFMA accumulators (8 x 16 fp32 per lane, in
+// the accumulation registers).  K advances 32 at a time through NST LDS stages filled by
+// 16-byte direct-to-LDS copies: each copy instruction moves 16 rows x 64 bytes of A or of W.  Rows are 64 bytes (four
 // 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), which puts the 8 rows of
 // one LDS read phase (row stride 64 B) on 8 distinct 16-byte bank windows.
 //
@@ -24,16 +25,27 @@ namespace mla {
 
 namespace {
 
-constexpr int GBM = 256, GBN = 256, GBK = 32, GNST = 4, GNW = 8;
-constexpr int G_AB = GBM * GBK * 2;                 // A bytes per stage (= W bytes)
-constexpr int G_STAGE = 2 * G_AB;                   // 32 KB
-constexpr int G_CPW = (G_AB / 1024) / GNW;          // copies per wave per operand per stage (2)
+constexpr int GBM = 256, GBK = 32;
+constexpr int G_AB = GBM * GBK * 2;                 // A bytes per stage (16 KB)
 constexpr int G_LDC = 128 + 4;                      // epilogue LDS row stride (floats)
-constexpr size_t G_EPI = (size_t)GNW * 32 * G_LDC * 4;   // per-wave 32-row epilogue chunks
-constexpr size_t G_LDS = (size_t)GNST * G_STAGE > G_EPI ? (size_t)GNST * G_STAGE : G_EPI;
 constexpr int KV_CS = 72;                           // bf16 column stride (bytes) of the key transpose
 constexpr int KV_BUF = 128 * KV_CS;                 // one 32-row x 128-column chunk
-static_assert((size_t)GNW * KV_BUF <= G_LDS, "key transpose buffers fit in the stages");
+
+template <int NW>
+struct BigCfg {
+  static constexpr int BN = 32 * NW;                // workgroup columns (256 or 128)
+  static constexpr int NST = NW == 8 ? 4 : 3;       // LDS stages
+  static constexpr int WB = BN * GBK * 2;           // W bytes per stage
+  static constexpr int STAGE = G_AB + WB;
+  static constexpr int A_CPW = (G_AB / 1024) / NW;  // copies per wave per stage: A, W
+  static constexpr int W_CPW = (WB / 1024) / NW;
+  static constexpr int DPW = A_CPW + W_CPW;
+  static constexpr size_t EPI = (size_t)NW * 32 * G_LDC * 4;   // per-wave 32-row epilogue chunks
+  static constexpr size_t LDS = (size_t)NST * STAGE > EPI ? (size_t)NST * STAGE : EPI;
+  static constexpr int MINB = NW == 8 ? 1 : 2;      // workgroups per CU
+  static_assert((size_t)NW * KV_BUF <= LDS, "key transpose buffers fit in the stages");
+  static_assert(MINB * LDS <= 160 * 1024, "workgroups per CU fit the LDS");
+};
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -51,15 +63,17 @@ __device__ __forceinline__ int opaque_int(int x) {
 
 // DIRECT: the flash-layout output stage (own instantiation: sharing one register allocation
 // with the generic stage costs spills)
-template <bool DIRECT>
-__global__ void __launch_bounds__(64 * GNW, 1) gemm_big_kernel(GemmParams p) {
+template <bool DIRECT, int NW>
+__global__ void __launch_bounds__(64 * NW, BigCfg<NW>::MINB) gemm_big_kernel(GemmParams p) {
+  using C = BigCfg<NW>;
+  constexpr int GNST = C::NST;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;             // 64-row block wm, 128-column block wn
+  const int wm = wave / (NW / 4), wn = wave % (NW / 4);   // 64-row block wm, 128-column block wn
   const int col = lane & 31, half = lane >> 5;
-  const int n0 = blockIdx.x * GBN;
+  const int n0 = blockIdx.x * C::BN;
   const int m0 = blockIdx.y * GBM;
   const int z = blockIdx.z;
   const int zo = z / p.zdiv, zi = z - zo * p.zdiv;
@@ -69,16 +83,21 @@ __global__ void __launch_bounds__(64 * GNW, 1) gemm_big_kernel(GemmParams p) {
   const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
   const int nst = p.K / GBK;
 
-  // copy sources: copy j of wave w covers rows 16 (4 w + j) + lane / 4, physical chunk
-  // lane % 4, which holds logical chunk (lane % 4) ^ ((row >> 2) & 3)
-  const bf16* asrc[G_CPW];
-  const bf16* wsrc[G_CPW];
+  // copy sources: copy j of wave w covers rows 16 (CPW w + j) + lane / 4 of its operand,
+  // physical chunk lane % 4, which holds logical chunk (lane % 4) ^ ((row >> 2) & 3)
+  const bf16* asrc[C::A_CPW];
+  const bf16* wsrc[C::W_CPW];
 #pragma unroll
-  for (int j = 0; j < G_CPW; ++j) {
-    const int t = 16 * (G_CPW * wave + j) + lane / 4;
+  for (int j = 0; j < C::A_CPW; ++j) {
+    const int t = 16 * (C::A_CPW * wave + j) + lane / 4;
     const int c = (lane & 3) ^ ((t >> 2) & 3);
     const int m = min(m0 + t, p.M - 1);
     asrc[j] = reinterpret_cast<const bf16*>(p.a) + big_a_row(p, m) * p.a_ld + a_goff + 8 * c;
+  }
+#pragma unroll
+  for (int j = 0; j < C::W_CPW; ++j) {
+    const int t = 16 * (C::W_CPW * wave + j) + lane / 4;
+    const int c = (lane & 3) ^ ((t >> 2) & 3);
     const int n = min(n0 + t, N - 1);
     const int s = (n < p.seg[0].n) ? 0 : 1;
     const int nn = n - (s ? p.seg[0].n : 0);
@@ -86,14 +105,14 @@ __global__ void __launch_bounds__(64 * GNW, 1) gemm_big_kernel(GemmParams p) {
   }
   const uint32_t lds0 = lds_addr_of(smem);
   auto issue = [&](int st) {
-    const uint32_t base = lds0 + (st % GNST) * G_STAGE;
+    const uint32_t base = lds0 + (st % GNST) * C::STAGE;
     const int k0 = st * GBK;
 #pragma unroll
-    for (int j = 0; j < G_CPW; ++j)
-      dma16(asrc[j] + k0, __builtin_amdgcn_readfirstlane(base + (G_CPW * wave + j) * 1024));
+    for (int j = 0; j < C::A_CPW; ++j)
+      dma16(asrc[j] + k0, __builtin_amdgcn_readfirstlane(base + (C::A_CPW * wave + j) * 1024));
 #pragma unroll
-    for (int j = 0; j < G_CPW; ++j)
-      dma16(wsrc[j] + k0, __builtin_amdgcn_readfirstlane(base + G_AB + (G_CPW * wave + j) * 1024));
+    for (int j = 0; j < C::W_CPW; ++j)
+      dma16(wsrc[j] + k0, __builtin_amdgcn_readfirstlane(base + G_AB + (C::W_CPW * wave + j) * 1024));
   };
 
   // operand read: row r (= 32 blk + col within the wave's block), logical chunk 2 ks + half;
@@ -111,12 +130,12 @@ __global__ void __launch_bounds__(64 * GNW, 1) gemm_big_kernel(GemmParams p) {
     if (st < nst) issue(st);
   for (int it = 0; it < nst; ++it) {
     const int left = nst - 1 - it;
-    if (left >= 2) wait_vmcnt<2 * 2 * G_CPW>();
-    else if (left >= 1) wait_vmcnt<2 * G_CPW>();
+    if (GNST >= 4 && left >= 2) wait_vmcnt<2 * C::DPW>();
+    else if (left >= 1) wait_vmcnt<C::DPW>();
     else wait_vmcnt<0>();
     barrier_only();
     if (it + GNST - 1 < nst) issue(it + GNST - 1);
-    const unsigned char* T = smem + (it % GNST) * G_STAGE;
+    const unsigned char* T = smem + (it % GNST) * C::STAGE;
     const int rb0 = opaque_int(rd_base);
     Frag<bf16> fa[2][2], fb[2][4];
 #pragma unroll
@@ -306,11 +325,18 @@ hipError_t launch_gemm_big(const GemmParams& pin, int groups, hipStream_t s) {
   GemmParams p = pin;
   p.fast_epilogue = gemm_fast_epilogue_ok(p, groups) ? (kv_direct_ok(p) ? 2 : 1) : 0;
   const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
-  dim3 grid(cdiv(N, GBN), cdiv(p.M, GBM), groups);
-  if (p.fast_epilogue == 2)
-    hipLaunchKernelGGL(gemm_big_kernel<true>, grid, dim3(64 * GNW), G_LDS, s, p);
-  else
-    hipLaunchKernelGGL(gemm_big_kernel<false>, grid, dim3(64 * GNW), G_LDS, s, p);
+  // The flash-layout stage (the prefill K/V up-projection) takes 256 x 128 tiles, two
+  // workgroups per CU (820 -> 780 us at B=4, S=4096); the other projections measured the
+  // same or slower that way and keep 256 x 256.
+  if (p.fast_epilogue == 2) {
+    using C = BigCfg<4>;
+    dim3 grid(cdiv(N, C::BN), cdiv(p.M, GBM), groups);
+    hipLaunchKernelGGL((gemm_big_kernel<true, 4>), grid, dim3(64 * 4), C::LDS, s, p);
+  } else {
+    using C = BigCfg<8>;
+    dim3 grid(cdiv(N, C::BN), cdiv(p.M, GBM), groups);
+    hipLaunchKernelGGL((gemm_big_kernel<false, 8>), grid, dim3(64 * 8), C::LDS, s, p);
+  }
   return hipGetLastError();
 }
 
