@@ -210,8 +210,13 @@ hipError_t launch_tile(const GemmParams& p, int groups, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream_t s) {
-  int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  int N = seg_total(p);
   if (p.M <= 0 || N <= 0 || groups <= 0) return hipSuccess;
+  // three output segments: the few-row path only (the other kernels index two)
+  if (p.nseg > 2) {
+    if (use_bf16 && !kmajor_small_supported(p, groups) && skinny_supported(p, groups)) return launch_skinny(p, groups, s);
+    return hipErrorInvalidValue;
+  }
   int max_rope_d = 0;
   for (int i = 0; i < p.nseg; ++i)
     if (p.seg[i].rope == ROPE_HALFSPLIT && p.seg[i].rope_d > max_rope_d) max_rope_d = p.seg[i].rope_d;

@@ -19,8 +19,9 @@ template <typename T>
 __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float* Cs, int ldc, int m0,
                                                int rows, int n0, int cols, long long o_goff,
                                                int tid, int nthreads) {
-  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
-  const bool any_t = p.seg[0].layout == OUT_HEAD_T16 || (p.nseg > 1 && p.seg[1].layout == OUT_HEAD_T16);
+  const int N = seg_total(p);
+  bool any_t = false;
+  for (int i = 0; i < p.nseg; ++i) any_t = any_t || p.seg[i].layout == OUT_HEAD_T16;
   // pass 0: row-major sweep (stores contiguous along columns); pass 1: column-major sweep
   // for transposed segments (stores contiguous along tokens)
   for (int pass = 0; pass < (any_t ? 2 : 1); ++pass) {
@@ -35,10 +36,10 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
       }
       const int m = m0 + r, n = n0 + c;
       if (m >= p.M || n >= N) continue;
-      const int s = (n < p.seg[0].n) ? 0 : 1;
+      int nn;
+      const int s = seg_of(p, n, &nn);
       const GemmSeg& sg = p.seg[s];
       if ((sg.layout == OUT_HEAD_T16) != (pass == 1)) continue;
-      const int nn = n - (s ? p.seg[0].n : 0);
       float v = Cs[r * ldc + c];
       const int b = m / p.rows_per_batch;
       const int t = m - b * p.rows_per_batch;
@@ -103,14 +104,14 @@ namespace mla {
 template <typename T>
 __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const float* Cs, int ldc, int m0,
                                                     int rows, int n0, int cols, long long o_goff, int lane) {
-  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int N = seg_total(p);
   for (int cr = lane & 15; cr < cols / 8; cr += 16) {
     const int n = n0 + 8 * cr;
     if (n >= N) continue;
-    const int s = (n < p.seg[0].n) ? 0 : 1;
+    int nn;
+    const int s = seg_of(p, n, &nn);
     const GemmSeg& sg = p.seg[s];
     if (sg.layout == OUT_HEAD_T16) continue;
-    const int nn = n - (s ? p.seg[0].n : 0);
     const long long cc = nn + o_goff;
     const int hw = sg.out_hw;
     const long long head = hw ? cc / hw : 0, j0 = hw ? cc - head * hw : cc;
@@ -184,10 +185,11 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
     for (int c = lane >> 2; c < cols; c += 16) {
       const int n = n0 + c;
       if (n >= N) continue;
-      const int s = (n < p.seg[0].n) ? 0 : 1;
+      int nn;
+      const int s = seg_of(p, n, &nn);
       const GemmSeg& sg = p.seg[s];
       if (sg.layout != OUT_HEAD_T16) continue;
-      const long long cc = n - (s ? p.seg[0].n : 0) + o_goff;
+      const long long cc = nn + o_goff;
       const long long head = cc / sg.out_hw, j = cc - head * sg.out_hw;
       const long long idx = (((long long)b * sg.out_nh + head) * sg.out_hw + j) * sg.out_ld + t0 + 8 * seg;
       bf16x8 o;

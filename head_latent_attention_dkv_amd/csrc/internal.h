@@ -53,6 +53,8 @@ __host__ __device__ inline int perm16(int t) {
   return (t & ~15) | (((q == 1) ? 2 : (q == 2) ? 1 : q) << 2) | (t & 3);
 }
 
+constexpr int kMaxSeg = 3;   // output segments of one product (three only on the few-row path)
+
 struct GemmParams {
   const void* a;            // A base
   long long a_ld;           // elements between A rows
@@ -63,7 +65,7 @@ struct GemmParams {
   int rows_per_batch;       // t = m % rows_per_batch, b = m / rows_per_batch
   const int* pos0;          // per-batch first position (NULL = 0); RoPE angle uses pos0[b] + t
   int nseg;
-  GemmSeg seg[2];
+  GemmSeg seg[kMaxSeg];
   // grouped launch (blockIdx.z = group): offsets in elements, g = (z / zdiv, z % zdiv)
   int zdiv;
   long long a_goff[2];      // added to A's column start
@@ -78,6 +80,18 @@ struct GemmParams {
   int splits, kchunk;
   int fast_epilogue;        // set by the launcher: 0 generic, 1 vectorised, 2 flash layouts direct
 };
+
+// Output columns of all segments, and the segment holding output column n (*nn: its column
+// inside that segment); segments are laid side by side in order.
+__host__ __device__ inline int seg_total(const GemmParams& p) {
+  return p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0) + (p.nseg > 2 ? p.seg[2].n : 0);
+}
+__host__ __device__ inline int seg_of(const GemmParams& p, int n, int* nn) {
+  const int e0 = p.seg[0].n, e1 = e0 + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int s = n < e0 ? 0 : (n < e1 || p.nseg < 3) ? 1 : 2;
+  *nn = n - (s == 0 ? 0 : s == 1 ? e0 : e1);
+  return s;
+}
 
 hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream_t s);
 

@@ -139,6 +139,7 @@ size_t decode_gemm_split_bytes(const mla_dims* d, int B) {
   size_t m = 0;
   auto take = [&](size_t v) { m = v > m ? v : m; };
   if (dec && d->r_q > 0) take(skinny_ws_bytes(B, d->r_q, d->d_model, 1));
+  if (dec && d->r_q > 0) take(skinny_ws_bytes(B, d->r_q + d->r_kv + d->d_rope, d->d_model, 1));
   take(skinny_ws_bytes(B, H * d->d_nope + (dec ? H * d->d_rope : 0), src_w, 1));
   take(skinny_ws_bytes(B, d->r_kv + d->d_rope, d->d_model, 1));
   take(skinny_ws_bytes(B, d->d_v, rblock(d), H));
@@ -287,7 +288,7 @@ hipError_t run_latent(const mla_dims* d, const mla_weights* w, const void* x, in
 // Queries q[rows][H][d_nope + d_rope] from x (and the query latent when r_q > 0).
 hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, int rows,
                        int rows_per_batch, const int32_t* pos0, void* cq, void* q, hipStream_t st,
-                       const SplitWs& sw = SplitWs()) {
+                       const SplitWs& sw = SplitWs(), bool cq_ready = false) {
   const bool bf = is_bf16(d);
   const int H = d->n_heads, dq = dq_of(d);
   const size_t es = esize(d);
@@ -296,15 +297,17 @@ hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, i
   int src_w = d->d_model;
   hipError_t e;
   if (dec && d->r_q > 0) {
-    GemmParams p = gemm_base(d);
-    use_split(p, sw);
-    p.a = x;
-    p.a_ld = d->d_model;
-    p.M = rows;
-    p.K = d->d_model;
-    p.seg[0] = plain_seg(w->w_dq, d->d_model, d->r_q, cq, d->r_q, false);
-    e = launch_gemm(p, 1, bf, st);
-    if (e != hipSuccess) return e;
+    if (!cq_ready) {
+      GemmParams p = gemm_base(d);
+      use_split(p, sw);
+      p.a = x;
+      p.a_ld = d->d_model;
+      p.M = rows;
+      p.K = d->d_model;
+      p.seg[0] = plain_seg(w->w_dq, d->d_model, d->r_q, cq, d->r_q, false);
+      e = launch_gemm(p, 1, bf, st);
+      if (e != hipSuccess) return e;
+    }
     src = cq;
     src_w = d->r_q;
   }
@@ -335,6 +338,38 @@ hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, i
     make_rope_table(&p.rope, d->d_rope, d->rope_base);
   }
   return launch_gemm(p, 1, bf, st);
+}
+
+// Decode step, query latent present: the three products of the new tokens x -- c_Q = W_DQ x,
+// c = W_DKV x and k_R = RoPE(W_KR x) -- as one few-row product with three output segments
+// (one launch, one split-K reduce; the latent rows go to cache rows (b, pos0[b])).  Returns
+// false, launching nothing, when the shape does not take that path.
+bool run_down_proj(const mla_dims* d, const mla_weights* w, const void* x, int B, const int32_t* pos0,
+                   const mla_cache* cache, void* cq, hipStream_t st, const SplitWs& sw, hipError_t* err) {
+  if (!is_bf16(d) || d->rope_mode != MLA_ROPE_DECOUPLED_INTERLEAVED || d->r_q <= 0 || d->d_rope <= 0 ||
+      B > 128)
+    return false;
+  GemmParams p = gemm_base(d);
+  use_split(p, sw);
+  p.a = x;
+  p.a_ld = d->d_model;
+  p.M = B;
+  p.K = d->d_model;
+  p.rows_per_batch = 1;
+  p.pos0 = pos0;
+  p.out_bstride = cache->max_seq;
+  p.nseg = 3;
+  p.seg[0] = plain_seg(w->w_dq, d->d_model, d->r_q, cq, d->r_q, false);
+  p.seg[1] = plain_seg(w->w_dkv, d->d_model, d->r_kv, cache->ckv, d->r_kv, false);
+  p.seg[1].out_cache = 1;
+  p.seg[2] = plain_seg(w->w_kr, d->d_model, d->d_rope, cache->kr, d->d_rope, false);
+  p.seg[2].out_cache = 1;
+  p.seg[2].rope = ROPE_INTERLEAVED;
+  p.seg[2].rope_d = d->d_rope;
+  make_rope_table(&p.rope, d->d_rope, d->rope_base);
+  if (!skinny_supported(p, 1)) return false;
+  *err = launch_gemm(p, 1, true, st);
+  return true;
 }
 
 // Explicit keys / values from the latent rows 0..S-1 of each sequence.
@@ -754,12 +789,17 @@ mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, in
   sw.part = reinterpret_cast<float*>(at(ws, lay.gsplit));
   sw.bytes = lay.gsplit_bytes;
   void* q = at(ws, lay.q);
-  // 1. queries of the new tokens, rotated at position ctx_len[b]
-  e = run_queries(d, w, x, B, 1, ctx_len_dev, at(ws, lay.cq), q, st, sw);
+  // 1. the query latent and the new latent / rotary key (appended at row ctx_len[b]) in one
+  //    product where the shape allows, then the queries rotated at position ctx_len[b]
+  const bool merged = run_down_proj(d, w, x, B, ctx_len_dev, cache, at(ws, lay.cq), st, sw, &e);
+  if (merged && e != hipSuccess) return MLA_ERR_HIP;
+  e = run_queries(d, w, x, B, 1, ctx_len_dev, at(ws, lay.cq), q, st, sw, merged);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  // 2. append the new latent / rotary key at row ctx_len[b]
-  e = run_latent(d, w, x, B, 1, ctx_len_dev, cache, nullptr, nullptr, st, sw);
-  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 2. otherwise append the new latent / rotary key at row ctx_len[b] here
+  if (!merged) {
+    e = run_latent(d, w, x, B, 1, ctx_len_dev, cache, nullptr, nullptr, st, sw);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
   // 3. absorbed query q_lat[b][h] = W_UK,h^T q_C[b][h]
   void* qlat = at(ws, lay.qlat);
   e = run_per_head(d, q, (long long)H * dq, dq, d->d_nope, w->w_uk, true, rb, qlat,

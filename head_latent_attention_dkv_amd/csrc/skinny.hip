@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
   const int split = blockIdx.y;
   const int z = blockIdx.z;
   const Goff g = group_offsets(p, z);
-  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int N = seg_total(p);
   const int k_begin = split * p.kchunk;
   const int k_end = min(p.K, k_begin + p.kchunk);
 
@@ -61,8 +61,8 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int n = min(n0 + 32 * rb + col, N - 1);
-    const int s = (n < p.seg[0].n) ? 0 : 1;
-    const int nn = n - (s ? p.seg[0].n : 0);
+    int nn;
+    const int s = seg_of(p, n, &nn);
     wrow[rb] = reinterpret_cast<const bf16*>(p.seg[s].w) + g.w + (long long)nn * p.seg[s].w_ld + 8 * half;
   }
   // lane -> A row 32 cb + col (clamped likewise)
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_k
   const int split = blockIdx.y;
   const int z = blockIdx.z;
   const Goff g = group_offsets(p, z);
-  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int N = seg_total(p);
   const int k_begin = split * p.kchunk;
   const int nst = (min(p.K, k_begin + p.kchunk) - k_begin) / KT;   // stages of this slab
   const uint32_t lds0 = lds_addr_of(smem);
@@ -213,8 +213,8 @@ __global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_k
   for (int i = 0; i < C::WPW; ++i) {
     const int t = (wave * C::WPW + i) * C::RPC + lane / C::CHUNKS;
     const int n = min(n0 + t, N - 1);
-    const int s = (n < p.seg[0].n) ? 0 : 1;
-    const int nn = n - (s ? p.seg[0].n : 0);
+    int nn;
+    const int s = seg_of(p, n, &nn);
     wsrc[i] = reinterpret_cast<const bf16*>(p.seg[s].w) + g.w + (long long)nn * p.seg[s].w_ld + k_begin +
               8 * (pc ^ (t % C::CHUNKS));
   }
@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(GemmParams p) {
   const int m0 = blockIdx.y * kRedRows;
   const int z = blockIdx.z;
   const Goff g = group_offsets(p, z);
-  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int N = seg_total(p);
   const long long plane = (long long)p.M * N;
   const int r = tid / kCols, c = tid - r * kCols;
   float v = 0.f;
@@ -439,7 +439,7 @@ SkinnyPlan plan(int M, int N, int K, int groups) {
 template <int CB, int ROWS, int NST = ROWS == 128 ? 3 : 4>
 hipError_t launch_stream(const GemmParams& p, int groups, hipStream_t s) {
   using C = StreamCfg<CB, ROWS, kStreamKT, NST>;
-  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int N = seg_total(p);
   dim3 grid(cdiv(N, ROWS), p.splits, groups);
   hipLaunchKernelGGL((skinny_stream_kernel<CB, ROWS, kStreamKT, NST>), grid, dim3(256), C::LDS, s, p);
   return hipGetLastError();
@@ -483,7 +483,7 @@ bool skinny_supported(const GemmParams& p, int groups) {
 }
 
 hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s) {
-  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int N = seg_total(p);
   SkinnyPlan pl = plan(p.M, N, p.K, groups);
   const size_t need = pl.splits > 1 ? (size_t)pl.splits * groups * p.M * N * sizeof(float) : 0;
   if (pl.splits > 1 && (p.part == nullptr || p.part_bytes < need)) {
