@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
   const int ht = blockIdx.y - g * p.head_tiles;
   const int b = blockIdx.z;
 
-  const int n_tok = p.ctx_len[b] + 1;
+  const int n_tok = decode_tokens(p, b);
   const int tok_begin = split * p.chunk;
   if (tok_begin >= n_tok) return;
   const int tok_end = min(n_tok, tok_begin + p.chunk);
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   constexpr int CPT = DL >= 64 ? DL / 64 : 1;
   const int head = blockIdx.x;
   const int b = blockIdx.y;
-  const int n_tok = p.ctx_len[b] + 1;
+  const int n_tok = decode_tokens(p, b);
   const int ns = (n_tok + p.chunk - 1) / p.chunk;
   const long long base = ((long long)b * p.H + head) * p.nsplit;
   float M = -INFINITY;
@@ -323,7 +323,7 @@ __global__ void __launch_bounds__(64 * (DV / 32)) combine_uv_kernel(DecodeParams
   {
     const int sl = threadIdx.x >> 3, j = threadIdx.x & 7;
     const int b = b0 + sl;
-    const int ns = b < p.B ? (p.ctx_len[b] + 1 + p.chunk - 1) / p.chunk : 0;
+    const int ns = b < p.B ? (decode_tokens(p, b) + p.chunk - 1) / p.chunk : 0;
     const long long base = ((long long)min(b, p.B - 1) * p.H + h) * p.nsplit;
     float mx = -INFINITY;
     for (int s = j; s < ns; s += 8) mx = fmaxf(mx, p.part_ml[(base + s) * 2]);

@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   const int ht = blockIdx.y;
   const int b = blockIdx.z;
 
-  const int n_tok = p.ctx_len[b] + 1;
+  const int n_tok = decode_tokens(p, b);
   const int tok_begin = split * p.chunk;
   if (tok_begin >= n_tok) return;
   const int tok_end = min(n_tok, tok_begin + p.chunk);
@@ -327,7 +327,7 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
   const int pair = blockIdx.x / p.head_tiles;
   const int b = pair / p.nsplit;
   const int split = pair - b * p.nsplit;
-  const int n_tok = p.ctx_len[b] + 1;
+  const int n_tok = decode_tokens(p, b);
   const int tok_begin = split * p.chunk;
   if (tok_begin >= n_tok) return;
   const int tok_end = min(n_tok, tok_begin + p.chunk);

@@ -133,6 +133,15 @@ struct DecodeParams {
   void* z;                  // [B][H][rb] output
 };
 
+// Keys of sequence b: ctx_len[b] + 1, clamped to what the cache rows and the splits hold
+// (callers keep ctx_len[b] <= max_ctx; the clamp only keeps a bad value from reading past
+// the cache or the split partials).
+__device__ inline int decode_tokens(const DecodeParams& p, int b) {
+  const long long n = (long long)p.ctx_len[b] + 1;
+  const long long cap = min((long long)p.cache_bstride, (long long)p.nsplit * p.chunk);
+  return (int)(n < 1 ? 1 : (n > cap ? cap : n));
+}
+
 hipError_t launch_decode(const DecodeParams& p, bool use_bf16, int dl_pad, int dr_pad, int nw,
                          hipStream_t s);
 bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, int* dr_pad, int* nw);
