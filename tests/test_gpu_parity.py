@@ -165,6 +165,9 @@ def test_prefill_chunk_capacity(gu):
 # ---------------------------------------------------------------------------
 DECODE_CASES = [
     (DSV2, [37, 300, 1000]),          # one, several and many 32-token tiles; several splits
+    # 37 sequences: the fused combine's second group of 32 holds 5, the merged down-projection
+    # runs on 37 rows; short ragged contexts keep the oracle quick
+    (DSV2, [int(c) for c in np.random.default_rng(37).integers(0, 70, size=37)]),
     (MLRA, [5, 100, 700, 1500]),      # ragged, 4 latent heads
     (TINY_BF16_MLRA, [0, 39]),        # empty context (attends to itself only)
     (TINY.replace(mode="decode"), [0, 7]),
