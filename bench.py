@@ -356,10 +356,11 @@ def summarize_profiles(d):
         return vals
 
     def unit_kib(sub, counter):
-        v = per_dispatch(sub, counter, lambda n: "decode_h128_kernel" in n or "combine_kernel" in n)
+        v = per_dispatch(sub, counter, lambda n: "decode_h128_kernel" in n or "combine_kernel" in n
+                         or "combine_uv_kernel" in n)
         by = {}
         for (name, _), x in v.items():
-            by.setdefault("combine" if "combine_kernel" in name else "split", []).append(x)
+            by.setdefault("combine" if "combine" in name else "split", []).append(x)
         return {k: float(np.median(x)) for k, x in by.items()}
 
     def copy_kib(sub, counter):
@@ -390,9 +391,9 @@ def summarize_profiles(d):
         name = name.replace("mla::(anonymous namespace)::", "").replace("(mla::GemmParams)", "")
         name = name.replace("(mla::DecodeParams)", "").replace("void ", "")
         if name.startswith("_ZN3mla"):
-            m = re.match(r"_ZN3mla12_GLOBAL__N_114combine_kernelIDF16bLi(\d+)ELb([01])E", name)
+            m = re.match(r"_ZN3mla12_GLOBAL__N_114combine_kernelI(DF16b|f)Li(\d+)E", name)
             if m:
-                return f"combine_kernel<bf16,{m.group(1)}{',bf16 partials' if m.group(2) == '1' else ''}>"
+                return f"combine_kernel<{'bf16' if m.group(1) == 'DF16b' else 'float'},{m.group(2)}>"
             name = {"_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi64ELi64EEEvNS_10GemmParamsE": "gemm_kernel<bf16,64,64>",
                     "_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi128ELi128EEEvNS_10GemmParamsE":
                         "gemm_kernel<bf16,128,128>"}.get(name, name)
@@ -429,7 +430,7 @@ def summarize_profiles(d):
                 j += 1
             return j
 
-        combines = [i for i, n in enumerate(names) if n.startswith("combine_uv_kernel")]
+        combines = [i for i, n in enumerate(names) if n.startswith("combine_uv_kernel") and "false" not in n]
         ends = [step_end(c) for c in combines if c + 1 < len(names) and names[c + 1].startswith("skinny")]
         step = (ends[-2] + 1, ends[-1]) if len(ends) >= 2 else None
         if step:

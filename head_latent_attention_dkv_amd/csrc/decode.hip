@@ -221,10 +221,10 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 }
 
 // z[b][h] = sum_s 2^(m_s - M) z_s / sum_s 2^(m_s - M) l_s over the splits of sequence b
-// (PB: the splits stored y_s = z_s / l_s in bf16, so z_s = l_s y_s).  One 64-lane workgroup per (head, sequence); lane c owns CPT consecutive columns (vector
+// (fp32 split results; the bf16 ones of the 128-head kernel go to combine_uv_kernel).  One 64-lane workgroup per (head, sequence); lane c owns CPT consecutive columns (vector
 // loads), the split weights are formed once per split, and the split loop is unrolled so
 // that several partial rows are in flight at once.
-template <typename T, int DL, bool PB>
+template <typename T, int DL>
 __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   constexpr int CPT = DL >= 64 ? DL / 64 : 1;
   const int head = blockIdx.x;
@@ -242,24 +242,12 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   float a[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) a[j] = 0.f;
-  // PB: split s holds z_s / l_s in bf16 and weighs l_s 2^(m_s - M); otherwise z_s in fp32
-  // with weight 2^(m_s - M)
   const float* zs = p.part_z + base * DL + c0;
-  const bf16* ys = reinterpret_cast<const bf16*>(p.part_z) + base * DL + c0;
 #pragma unroll 4
   for (int s = 0; s < ns; ++s) {
-    float w = exp2f(p.part_ml[(base + s) * 2] - M);
+    const float w = exp2f(p.part_ml[(base + s) * 2] - M);
     float v[CPT];
-    if constexpr (PB) {
-      static_assert(CPT % 8 == 0, "16-byte partial loads");
-      w *= p.part_ml[(base + s) * 2 + 1];
-#pragma unroll
-      for (int j = 0; j < CPT; j += 8) {
-        const bf16x8 y = *reinterpret_cast<const bf16x8*>(ys + (long long)s * DL + j);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[j + e] = (float)y[e];
-      }
-    } else if constexpr (CPT % 4 == 0) {
+    if constexpr (CPT % 4 == 0) {
 #pragma unroll
       for (int j = 0; j < CPT; j += 4) *reinterpret_cast<f32x4*>(v + j) = *reinterpret_cast<const f32x4*>(zs + (long long)s * DL + j);
     } else {
@@ -275,9 +263,9 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
     if (c0 + j < p.rb) z[j] = from_f32<T>(a[j] * inv);
 }
 
-template <typename T, int DL, bool PB = false>
+template <typename T, int DL>
 hipError_t launch_combine_impl(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<T, DL, PB>), dim3(p.H, p.B), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((combine_kernel<T, DL>), dim3(p.H, p.B), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -300,20 +288,24 @@ hipError_t launch_impl(const DecodeParams& p, hipStream_t s) {
 //      32x32x16 MFMAs, A straight from global memory, B from LDS.  The contraction index is
 //      relabelled (k-step ks, lane half hk <-> latent columns 256 hk + 8 ks ..) identically on
 //      both operands, so every lane reads one contiguous 512-byte run of its weight row.
-template <int DV>
+// UV = false: the combine alone (mla_decode_attention), z[b][h] written to p.z; the same
+// workgroup shape, so that a wave has the partial rows of four sequences in flight at once.
+template <int DV, bool UV = true>
 __global__ void __launch_bounds__(64 * (DV / 32)) combine_uv_kernel(DecodeParams p, const bf16* __restrict__ w_uv,
                                                                     bf16* __restrict__ o) {
   constexpr int DL = 512, SEQ = 32, NWV = DV / 32, SPW = SEQ / NWV, LDZ = DL + 8, MAXS = 4;
-  __shared__ __attribute__((aligned(16))) bf16 zs[SEQ * LDZ];
+  __shared__ __attribute__((aligned(16))) bf16 zs[UV ? SEQ * LDZ : 8];
   const int h = blockIdx.x, b0 = blockIdx.y * SEQ;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bf16* part = reinterpret_cast<const bf16*>(p.part_z);
   // this wave's W_UV,h rows go out first; their latency overlaps the combine
   const int col = lane & 31, hk = lane >> 5;
-  const bf16* wrow = w_uv + ((long long)h * DV + 32 * wave + col) * DL + 256 * hk;
-  bf16x8 af[32];
+  bf16x8 af[UV ? 32 : 1];
+  if constexpr (UV) {
+    const bf16* wrow = w_uv + ((long long)h * DV + 32 * wave + col) * DL + 256 * hk;
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(wrow + 8 * ks);
+    for (int ks = 0; ks < 32; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(wrow + 8 * ks);
+  }
 
   // 1. combine.  Split weights first: thread (sequence t/8, lane t%8) scans splits t%8,
   // t%8 + 8, ..; the eight lanes of a sequence meet through lane shuffles.
@@ -389,9 +381,15 @@ __global__ void __launch_bounds__(64 * (DV / 32)) combine_uv_kernel(DecodeParams
       bf16x8 zz;
 #pragma unroll
       for (int e = 0; e < 8; ++e) zz[e] = (bf16)a[i][e];
-      *reinterpret_cast<bf16x8*>(zs + (wave * SPW + hh * SH + i) * LDZ + 8 * lane) = zz;
+      if constexpr (UV) {
+        *reinterpret_cast<bf16x8*>(zs + (wave * SPW + hh * SH + i) * LDZ + 8 * lane) = zz;
+      } else {
+        const int b = b0 + wave * SPW + hh * SH + i;
+        if (b < p.B) *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(p.z) + ((long long)b * p.H + h) * DL + 8 * lane) = zz;
+      }
     }
   }
+  if constexpr (!UV) return;
   __syncthreads();
 
   // 2. O^T = W_UV,h . Z^T
@@ -432,8 +430,12 @@ bool decode_supported(bool use_bf16, int rb, int d_rope, int hpb, int* dl_pad, i
 
 hipError_t launch_combine(const DecodeParams& p, bool use_bf16, int dl, hipStream_t s) {
   if (use_bf16) {
-    if (dl == 512 && p.part_bf16) return launch_combine_impl<bf16, 512, true>(p, s);
-    if (p.part_bf16) return hipErrorInvalidValue;
+    if (p.part_bf16) {                     // bf16 split results: latent 512 only
+      if (dl != 512 || p.rb != 512) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((combine_uv_kernel<128, false>), dim3(p.H, (p.B + 31) / 32), dim3(256), 0, s, p,
+                         nullptr, nullptr);
+      return hipGetLastError();
+    }
     if (dl == 512) return launch_combine_impl<bf16, 512>(p, s);
     if (dl == 128) return launch_combine_impl<bf16, 128>(p, s);
   } else {
