@@ -443,15 +443,16 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
     // (an empty asm reading one element of every fourth product of a chain keeps the pure
     // MFMAs in their steps: without it the products sink to their first use and every
-    // operand read stays live at once)
+    // operand read stays live at once.  It names the element as an accumulation register,
+    // where the product leaves it: a VGPR operand cost a copy and a hazard wait each time.)
     auto sstep = [&](auto n_c) {
       constexpr int n = decltype(n_c)::value;
       if constexpr (n % 2 == 0) {
         mma32_acc(sa, sring[n % (SPF + 1)], qf[n].v);
-        if constexpr (n % 8 == 6) asm volatile("" ::"v"(sa[0]));
+        if constexpr (n % 8 == 6) asm volatile("" ::"a"(sa[0]));
       } else {
         mma32_acc(sc, sring[n % (SPF + 1)], qf[n].v);
-        if constexpr (n % 8 == 7) asm volatile("" ::"v"(sc[0]));
+        if constexpr (n % 8 == 7) asm volatile("" ::"a"(sc[0]));
       }
       if constexpr (n + SPF < KS) sring[(n + SPF) % (SPF + 1)] = sread(n + SPF);
       __builtin_amdgcn_sched_barrier(0);
