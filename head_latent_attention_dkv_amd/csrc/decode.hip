@@ -230,7 +230,7 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeParams p) {
   const int head = blockIdx.x;
   const int b = blockIdx.y;
   const int n_tok = decode_tokens(p, b);
-  const int ns = (n_tok + p.chunk - 1) / p.chunk;
+  const int ns = p.sub * ((n_tok + p.chunk - 1) / p.chunk);   // partial rows written for b
   const long long base = ((long long)b * p.H + head) * p.nsplit;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[(base + s) * 2]);
@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(64 * (DV / 32)) combine_uv_kernel(DecodeParams
   {
     const int sl = threadIdx.x >> 3, j = threadIdx.x & 7;
     const int b = b0 + sl;
-    const int ns = b < p.B ? (decode_tokens(p, b) + p.chunk - 1) / p.chunk : 0;
+    const int ns = b < p.B ? p.sub * ((decode_tokens(p, b) + p.chunk - 1) / p.chunk) : 0;
     const long long base = ((long long)min(b, p.B - 1) * p.H + h) * p.nsplit;
     float mx = -INFINITY;
     for (int s = j; s < ns; s += 8) mx = fmaxf(mx, p.part_ml[(base + s) * 2]);

@@ -72,10 +72,19 @@ __device__ __forceinline__ int opaque(int x) {
 // which is exactly its slice of P^T as the B operand, so P never leaves registers.
 // Softmax against a fixed reference per head (the maximum of its first tile), with the
 // overflow test on the row sums and the rare exact-maximum re-stream of decode_h128_kernel.
-template <int VL, int VR, int NW, int NSTAGE>
+//
+// TSPLIT (one latent block of rank 128 per token, e.g. one latent head of MLRA on its own):
+// the four waves take different tokens instead of different latent blocks.  A tile is 128
+// tokens of 256 B; LDS row t of a stage holds tokens t, 32 + t, 64 + t, 96 + t in its four
+// 256-byte quarters, so wave w's quarter-row reads (the same code as above) are its own 32
+// tokens.  Each wave keeps its own softmax state and writes its own partial row (sub-split
+// w of the split); the combine merges the 4 x splits rows like any others.
+template <int VL, int VR, int NW, int NSTAGE, bool TSPLIT = false>
 __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   using C = FastCfg<VL, VR, NW, NSTAGE>;
   static_assert(VR == 0, "latent blocks without a rotary key (the copies below move latent rows only)");
+  static_assert(!TSPLIT || (VL == 128 && NW == 4), "token split: rank-128 rows, four waves");
+  constexpr int TOK = TSPLIT ? 4 * TT : TT;            // tokens per tile
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   int* const vote = reinterpret_cast<int*>(smem_raw + C::LDS);
 
@@ -91,11 +100,14 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   const int tok_begin = split * p.chunk;
   if (tok_begin >= n_tok) return;
   const int tok_end = min(n_tok, tok_begin + p.chunk);
-  const int ntiles = (tok_end - tok_begin + TT - 1) / TT;
+  const int ntiles = (tok_end - tok_begin + TOK - 1) / TOK;
 
   // wave -> (latent block, heads, latent view)
   int g, hloc;
-  if (p.L == 1) {
+  if (TSPLIT) {
+    g = 0;
+    hloc = ht * 16 + hl;
+  } else if (p.L == 1) {
     g = 0;
     hloc = ht * (16 * NW) + wave * 16 + hl;
   } else {
@@ -104,7 +116,8 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   }
   const bool head_ok = hloc < p.hpb;
   const int head = g * p.hpb + hloc;
-  const int vc0 = (p.L == 1) ? 0 : g * (VL / 8);       // first latent chunk of the view
+  // first latent chunk of the view (TSPLIT: the quarter of each LDS row holding the wave's tokens)
+  const int vc0 = TSPLIT ? wave * 16 : (p.L == 1) ? 0 : g * (VL / 8);
 
   // ---- Q^T slice (B operand), loaded branch-free (padded heads read a valid row, then zero) ----
   const bf16* ql = reinterpret_cast<const bf16*>(p.q_lat);
@@ -129,15 +142,24 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   const unsigned char* ckv_seq = reinterpret_cast<const unsigned char*>(p.ckv) + (long long)b * p.cache_bstride * p.r_kv * 2;
   const uint32_t lds_base = lds_addr_of(smem_raw);
   auto issue_tile = [&](int tile, int stage) {
-    const int t0 = tok_begin + tile * TT;
+    const int t0 = tok_begin + tile * TOK;
     const uint32_t sbase = lds_base + stage * C::STAGE_BYTES;
-    const uint32_t ln16 = (uint32_t)opaque(lane) << 4;
+    const int ln = opaque(lane);
+    const uint32_t ln16 = (uint32_t)ln << 4;
 #pragma unroll
     for (int i = 0; i < C::RPW; ++i) {
       const int t = wave * C::RPW + i;
-      const int tok = min(t0 + t, tok_end - 1);
-      dma16_s(ckv_seq + (long long)tok * p.r_kv * 2, ln16 ^ ((uint32_t)bitrev4(t & 15) << 4),
-              __builtin_amdgcn_readfirstlane(sbase + t * 1024));
+      if constexpr (TSPLIT) {
+        // lane ln fills physical chunk ln of LDS row t: quarter ln / 16 = token 32 (ln / 16) + t
+        // of the tile, its chunk (ln ^ key) % 16 (key < 16 leaves the quarter unchanged)
+        const int tok = min(t0 + 32 * (ln >> 4) + t, tok_end - 1);
+        const uint32_t c = (uint32_t)((ln ^ bitrev4(t & 15)) & 15);
+        dma16_s(ckv_seq, (uint32_t)tok * (VL * 2) + (c << 4), __builtin_amdgcn_readfirstlane(sbase + t * 1024));
+      } else {
+        const int tok = min(t0 + t, tok_end - 1);
+        dma16_s(ckv_seq + (long long)tok * p.r_kv * 2, ln16 ^ ((uint32_t)bitrev4(t & 15) << 4),
+                __builtin_amdgcn_readfirstlane(sbase + t * 1024));
+      }
     }
   };
 
@@ -196,13 +218,14 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
         s[rb] = mma16(a, qf[ks], s[rb]);
       }
     }
-    if (t0 + TT > tok_end) {                                // ragged last tile only
+    const int tw = TSPLIT ? t0 + 32 * wave : t0;           // this wave's first token
+    if (tw + TT > tok_end) {                                // ragged last tile only
       asm volatile("; ragged tile");                        // keeps this a branch
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t0 + 16 * rb + 4 * grp + i >= tok_end) s[rb][i] = -INFINITY;
+          if (tw + 16 * rb + 4 * grp + i >= tok_end) s[rb][i] = -INFINITY;
     }
     if (MODE == 1 || first) {
       const float mt = head_max(fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
@@ -210,7 +233,8 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
       m_ref = MODE == 1 ? fmaxf(m_ref, mt) : mt;
     }
     if constexpr (MODE == 1) return;
-    const float nm = -m_ref;
+    // a token-split wave can hold no token of its split at all (m_ref = -inf): its p are 0
+    const float nm = (TSPLIT && m_ref == -INFINITY) ? 0.f : -m_ref;
     float pv[8];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -251,7 +275,7 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
       barrier_only();
       if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
       if (MODE != 0 && !redo) continue;
-      tile(smem_raw + (it % NSTAGE) * C::STAGE_BYTES, tok_begin + it * TT, MODE == 0 && it == 0, mode_c);
+      tile(smem_raw + (it % NSTAGE) * C::STAGE_BYTES, tok_begin + it * TOK, MODE == 0 && it == 0, mode_c);
     }
   };
 
@@ -280,7 +304,7 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
 
   const float l_tot = head_sum(l_run);
   if (!head_ok) return;
-  const long long pidx = ((long long)b * p.H + head) * p.nsplit + split;
+  const long long pidx = ((long long)b * p.H + head) * p.nsplit + split * p.sub + (TSPLIT ? wave : 0);
   if (grp == 0) {
     p.part_ml[pidx * 2 + 0] = m_ref;
     p.part_ml[pidx * 2 + 1] = l_tot;
@@ -587,10 +611,14 @@ bool decode_fast_supported(const DecodeParams& p, int* variant) {
     *variant = 2;
     return true;
   }
+  if (p.L == 1 && p.r_kv == 128 && p.rb == 128 && p.d_rope == 0) {
+    *variant = 5;
+    return true;
+  }
   return false;
 }
 
-int decode_fast_head_tile(int variant) { return variant == 2 ? 16 : 128; }
+int decode_fast_head_tile(int variant) { return (variant == 2 || variant == 5) ? 16 : 128; }
 
 bool decode_fast_bf16_partials(int variant) { return variant == 3 || variant == 4; }
 
@@ -615,6 +643,13 @@ hipError_t launch_decode_fast(const DecodeParams& p, int variant, hipStream_t s)
       // other's stream
       using C = FastCfg<128, 0, 4, 2>;
       hipLaunchKernelGGL((decode_fast_kernel<128, 0, 4, 2>), grid, dim3(256), C::LDS + 16, s, p);
+      break;
+    }
+    case 5: {
+      using C = FastCfg<128, 0, 4, 2>;
+      if (p.sub != 4) return hipErrorInvalidValue;
+      dim3 g5(p.nsplit / p.sub, p.head_tiles, p.B);
+      hipLaunchKernelGGL((decode_fast_kernel<128, 0, 4, 2, true>), g5, dim3(256), C::LDS + 16, s, p);
       break;
     }
     default:

@@ -124,7 +124,8 @@ struct DecodeParams {
   int B, H, L, hpb;         // hpb = H / L heads per latent block
   int r_kv, rb, d_rope;     // total latent, block width, rotary width
   int chunk;                // tokens per split (multiple of 32)
-  int nsplit;               // splits allocated per (b, head)
+  int nsplit;               // partial rows per (b, head): splits x sub
+  int sub;                  // partial rows per split (4: one per wave of the token-split kernel)
   int head_tiles;           // head tiles per latent block
   float scale_log2;         // softmax scale * log2(e)
   float* part_z;            // [B][H][nsplit][DLP]: fp32 z, or bf16 z / l when part_bf16
@@ -138,7 +139,7 @@ struct DecodeParams {
 // the cache or the split partials).
 __device__ inline int decode_tokens(const DecodeParams& p, int b) {
   const long long n = (long long)p.ctx_len[b] + 1;
-  const long long cap = min((long long)p.cache_bstride, (long long)p.nsplit * p.chunk);
+  const long long cap = min((long long)p.cache_bstride, (long long)(p.nsplit / p.sub) * p.chunk);
   return (int)(n < 1 ? 1 : (n > cap ? cap : n));
 }
 

@@ -55,6 +55,7 @@ float softmax_scale(const mla_dims* d) {
 // whole waves of 256 workgroups.
 struct SplitPlan {
   int chunk, nsplit, head_tiles, dl, dr, nw;
+  int sub = 1;        // partial rows per split (nsplit counts rows)
   int fast_variant;   // -1: generic kernel
   int fast_head_tiles;
   bool ok;
@@ -65,6 +66,7 @@ int fast_variant_for(const mla_dims* d) {
   const int L = d->n_latent_heads, hpb = d->n_heads / L;
   if (L == 1 && d->r_kv == 512 && (d->d_rope == 64 || d->d_rope == 0)) return d->d_rope ? 3 : 4;
   if (L == 4 && d->r_kv == 512 && d->d_rope == 0 && hpb <= 16) return 2;
+  if (L == 1 && d->r_kv == 128 && d->d_rope == 0) return 5;   // one rank-128 latent block
   return -1;
 }
 
@@ -78,13 +80,16 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
   const int ntok = max_ctx + 1;
   int chunk;
   if (sp.fast_variant >= 0) {
-    sp.fast_head_tiles = sp.fast_variant == 2 ? 1 : cdiv(hpb, 128);
+    sp.fast_head_tiles = sp.fast_variant == 2 ? 1 : sp.fast_variant == 5 ? cdiv(hpb, 16) : cdiv(hpb, 128);
     const long long wgs = (long long)B * sp.fast_head_tiles;
     int ns = (int)((kCUs + wgs - 1) / wgs);
     chunk = round_up(cdiv(ntok, ns < 1 ? 1 : ns), 32);
     // MLRA (latent blocks): splits of at most 1024 tokens keep ragged batches balanced over
     // the CUs while each workgroup streams long enough to amortise its start
     if (sp.fast_variant == 2 && chunk > 1024) chunk = 1024;
+    // token split (four waves on four 32-token slices of 128-token tiles): the same bytes per
+    // split as the MLRA kernel's 1024 tokens of 1 KB rows
+    if (sp.fast_variant == 5) chunk = min(round_up(chunk, 128), 4096);
   } else {
     const long long wgs = (long long)B * L * sp.head_tiles;
     const int wg_per_cu = sp.nw == 4 ? 1 : 8;
@@ -95,6 +100,10 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
   if (chunk < 32) chunk = 32;
   sp.chunk = chunk;
   sp.nsplit = cdiv(ntok, chunk);
+  if (sp.fast_variant == 5) {
+    sp.sub = 4;
+    sp.nsplit *= 4;
+  }
   return sp;
 }
 
@@ -111,8 +120,10 @@ hipError_t run_decode_attention(const mla_dims* d, DecodeParams p, const SplitPl
                     (p.d_rope == 0 || (aligned16(p.q_rope) && p.q_rope_hs % 8 == 0 && aligned16(p.kr)));
   hipError_t e;
   p.part_bf16 = 0;
+  p.sub = 1;                     // the generic kernel writes one row per split
   if (fast) {
     p.head_tiles = sp.fast_head_tiles;
+    p.sub = variant == 5 ? sp.sub : 1;
     p.part_bf16 = decode_fast_bf16_partials(variant) ? 1 : 0;
     e = launch_decode_fast(p, variant, st);
   } else {
@@ -495,6 +506,7 @@ DecodeParams decode_params(const mla_dims* d, const mla_cache* cache, const int3
   p.d_rope = d->d_rope;
   p.chunk = sp.chunk;
   p.nsplit = sp.nsplit;
+  p.sub = 1;
   p.head_tiles = sp.head_tiles;
   p.scale_log2 = softmax_scale(d) * kLog2e;
   p.part_z = reinterpret_cast<float*>(at(ws, lay.part_z));

@@ -8,6 +8,7 @@ max-abs <= 3e-2 (whole tensor).
 import numpy as np
 import pytest
 
+import latent_heads as LH
 import mla_synth as S
 from oracle import mla_oracle as O
 
@@ -227,7 +228,9 @@ def test_decode_is_deterministic(gu):
 # ---------------------------------------------------------------------------
 # Staged entry points with oracle-made inputs
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg,ctx", [(DSV2, [40, 513, 999]), (MLRA, [5, 1030])], ids=["dsv2", "mlra"])
+@pytest.mark.parametrize("cfg,ctx", [(DSV2, [40, 513, 999]), (MLRA, [5, 1030]),
+                                     (LH.block_cfg(MLRA), [0, 5, 127, 128, 129, 1030])],
+                         ids=["dsv2", "mlra", "mlra_latent_head"])
 def test_decode_attention_entry(gu, cfg, ctx):
     """mla_decode_attention on latent rows and absorbed queries made by the oracle."""
     import head_latent_attention_dkv_amd as M
@@ -409,3 +412,34 @@ def test_prefill_attention_exact_max_restream(gu):
     M.mla_prefill_attention(lay.dims, lay.ws_struct, gu.to_dev(q_h, cfg), B, S_,
                             M.cache_struct(gu.to_dev(ckv_h, cfg), gu.to_dev(kr_h, cfg), B, S_), o, ws, nbytes)
     gu.assert_close(gu.to_host(o), want, cfg.dtype, "o with far-above-reference scores")
+
+
+# ---------------------------------------------------------------------------
+# One MLRA latent head on its own (L = 1, rank 128, its H/L query heads): the token-split
+# decode kernel.  Every latent head against the oracle run on it alone, and the sum over
+# the latent heads against the oracle's whole layer (the MLRA page's partition of the
+# latent: the sum a latent-head-parallel decode would all-reduce).
+# ---------------------------------------------------------------------------
+def test_decode_latent_heads_sum(gu):
+    cfg = MLRA
+    prob = S.make_problem(cfg)
+    ctx = [5, 300, 1500, 129, 128, 0, 33]   # ragged; 128-token tile edges; empty context
+    gu.say(f"[decode latent heads] {cfg.name} ctx={ctx}")
+    B = len(ctx)
+    seqs = [S.make_x(cfg, b, ctx[b] + 1) for b in range(B)]
+    ys = []
+    for g in range(cfg.n_latent_heads):
+        pg = LH.block_problem(prob, g)
+        lay = gu.Layer(pg.cfg, pg)
+        x = gu.to_dev(np.stack([sq[-1] for sq in seqs]), pg.cfg)
+        ckv, kr = lay.new_cache(B, max(ctx) + 9, fill=SENTINEL)
+        lay.fill_cache(ckv, kr, ctx)
+        y = gu.to_host(lay.decode(x, ctx, lay.cache_view(ckv, kr, 0, B)))
+        dg = _dims(pg.cfg)
+        for b in range(B):
+            gu.assert_close(y[b], O.decode(seqs[b], pg.weights, dg), cfg.dtype, f"latent head {g} b={b}")
+        ys.append(y)
+    d = _dims(cfg)
+    ysum = np.sum(ys, axis=0)
+    for b in range(B):
+        gu.assert_close(ysum[b], O.decode(seqs[b], prob.weights, d), cfg.dtype, f"sum over latent heads b={b}")

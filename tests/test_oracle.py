@@ -482,3 +482,22 @@ def test_activations_are_independent_of_the_weights():
     x = S.make_x(cfg, 0, 2600)
     c = x @ p.weights["w_dkv"].T
     assert np.abs(c).max() < 8.0
+
+
+def test_mlra_output_is_the_sum_over_latent_heads():
+    """MLRA page: head h reads latent block h // (H/L) only, and W_O is linear in the heads'
+    outputs, so each latent head with its H/L query heads is an L = 1 layer of rank r/L and
+    the layer's output is the sum of theirs (decode of the same token, fp64)."""
+    import latent_heads as LH
+    cfg = S.CONFIGS["mlra_decode"].replace(d_model=96, n_heads=8, d_nope=16, r_kv=32, n_latent_heads=4,
+                                           batch=2, ctx_lo=0, ctx_hi=0, dtype="f32")
+    prob = S.make_problem(cfg)
+    x = S.make_x(cfg, 0, 7)
+    y = O.decode(x, prob.weights, O.Dims.from_cfg(cfg))
+    parts = []
+    for g in range(cfg.n_latent_heads):
+        pg = LH.block_problem(prob, g)
+        parts.append(O.decode(x, pg.weights, O.Dims.from_cfg(pg.cfg)))
+    np.testing.assert_allclose(np.sum(parts, axis=0), y, rtol=1e-10, atol=1e-12)
+    # and each part is a real share of the output, not the whole of it
+    assert all(np.linalg.norm(p) < 0.9 * np.linalg.norm(y) for p in parts)
