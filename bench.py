@@ -20,6 +20,8 @@ The JSON line also carries:
   * prefill -- the DeepSeek-V2-shaped causal prefill (B=4, S=4096): whole mla_prefill and
     the attention core unit mla_prefill_attention against the 2.5 PFLOP/s bf16 MFMA peak;
   * mlra_decode -- the MLRA decode (B=128, ragged contexts, 4 latent heads of rank 128);
+  * mlra_latent_head_decode -- one of those latent heads on its own (rank 128, its 4 query
+    heads, the same contexts): what one GPU of a latent-head-parallel decode runs;
   * small_lm_prefill -- the small-LM prefill (B=8, S=1024);
   * cpu_baseline -- the fp64 CPU oracle timed on the host on a bounded sample of the
     decode workload (whole sequences, ~15 s).
@@ -172,12 +174,16 @@ def traffic_from_profiles(name, digest):
 # ---------------------------------------------------------------------------
 # Workloads
 # ---------------------------------------------------------------------------
-def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None):
+# one MLRA latent head (L = 1, rank r/L, H/L query heads) as a workload of its own
+MLRA_LATENT_HEAD = S.CONFIGS["mlra_decode"].replace(name="mlra_latent_head", n_heads=4, r_kv=128, n_latent_heads=1)
+
+
+def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None, ctx_from=None):
     torch = __import__("torch")
     d = Dev(cfg)
     M = d.M
     B = cfg.batch
-    ctx = [int(c) for c in d.prob.ctx_lens]
+    ctx = [int(c) for c in (S.make_problem(ctx_from).ctx_lens if ctx_from is not None else d.prob.ctx_lens)]
     max_ctx = max(ctx)
     max_seq = max_ctx + 8
     log(f"[bench] {cfg.name}: filling latent cache ({sum(ctx)} tokens)")
@@ -489,17 +495,18 @@ def summarize_profiles(d):
     mstats = rows("mlra_stats", "*kernel_stats.csv")
     if mstats:
         ml = ["# Kernel times: MLRA decode (B=128, contexts U[512, 16384], 4 latent blocks x rank 128, "
-              "H=16, d_model=2048)", "",
+              "H=16, d_model=2048) and one of its latent heads on its own (rank 128, 4 query heads)", "",
               "Command (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
               "```",
               "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/mlra_stats -o run -- "
               "python3 bench.py --only mlra --steps 20 --warmup 5",
               "python3 bench.py --summarize <dir>",
               "```", "",
-              "mla_decode_attention = split kernel (decode_fast_kernel) + combine kernel; the call also runs "
-              "the few-row projections and the cache append.", "",
+              "mla_decode_attention = split kernel (decode_fast_kernel; `true` = the token-split form of the "
+              "latent-head workload) + combine kernel; the calls also run the few-row projections and the "
+              "cache append.", "",
               "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
-        for r in mstats[:10]:
+        for r in mstats[:14]:
             ml.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                       f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
         ml += ["", f"Kernel sources digest: {src_digest(*UNIT_SOURCES['mlra_decode_attention'])}", ""]
@@ -554,6 +561,8 @@ def main():
         out["prefill"] = bench_prefill(S.CONFIGS["dsv2_prefill"], max(3, args.steps // 4), max(1, args.warmup // 2))
     if args.only in ("all", "mlra"):
         out["mlra"], _ = bench_decode(S.CONFIGS["mlra_decode"], args.steps, args.warmup, copies=1)
+        out["mlra_lh"], _ = bench_decode(MLRA_LATENT_HEAD, args.steps, args.warmup, copies=1,
+                                         ctx_from=S.CONFIGS["mlra_decode"])
     if args.only in ("all", "small"):
         out["small"] = bench_prefill(S.CONFIGS["small_lm"], args.steps, args.warmup)
     if args.only != "all":
@@ -633,6 +642,16 @@ def main():
                      "achieved": ml["attention_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ml["attention_GBps"] / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": ml["cache_bytes"], "ms_per_launch": ml["attention_ms"]},
+    }
+    lh = out["mlra_lh"]
+    line["mlra_latent_head_decode"] = {
+        "workload": "one MLRA latent head: rank 128, its 4 query heads, d_model=2048, B=128, the contexts of "
+                    "mlra_decode (token-split decode kernel)",
+        "ms_per_call": lh["ms_per_call"], "cache_GBps_call": lh["cache_GBps_call"], "cache_bytes": lh["cache_bytes"],
+        "roofline": {"kernel": "mla_decode_attention unit (token-split kernel + combine)", "bound": "hbm",
+                     "achieved": lh["attention_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": lh["attention_GBps"] / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_launch": lh["cache_bytes"], "ms_per_launch": lh["attention_ms"]},
     }
     sm = out["small"]
     line["small_lm_prefill"] = {"workload": "small-LM MLA prefill B=8, S=1024, d_model=512, H=8, r_kv=256",
