@@ -64,6 +64,29 @@ def test_decode_full(gu, name, sample):
         gu.assert_close(y[b], O.decode(seq, lay.prob.weights, d), cfg.dtype, f"y b={b} ctx={ctx[b]}")
 
 
+def test_decode_latent_head_full(gu):
+    """One MLRA latent head on its own (rank 128, its 4 query heads) over the full MLRA
+    contexts: the token-split decode kernel with 4096-token splits, four partial rows each."""
+    import latent_heads as LH
+    full = S.make_problem(S.CONFIGS["mlra_decode"])
+    pg = LH.block_problem(full, 2)
+    cfg = pg.cfg
+    sample = [0, 77, 127]
+    gu.say(f"[decode-full] {cfg.name} B={cfg.batch} sample={sample}")
+    lay = gu.Layer(cfg, pg)
+    ctx = [int(c) for c in pg.ctx_lens]
+    B = cfg.batch
+    max_ctx = max(ctx)
+    ckv, kr = lay.new_cache(B, max_ctx + 8, fill=3.0)
+    last = _fill_with_last(gu, lay, ckv, kr, ctx)
+    y = gu.to_host(lay.decode(gu.to_dev(last, cfg), ctx, lay.cache_view(ckv, kr, 0, B)))
+    assert np.all(np.isfinite(y))
+    d = O.Dims.from_cfg(cfg)
+    for b in sample:
+        seq = S.make_x(cfg, b, ctx[b] + 1)
+        gu.assert_close(y[b], O.decode(seq, pg.weights, d), cfg.dtype, f"y b={b} ctx={ctx[b]}")
+
+
 @pytest.mark.parametrize("name,sample", [("dsv2_decode", [0, 63]), ("mlra_decode", [0, 77, 127])])
 def test_decode_attention_full(gu, name, sample):
     """mla_decode_attention at full size over the cache the library filled, with absorbed
