@@ -151,6 +151,7 @@ size_t decode_gemm_split_bytes(const mla_dims* d, int B) {
   auto take = [&](size_t v) { m = v > m ? v : m; };
   if (dec && d->r_q > 0) take(skinny_ws_bytes(B, d->r_q, d->d_model, 1));
   if (dec && d->r_q > 0) take(skinny_ws_bytes(B, d->r_q + d->r_kv + d->d_rope, d->d_model, 1));
+  if (d->r_q == 0 && d->d_rope == 0) take(skinny_ws_bytes(B, H * d->d_nope + d->r_kv, d->d_model, 1));
   take(skinny_ws_bytes(B, H * d->d_nope + (dec ? H * d->d_rope : 0), src_w, 1));
   take(skinny_ws_bytes(B, d->r_kv + d->d_rope, d->d_model, 1));
   take(skinny_ws_bytes(B, d->d_v, rblock(d), H));
@@ -351,15 +352,16 @@ hipError_t run_queries(const mla_dims* d, const mla_weights* w, const void* x, i
   return launch_gemm(p, 1, bf, st);
 }
 
-// Decode step, query latent present: the three products of the new tokens x -- c_Q = W_DQ x,
-// c = W_DKV x and k_R = RoPE(W_KR x) -- as one few-row product with three output segments
-// (one launch, one split-K reduce; the latent rows go to cache rows (b, pos0[b])).  Returns
-// false, launching nothing, when the shape does not take that path.
-bool run_down_proj(const mla_dims* d, const mla_weights* w, const void* x, int B, const int32_t* pos0,
-                   const mla_cache* cache, void* cq, hipStream_t st, const SplitWs& sw, hipError_t* err) {
-  if (!is_bf16(d) || d->rope_mode != MLA_ROPE_DECOUPLED_INTERLEAVED || d->r_q <= 0 || d->d_rope <= 0 ||
-      B > 128)
-    return false;
+// Decode step: the products of the new tokens x in one few-row product with several output
+// segments (one launch, one split-K reduce; latent rows go to cache rows (b, pos0[b])):
+//   DOWN_CQ  query latent present: c_Q = W_DQ x, c = W_DKV x, k_R = RoPE(W_KR x);
+//   DOWN_Q   no query latent and no rotary part (MLRA): q = W_Q x, c = W_DKV x.
+// Returns DOWN_NONE, launching nothing, when the shape does not take that path.
+enum DownMerge { DOWN_NONE = 0, DOWN_CQ = 1, DOWN_Q = 2 };
+DownMerge run_down_proj(const mla_dims* d, const mla_weights* w, const void* x, int B, const int32_t* pos0,
+                        const mla_cache* cache, void* cq, void* q, hipStream_t st, const SplitWs& sw,
+                        hipError_t* err) {
+  if (!is_bf16(d) || B > 128) return DOWN_NONE;
   GemmParams p = gemm_base(d);
   use_split(p, sw);
   p.a = x;
@@ -369,18 +371,30 @@ bool run_down_proj(const mla_dims* d, const mla_weights* w, const void* x, int B
   p.rows_per_batch = 1;
   p.pos0 = pos0;
   p.out_bstride = cache->max_seq;
-  p.nseg = 3;
-  p.seg[0] = plain_seg(w->w_dq, d->d_model, d->r_q, cq, d->r_q, false);
-  p.seg[1] = plain_seg(w->w_dkv, d->d_model, d->r_kv, cache->ckv, d->r_kv, false);
-  p.seg[1].out_cache = 1;
-  p.seg[2] = plain_seg(w->w_kr, d->d_model, d->d_rope, cache->kr, d->d_rope, false);
-  p.seg[2].out_cache = 1;
-  p.seg[2].rope = ROPE_INTERLEAVED;
-  p.seg[2].rope_d = d->d_rope;
-  make_rope_table(&p.rope, d->d_rope, d->rope_base);
-  if (!skinny_supported(p, 1)) return false;
+  DownMerge kind;
+  if (d->rope_mode == MLA_ROPE_DECOUPLED_INTERLEAVED && d->r_q > 0 && d->d_rope > 0) {
+    kind = DOWN_CQ;
+    p.nseg = 3;
+    p.seg[0] = plain_seg(w->w_dq, d->d_model, d->r_q, cq, d->r_q, false);
+    p.seg[1] = plain_seg(w->w_dkv, d->d_model, d->r_kv, cache->ckv, d->r_kv, false);
+    p.seg[1].out_cache = 1;
+    p.seg[2] = plain_seg(w->w_kr, d->d_model, d->d_rope, cache->kr, d->d_rope, false);
+    p.seg[2].out_cache = 1;
+    p.seg[2].rope = ROPE_INTERLEAVED;
+    p.seg[2].rope_d = d->d_rope;
+    make_rope_table(&p.rope, d->d_rope, d->rope_base);
+  } else if (d->rope_mode == MLA_ROPE_NONE && d->r_q == 0 && d->d_rope == 0) {
+    kind = DOWN_Q;                     // q rows [H][d_nope] are plain rows of H * d_nope
+    p.nseg = 2;
+    p.seg[0] = plain_seg(w->w_q, d->d_model, d->n_heads * d->d_nope, q, (long long)d->n_heads * d->d_nope, false);
+    p.seg[1] = plain_seg(w->w_dkv, d->d_model, d->r_kv, cache->ckv, d->r_kv, false);
+    p.seg[1].out_cache = 1;
+  } else {
+    return DOWN_NONE;
+  }
+  if (!skinny_supported(p, 1)) return DOWN_NONE;
   *err = launch_gemm(p, 1, true, st);
-  return true;
+  return kind;
 }
 
 // Explicit keys / values from the latent rows 0..S-1 of each sequence.
@@ -803,12 +817,14 @@ mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, in
   void* q = at(ws, lay.q);
   // 1. the query latent and the new latent / rotary key (appended at row ctx_len[b]) in one
   //    product where the shape allows, then the queries rotated at position ctx_len[b]
-  const bool merged = run_down_proj(d, w, x, B, ctx_len_dev, cache, at(ws, lay.cq), st, sw, &e);
-  if (merged && e != hipSuccess) return MLA_ERR_HIP;
-  e = run_queries(d, w, x, B, 1, ctx_len_dev, at(ws, lay.cq), q, st, sw, merged);
-  if (e != hipSuccess) return MLA_ERR_HIP;
+  const DownMerge merged = run_down_proj(d, w, x, B, ctx_len_dev, cache, at(ws, lay.cq), q, st, sw, &e);
+  if (merged != DOWN_NONE && e != hipSuccess) return MLA_ERR_HIP;
+  if (merged != DOWN_Q) {
+    e = run_queries(d, w, x, B, 1, ctx_len_dev, at(ws, lay.cq), q, st, sw, merged == DOWN_CQ);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
   // 2. otherwise append the new latent / rotary key at row ctx_len[b] here
-  if (!merged) {
+  if (merged == DOWN_NONE) {
     e = run_latent(d, w, x, B, 1, ctx_len_dev, cache, nullptr, nullptr, st, sw);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
