@@ -195,6 +195,27 @@ def test_decode(gu, cfg, ctx):
         assert np.all(ckv_h[b, ctx[b] + 1:] == SENTINEL)
 
 
+def test_decode_many_sequences(gu):
+    """150 sequences: above the few-row path's 128 rows, so the decode step's projections run
+    on the general GEMM kernels, and the fused combine's fifth group of 32 holds 22.  All
+    outputs finite; sampled sequences (both sides of every group edge) against the oracle."""
+    cfg = DSV2
+    ctx = [int(c) for c in np.random.default_rng(150).integers(0, 24, size=150)]
+    sample = [0, 31, 32, 127, 128, 129, 140, 149]
+    gu.say(f"[decode] {cfg.name} B={len(ctx)} sample={sample}")
+    lay = layer(gu, cfg)
+    B = len(ctx)
+    ckv, kr = lay.new_cache(B, max(ctx) + 9, fill=SENTINEL)
+    lay.fill_cache(ckv, kr, ctx)
+    last = np.stack([S.make_x(cfg, b, ctx[b] + 1)[-1] for b in range(B)])
+    y = gu.to_host(lay.decode(gu.to_dev(last, cfg), ctx, lay.cache_view(ckv, kr, 0, B)))
+    assert np.all(np.isfinite(y))
+    d = _dims(cfg)
+    for b in sample:
+        gu.assert_close(y[b], O.decode(S.make_x(cfg, b, ctx[b] + 1), lay.prob.weights, d), cfg.dtype,
+                        f"y b={b} ctx={ctx[b]}")
+
+
 def test_decode_every_position_tiny(gu):
     """fp32: decoding token t after a cache of t tokens equals prefill row t, for all t."""
     cfg = TINY
