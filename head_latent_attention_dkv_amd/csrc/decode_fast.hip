@@ -602,7 +602,8 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
 // Shapes served by the fast path: bf16; MLA with latent 512 (+ rotary 64 or none) and a
 // multiple of 128 heads... or fewer; MLRA with 4 blocks of 128 and <= 32 heads per block.
 bool decode_fast_supported(const DecodeParams& p, int* variant) {
-  const bool rope_ok = p.d_rope == 64 || p.d_rope == 0;
+  // (the rotary rows are addressed inside their sequence with a 32-bit byte offset)
+  const bool rope_ok = p.d_rope == 0 || (p.d_rope == 64 && p.cache_bstride < (1LL << 25));
   if (p.L == 1 && p.r_kv == 512 && p.rb == 512 && rope_ok) {
     *variant = p.d_rope ? 3 : 4;
     return true;
@@ -611,7 +612,8 @@ bool decode_fast_supported(const DecodeParams& p, int* variant) {
     *variant = 2;
     return true;
   }
-  if (p.L == 1 && p.r_kv == 128 && p.rb == 128 && p.d_rope == 0) {
+  // (the token-split copies address a row inside its sequence with a 32-bit byte offset)
+  if (p.L == 1 && p.r_kv == 128 && p.rb == 128 && p.d_rope == 0 && p.cache_bstride < (1LL << 23)) {
     *variant = 5;
     return true;
   }

@@ -254,15 +254,39 @@ def test_decode_is_deterministic(gu):
                          ids=["dsv2", "mlra", "mlra_latent_head"])
 def test_decode_attention_entry(gu, cfg, ctx):
     """mla_decode_attention on latent rows and absorbed queries made by the oracle."""
+    _decode_attention_case(gu, cfg, ctx)
+
+
+# Cache strides (rows per sequence) around the point where a row's byte offset inside its
+# sequence stops fitting 32 bits for the fast kernels: the latent-head kernel's 256-byte
+# rows (2^23) and the 128-byte rotary rows of the DSV2 kernel (2^25).  Only the first rows
+# of each sequence are filled; the rows just past each context hold large values that any
+# read beyond the context would turn into a mismatch.
+@pytest.mark.parametrize("cfg,max_seq", [(LH.block_cfg(MLRA), 2**23 - 64), (LH.block_cfg(MLRA), 2**23 + 64),
+                                         (DSV2, 2**25 + 64)],
+                         ids=["latent_head_below", "latent_head_above", "dsv2_above"])
+def test_decode_attention_long_cache_stride(gu, cfg, max_seq):
+    cache_bytes = 2 * max_seq * (cfg.r_kv + cfg.d_rope) * 2
+    free, _ = torch.cuda.mem_get_info()
+    if free < cache_bytes + (4 << 30):
+        pytest.skip(f"needs {cache_bytes >> 30} GiB of free device memory")
+    try:
+        _decode_attention_case(gu, cfg, [300, 77], max_seq=max_seq)
+    finally:
+        torch.cuda.empty_cache()
+
+
+def _decode_attention_case(gu, cfg, ctx, max_seq=None):
     import head_latent_attention_dkv_amd as M
-    gu.say(f"[decode_attention] {cfg.name} ctx={ctx}")
+    gu.say(f"[decode_attention] {cfg.name} ctx={ctx} max_seq={max_seq}")
     lay = layer(gu, cfg)
     d = _dims(cfg)
     B, H, L = len(ctx), cfg.n_heads, cfg.n_latent_heads
     rb = cfg.r_kv // L
-    max_seq = max(ctx) + 1
-    ckv_h = np.zeros((B, max_seq, cfg.r_kv), np.float32)
-    kr_h = np.zeros((B, max_seq, cfg.d_rope), np.float32) if cfg.d_rope else None
+    n_host = max(ctx) + 1
+    max_seq = max_seq or n_host
+    ckv_h = np.zeros((B, n_host, cfg.r_kv), np.float32)
+    kr_h = np.zeros((B, n_host, cfg.d_rope), np.float32) if cfg.d_rope else None
     q_lat = np.zeros((B, H, rb), np.float32)
     q_rope = np.zeros((B, H, cfg.d_rope), np.float32) if cfg.d_rope else None
     want = np.zeros((B, H, rb))
@@ -282,7 +306,19 @@ def test_decode_attention_entry(gu, cfg, ctx):
             lat = ckv_h[b, :n, g * rb:(g + 1) * rb]
             want[b, h] = O.latent_attention(q_lat[b, h][None], None if q_rope is None else q_rope[b, h][None],
                                             lat, None if kr_h is None else kr_h[b, :n], d.scale())[0]
-    ckv, kr = gu.to_dev(ckv_h, cfg), (gu.to_dev(kr_h, cfg) if kr_h is not None else None)
+    if max_seq == n_host:
+        ckv, kr = gu.to_dev(ckv_h, cfg), (gu.to_dev(kr_h, cfg) if kr_h is not None else None)
+    else:
+        tail = min(64, max_seq - n_host)
+        ckv = torch.empty((B, max_seq, cfg.r_kv), dtype=gu.tdtype(cfg), device="cuda")
+        kr = torch.empty((B, max_seq, cfg.d_rope), dtype=gu.tdtype(cfg), device="cuda") if cfg.d_rope else None
+        for b in range(B):
+            n = ctx[b] + 1
+            ckv[b, :n].copy_(gu.to_dev(ckv_h[b, :n], cfg))
+            ckv[b, n:n + tail].fill_(SENTINEL * 1e4)
+            if kr is not None:
+                kr[b, :n].copy_(gu.to_dev(kr_h[b, :n], cfg))
+                kr[b, n:n + tail].fill_(SENTINEL * 1e4)
     z = torch.empty((B, H, rb), dtype=gu.tdtype(cfg), device="cuda")
     cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
     ws, nbytes = lay.workspace(M.MLA_OP_DECODE_ATTENTION, B, max(ctx))
