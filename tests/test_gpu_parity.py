@@ -246,6 +246,53 @@ def test_decode_is_deterministic(gu):
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("cfg,ctx", [(DSV2, [37, 300, 1000]), (MLRA, [5, 1030]),
+                                     (LH.block_cfg(MLRA), [0, 129, 1030])],
+                         ids=["dsv2", "mlra", "mlra_latent_head"])
+def test_decode_graph_replay(gu, cfg, ctx):
+    """mla_decode captured into a HIP graph: the call makes no allocation, fill or host
+    synchronisation, so the captured kernels replay it.  Every replay, with eager work and a
+    synchronisation between replays, equals the eager call bit for bit, and leaves the same
+    cache."""
+    import head_latent_attention_dkv_amd as M
+    gu.say(f"[decode graph] {cfg.name} ctx={ctx}")
+    lay = layer(gu, cfg)
+    B = len(ctx)
+    ckv, kr = lay.new_cache(B, max(ctx) + 1)
+    lay.fill_cache(ckv, kr, ctx)
+    x = gu.to_dev(np.stack([S.make_x(cfg, b, ctx[b] + 1)[-1] for b in range(B)]), cfg)
+    cs = lay.cache_view(ckv, kr, 0, B)
+    cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    mc = max(ctx)
+    ws, n = lay.workspace(M.MLA_OP_DECODE, B, mc)
+    y = torch.empty((B, cfg.d_model), dtype=torch.float32, device="cuda")
+
+    def call():
+        M.mla_decode(lay.dims, lay.ws_struct, x, B, cl, mc, cs, y, ws, n)
+
+    call()
+    torch.cuda.synchronize()
+    want, ckv_want = y.clone(), ckv.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want), f"replay {i}"
+        assert torch.equal(ckv, ckv_want), f"cache after replay {i}"
+    del g
+
+
 # ---------------------------------------------------------------------------
 # Staged entry points with oracle-made inputs
 # ---------------------------------------------------------------------------
