@@ -206,6 +206,27 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None, ctx_from=No
     st_call = {}
     ms = timed(torch, step, steps, warmup, st_call)
 
+    # the same step replayed from HIP graphs (one per cache copy): the launches of the
+    # step's kernels are recorded once
+    ms_graph, st_graph = float("nan"), {}
+    if steps > 0:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(copies):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(copies):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(i)
+            graphs.append(gr)
+        log(f"[bench] {cfg.name}: timing mla_decode replayed from a graph")
+        ms_graph = timed(torch, lambda i: graphs[i % copies].replay(), steps, warmup, st_graph)
+        del graphs
+
     # dominant kernel unit: split-context latent attention + combine
     H, L = cfg.n_heads, cfg.n_latent_heads
     rb = cfg.r_kv // L
@@ -222,7 +243,7 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None, ctx_from=No
     st_att = {}
     ms_att = timed(torch, att, attention_steps or steps, warmup, st_att)
     res = {
-        "call_stats": st_call, "attention_stats": st_att,
+        "call_stats": st_call, "attention_stats": st_att, "ms_per_call_graph": ms_graph, "graph_stats": st_graph,
         "workload": cfg.name, "batch": B, "ctx_total": int(sum(ctx)), "max_ctx": max_ctx,
         "ms_per_call": ms, "cache_bytes": int(cache_bytes), "weight_bytes": int(weight_bytes),
         "cache_GBps_call": cache_bytes / ms / 1e6,
@@ -611,7 +632,9 @@ def main():
                         "GBps_incl_weights": dec["call_GBps_incl_weights"], "weight_bytes": dec["weight_bytes"],
                         "cache_bytes": dec["cache_bytes"],
                         "frac_of_hbm_incl_weights": dec["call_GBps_incl_weights"] / HBM_PEAK_GBS,
-                        "tokens_per_s": cfg3.batch / (dec["ms_per_call"] * 1e-3)},
+                        "tokens_per_s": cfg3.batch / (dec["ms_per_call"] * 1e-3),
+                        "graph_replay": {"ms": dec["ms_per_call_graph"], "timing": dec["graph_stats"],
+                                         "cache_GBps": dec["cache_bytes"] / dec["ms_per_call_graph"] / 1e6}},
     }
     pre = out["prefill"]
     line["prefill"] = {
