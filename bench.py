@@ -54,6 +54,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+_PROBLEMS = {}
+
+
+def problem(cfg):
+    """Seeded weights of a workload, drawn once per process (the draw takes seconds at d_model 5120)."""
+    if cfg not in _PROBLEMS:
+        _PROBLEMS[cfg] = S.make_problem(cfg)
+    return _PROBLEMS[cfg]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -71,7 +81,7 @@ class Dev:
         import head_latent_attention_dkv_amd as M
         self.torch, self.M = torch, M
         self.cfg = cfg
-        self.prob = S.make_problem(cfg)
+        self.prob = problem(cfg)
         self.dims = M.dims_from_cfg(cfg)
         self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.w = {k: self.up(v) for k, v in self.prob.weights.items()}
@@ -183,7 +193,7 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None, ctx_from=No
     d = Dev(cfg)
     M = d.M
     B = cfg.batch
-    ctx = [int(c) for c in (S.make_problem(ctx_from).ctx_lens if ctx_from is not None else d.prob.ctx_lens)]
+    ctx = [int(c) for c in (problem(ctx_from).ctx_lens if ctx_from is not None else d.prob.ctx_lens)]
     max_ctx = max(ctx)
     max_seq = max_ctx + 8
     log(f"[bench] {cfg.name}: filling latent cache ({sum(ctx)} tokens)")
@@ -334,7 +344,7 @@ def cpu_baseline(cfg, budget_s=15.0, max_seqs=64):
         cores = max([i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"] or [0])
     except Exception:  # pragma: no cover
         cores = 0
-    prob = S.make_problem(cfg)
+    prob = problem(cfg)
     d = O.Dims.from_cfg(cfg)
     done, t_tot, nbytes = 0, 0.0, 0
     while done < max_seqs and (t_tot < budget_s or done == 0):
@@ -350,6 +360,40 @@ def cpu_baseline(cfg, budget_s=15.0, max_seqs=64):
             "kind": "oracle",
             "sample": f"{done} of {cfg.batch} sequences of {cfg.name} (fp64 numpy decode step with "
                       f"explicit K/V up-projection), {t_tot:.1f} s; value = their latent-cache bytes / time"}
+
+
+def cpu_baseline_prefill(cfg, budget_s=12.0, rows_per_seq=32):
+    """fp64 oracle on a bounded sample of the prefill workload: for each sampled sequence,
+    its whole explicit K/V up-projection and the causal attention of `rows_per_seq` query rows
+    spread over the sequence (the oracle's forward restricted to those rows).  The value counts
+    the same algorithmic flops as the GPU attention unit for that sample."""
+    from oracle import mla_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"] or [0])
+    except Exception:  # pragma: no cover
+        cores = 0
+    prob = problem(cfg)
+    d = O.Dims.from_cfg(cfg)
+    S_, H = cfg.seq, cfg.n_heads
+    dq, dv = cfg.d_nope + cfg.d_rope, cfg.d_v
+    rows = np.linspace(0, S_ - 1, rows_per_seq).round().astype(int)
+    kvup = 2.0 * S_ * cfg.r_kv * H * (cfg.d_nope + dv) / cfg.n_latent_heads
+    core = float(sum(2.0 * H * (r + 1) * (dq + dv) for r in rows))
+    done, t_tot = 0, 0.0
+    while done < cfg.batch and (t_tot < budget_s or done == 0):
+        x = S.make_x(cfg, done, S_)
+        t0 = time.perf_counter()
+        O.forward(x, prob.weights, d, q_rows=rows)
+        t_tot += time.perf_counter() - t0
+        done += 1
+    flop = done * (kvup + core)
+    return {"value": flop / t_tot / 1e12, "unit": "TFLOP/s", "cores": int(cores or host_threads()),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences of {cfg.name}: explicit K/V up-projection of all "
+                      f"{S_} rows + causal attention of {rows_per_seq} query rows each (fp64 numpy), "
+                      f"{t_tot:.1f} s; value = that sample's attention-unit flops / time"}
 
 
 def summarize_profiles(d):
@@ -582,7 +626,8 @@ def main():
         out["prefill"] = bench_prefill(S.CONFIGS["dsv2_prefill"], max(3, args.steps // 4), max(1, args.warmup // 2))
     if args.only in ("all", "mlra"):
         out["mlra"], _ = bench_decode(S.CONFIGS["mlra_decode"], args.steps, args.warmup, copies=1)
-        out["mlra_lh"], _ = bench_decode(MLRA_LATENT_HEAD, args.steps, args.warmup, copies=1,
+        # one latent head's cache is 288 MB: two copies (576 MB) exceed the 256 MB Infinity Cache
+        out["mlra_lh"], _ = bench_decode(MLRA_LATENT_HEAD, args.steps, args.warmup, copies=2,
                                          ctx_from=S.CONFIGS["mlra_decode"])
     if args.only in ("all", "small"):
         out["small"] = bench_prefill(S.CONFIGS["small_lm"], args.steps, args.warmup)
@@ -683,6 +728,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(S.CONFIGS["dsv2_decode"])
+        log("[bench] cpu baseline of the prefill unit (oracle)")
+        line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(S.CONFIGS["dsv2_prefill"])
     print(json.dumps(line))
 
 

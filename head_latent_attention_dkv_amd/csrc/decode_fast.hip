@@ -131,11 +131,10 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
     qf[ks] = frag_load<bf16>(ks < C::KSL ? qlp + ks * 32 : qrp + (ks - C::KSL) * 32);
     if (!head_ok) qf[ks] = frag_zero<bf16>();
   }
-  // Materialise Q before the first copies are issued, so that no wait for these loads
-  // lands behind (and drains) the copy pipeline.
-  wait_vmcnt<0>();
+  // Materialise Q, then open the copy phase (lds_dma.h, rule 1).
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(qf[ks].v));
+  copies_begin();
 
   // DMA: latent row t of the tile is one wave-wide 1 KB load (scalar row base, 32-bit lane
   // offset: physical chunk ln holds logical chunk ln ^ bitrev4(t))
@@ -282,7 +281,7 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
   pass(std::integral_constant<int, 0>{});
   // p >= 0, so a p above 2^kRestartGap shows in its lane's sum
   if (__builtin_amdgcn_readfirstlane(__any(!(l_run <= kRestartLimit)))) redo = true;
-  wait_vmcnt<0>();
+  copies_end();
   __syncthreads();
   if (threadIdx.x == 0) *vote = 0;
   __syncthreads();
@@ -299,7 +298,7 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
     wait_vmcnt<0>();
     __syncthreads();
     pass(std::integral_constant<int, 2>{});
-    wait_vmcnt<0>();
+    copies_end();   // lds_dma.h, rule 3: before the partial-result stores
   }
 
   const float l_tot = head_sum(l_run);
@@ -393,12 +392,12 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
   Frag<bf16> qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_load<bf16>(ks < KSL ? qlp + 16 * ks : qrp + 16 * (ks - KSL));
-  wait_vmcnt<0>();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (!head_ok) qf[ks] = frag_zero<bf16>();
     asm volatile("" ::"v"(qf[ks].v));
   }
+  copies_begin();   // lds_dma.h, rule 1
 
   // ---- per-lane LDS byte offsets inside a stage.  The XOR swizzle only touches the low 4
   // bits of a chunk index, so for a step index n = 8 j + r (scores) or 4 j + r (values) the
@@ -554,7 +553,7 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
   pass(std::integral_constant<int, 0>{});
   // p >= 0, so a p above 2^kRestartGap shows in its lane's sum
   if (__builtin_amdgcn_readfirstlane(__any(!(l_run <= kRestartLimit)))) redo = true;
-  wait_vmcnt<0>();
+  copies_end();
   __syncthreads();
   if (threadIdx.x == 0) *vote = 0;
   __syncthreads();
@@ -571,7 +570,7 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
     wait_vmcnt<0>();
     __syncthreads();
     pass(std::integral_constant<int, 2>{});
-    wait_vmcnt<0>();
+    copies_end();   // lds_dma.h, rule 3: before the partial-result stores
   }
 
   auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);

@@ -125,6 +125,7 @@ __global__ void __launch_bounds__(64 * NW, BigCfg<NW>::MINB) gemm_big_kernel(Gem
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  copies_begin();   // lds_dma.h, rule 1
 #pragma unroll
   for (int st = 0; st < GNST - 1; ++st)
     if (st < nst) issue(st);
@@ -164,7 +165,7 @@ __global__ void __launch_bounds__(64 * NW, BigCfg<NW>::MINB) gemm_big_kernel(Gem
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
   }
-  wait_vmcnt<0>();
+  copies_end();   // lds_dma.h, rule 3
   __syncthreads();
 
   if constexpr (DIRECT) {

@@ -74,7 +74,14 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
       if (sg.layout == OUT_ROWS) {
         long long oc = sg.out_hw ? (long long)(nn / sg.out_hw) * sg.out_hs + (nn % sg.out_hw) : nn;
         oc += o_goff;
-        const long long orow = sg.out_cache ? (long long)b * p.out_bstride + (p.pos0 ? p.pos0[b] : 0) + t : m;
+        long long orow = m;
+        if (sg.out_cache) {
+          // a cache row outside the sequence's rows (a start position beyond the host bound)
+          // is dropped rather than written into a neighbouring sequence
+          const long long crow = (long long)(p.pos0 ? p.pos0[b] : 0) + t;
+          if (crow < 0 || crow >= p.out_bstride) continue;
+          orow = (long long)b * p.out_bstride + crow;
+        }
         idx = orow * sg.out_ld + oc;
       } else {
         const long long cc = nn + o_goff;
@@ -153,7 +160,12 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
       long long idx;
       if (sg.layout == OUT_ROWS) {
         const long long oc = hw ? head * sg.out_hs + j0 : cc;
-        const long long orow = sg.out_cache ? (long long)b * p.out_bstride + (p.pos0 ? p.pos0[b] : 0) + t : m;
+        long long orow = m;
+        if (sg.out_cache) {
+          const long long crow = (long long)(p.pos0 ? p.pos0[b] : 0) + t;
+          if (crow < 0 || crow >= p.out_bstride) continue;
+          orow = (long long)b * p.out_bstride + crow;
+        }
         idx = orow * sg.out_ld + oc;
       } else {
         idx = (((long long)b * sg.out_nh + head) * p.rows_per_batch + t) * hw + j0;

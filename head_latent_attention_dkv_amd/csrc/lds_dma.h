@@ -7,11 +7,38 @@
 
 namespace mla {
 
+// Copy-phase rule (every kernel that issues the copies below follows it):
+//
+//   While any copy of a wave is in flight, that wave has no other vector-memory operation
+//   (global or buffer load, store or atomic that the compiler emits) in flight.
+//
+// One counter, vmcnt, tracks every vector-memory operation of a wave.  The pipelines wait
+// for "all but the newest N copies" with explicit wait_vmcnt<N>, which is exact only if
+// every counted operation is a copy: the ISA returns loads of one kind in issue order, but
+// a copy (which completes when its data is written to LDS) and a load into VGPRs, or a
+// store, are not ordered with respect to each other, so with both kinds in flight a count
+// of N no longer says which operations are done.  The compiler, for its part, computes the
+// waits before the uses of its own loads without seeing the copies (they are inline
+// assembly).  So a kernel
+//   1. issues and consumes its own loads (query fragments, table reads) first and calls
+//      copies_begin() -- which drains them -- before its first copy;
+//   2. issues no compiler-visible vector-memory operation inside the copy loop (the loop
+//      body reads LDS only);
+//   3. calls copies_end() -- which drains the copies -- before the first compiler-visible
+//      vector-memory operation after the loop (partial-result stores, the epilogue).
+// A kernel that once issued later tiles' copies behind its query loads, against rule 1,
+// read wrong tiles although the bytes in HBM were right.
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// Opens a copy phase (rule 1): no compiler-visible vector-memory operation stays in flight.
+__device__ __forceinline__ void copies_begin() { wait_vmcnt<0>(); }
+// Closes a copy phase (rule 3): every copy has landed in LDS.
+__device__ __forceinline__ void copies_end() { wait_vmcnt<0>(); }
 // Workgroup barrier without the compiler's implicit wait for all outstanding memory.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 

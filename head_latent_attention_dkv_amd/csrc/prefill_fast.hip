@@ -4,15 +4,15 @@
 // (the DSV2 page's concatenation of the decompressed key with the rotary key shared by
 // all heads; DR = 0 for the MLA and MLRA pages' keys, which carry no separate rotary part).
 //
-// Workgroup: 256 queries of one (sequence, head); 4 waves x 64 queries (two 32-query
-// column blocks), Q^T held in VGPRs as the B operand.  Keys stream in tiles of 64 through
+// Workgroup: 256 queries of one (sequence, head); 8 waves x 32 queries (one 32-query column
+// block per wave, two waves per SIMD), Q^T held in VGPRs as the B operand.  Keys stream in tiles of 64 through
 // LDS, NST stages deep, moved with 16-byte direct-to-LDS copies:
 //   K tile  [64 keys][DN] (decompressed part) and [64 keys][DR] (rotary part, shared rows),
 //   V tile  [DV][64 keys] -- values stored transposed per head by the up-projection, with
 //           the keys of every group of 16 in the order 0-3, 8-11, 4-7, 12-15.
 // Per tile and wave:
-//   S^T[64 keys x 64 queries]  = K . Q^T       (32x32x16 MFMA, K index = feature)
-//   O^T[DV x 64 queries]      += V^T . P^T     (32x32x16 MFMA, K index = key)
+//   S^T[64 keys x 32 queries]  = K . Q^T       (32x32x16 MFMA, K index = feature)
+//   O^T[DV x 32 queries]      += V^T . P^T     (32x32x16 MFMA, K index = key)
 // In the S^T accumulator lane l holds, for its query column, keys 4h..4h+3 and 8+4h..8+4h+3
 // (h = l / 32) of every 16-key group: exactly the order in which the transposed value rows
 // are stored, so P^T feeds the second product straight from registers and the V^T operand
@@ -33,10 +33,7 @@ namespace {
 constexpr int FQ = 256;          // queries per workgroup
 constexpr int FK = 64;           // keys per tile
 constexpr int FNST = 3;          // LDS stages
-#ifndef MLA_FLASH_QB
-#define MLA_FLASH_QB 1
-#endif
-constexpr int kFlashQB = MLA_FLASH_QB;   // 32-query blocks per wave (waves per workgroup = 8 / QB)
+constexpr int kFlashQB = 1;      // 32-query blocks per wave (waves per workgroup = 8 / QB)
 constexpr float kFlashGap = 64.0f;    // log2 units: p <= 2^64 stays far from bf16 / fp32 overflow
 constexpr float kFlashLimit = 0x1p64f;  // 2^kFlashGap
 
@@ -115,11 +112,11 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = frag_load<bf16>(qp + 16 * ks);
   }
-  wait_vmcnt<0>();
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(qf[qb][ks].v));
+  copies_begin();   // lds_dma.h, rule 1
 
   // ---- copy sources (byte offsets relative to the tile's first key) ----
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bh * S * DN * 2;
@@ -373,7 +370,7 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
     if (__builtin_amdgcn_readfirstlane(__any(!(l_run[qb] <= kFlashLimit)))) redo = true;
   // workgroup-wide vote: does any wave need the exact-maximum passes?
   __shared__ int redo_flag;
-  wait_vmcnt<0>();
+  copies_end();   // lds_dma.h, rule 3 (also before the output stores below)
   if (threadIdx.x == 0) redo_flag = 0;
   __syncthreads();
   if (redo) redo_flag = 1;
@@ -394,7 +391,7 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
     wait_vmcnt<0>();
     __syncthreads();
     pass(std::integral_constant<int, 2>{});
-    wait_vmcnt<0>();
+    copies_end();
   }
 
   // ---- normalise and store o[b][q][h][:] (4 consecutive features per 8-byte store) ----

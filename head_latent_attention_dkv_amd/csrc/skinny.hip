@@ -249,6 +249,7 @@ __global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_k
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16{};
 
+  copies_begin();   // lds_dma.h, rule 1
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
     if (st < nst) issue(st);
@@ -275,7 +276,7 @@ __global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_k
       }
     }
   }
-  wait_vmcnt<0>();
+  copies_end();   // lds_dma.h, rule 3
   __syncthreads();
 
   // Sum the four waves' partial products in wave order (Cs aliases the stages).
@@ -381,8 +382,12 @@ constexpr int kLongSlab = 2048;           // K per block from which one block pe
 // reach kMinBlocks blocks (or as many as the shape allows) with the least extra traffic:
 // fp32 partials written and read back (8 S M N bytes when S > 1) plus the activations
 // re-read from L2 by every row tile (weighted 1/2: they do not come from HBM).
-SkinnyPlan plan_stream(int M, int N, int K, int groups) {
-  SkinnyPlan best{128, 1, K};
+//
+// min_rows: the smallest tile that keeps every half-split rotary pair (j, j + d/2) of a head
+// inside one tile, whose epilogue reads the partner column from LDS (64 when a segment is
+// rotated half-split, 32 otherwise).
+SkinnyPlan plan_stream(int M, int N, int K, int groups, int min_rows = 32) {
+  SkinnyPlan best{M > 64 ? 64 : 128, 1, K};
   double best_cost = 1e300;
   int best_blocks = 0;
   const int max_s = K / (kStreamKT * kMinStagesPerSlab) > 0 ? K / (kStreamKT * kMinStagesPerSlab) : 1;
@@ -392,7 +397,8 @@ SkinnyPlan plan_stream(int M, int N, int K, int groups) {
   const bool wide = (long long)cdiv(N, 32) * groups >= 512;
   for (int rows : {128, 64, 32}) {
     if (M > 64 && rows == 128) continue;                 // accumulator budget
-    if (wide && rows != 32) continue;
+    if (rows < min_rows) continue;
+    if (wide && rows != (min_rows > 32 ? min_rows : 32)) continue;
     const long long tiles = (long long)cdiv(N, rows) * groups;
     int s = (int)((kMinBlocks + tiles - 1) / tiles);
     s = s < 1 ? 1 : (s > max_s ? max_s : s);
@@ -432,8 +438,15 @@ SkinnyPlan plan_direct(int M, int N, int K, int groups) {
   return {kCols, s, kc};
 }
 
-SkinnyPlan plan(int M, int N, int K, int groups) {
-  return use_stream(K) ? plan_stream(M, N, K, groups) : plan_direct(M, N, K, groups);
+SkinnyPlan plan(int M, int N, int K, int groups, int min_rows = 32) {
+  return use_stream(K) ? plan_stream(M, N, K, groups, min_rows) : plan_direct(M, N, K, groups);
+}
+
+// Smallest streaming tile (output columns) whose blocks hold whole half-split rotary heads.
+int min_stream_rows(const GemmParams& p) {
+  for (int i = 0; i < p.nseg; ++i)
+    if (p.seg[i].rope == ROPE_HALFSPLIT) return 64;
+  return 32;
 }
 
 template <int CB, int ROWS, int NST = ROWS == 128 ? 3 : 4>
@@ -484,7 +497,7 @@ bool skinny_supported(const GemmParams& p, int groups) {
 
 hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s) {
   const int N = seg_total(p);
-  SkinnyPlan pl = plan(p.M, N, p.K, groups);
+  SkinnyPlan pl = plan(p.M, N, p.K, groups, min_stream_rows(p));
   const size_t need = pl.splits > 1 ? (size_t)pl.splits * groups * p.M * N * sizeof(float) : 0;
   if (pl.splits > 1 && (p.part == nullptr || p.part_bytes < need)) {
     pl.splits = 1;

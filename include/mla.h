@@ -22,6 +22,12 @@
  * Every row computes causal softmax attention (query at position p sees keys at
  * positions <= p), then y = W_O [o_1; ...; o_H].
  *
+ * Citations below name a page by tag and a section of it by function or class:
+ *   [MLA page]  frankenstein-transformer docs, ``latent/mla_attn``
+ *   [MLRA page] frankenstein-transformer docs, ``latent/mlra_attn``
+ *   [DSV2 page] bird-of-paradise/deepseek-mla, ``src/mla.py``
+ * Every entry point's comment names its source passage, or says that it is the library's own.
+ *
  * Conventions for every entry point:
  *   - Weights are row-major [out_features][in_features] (torch.nn.Linear layout) in
  *     the element type of dims->dtype.  MLRA up-projections w_uk / w_uv are L dense
@@ -114,16 +120,22 @@ typedef struct {
   int32_t max_batch, max_seq;
 } mla_cache;
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage).
+ * Source: the library's own (the pages define no error codes). */
 const char* mla_status_str(mla_status s);
 
 /* Checks dims against the pages' rules and the kernels' limits.
+ * Source: the pages' constructor checks -- [MLA page] ``MLAAttention.__init__`` and
+ * [MLRA page] ``MLRAAttention.__init__`` (their ValueErrors: the latent-head count L must
+ * divide the latent rank and the heads), and the even-width assertion of [DSV2 page]
+ * ``apply_rotary_emb`` (a rotary width must be even).  The kernel limits are the library's own.
  * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_SHAPE or MLA_ERR_UNSUPPORTED.
  * Kernel limits: d_nope <= 256 (FULL_HALFSPLIT: d_nope divides 128), d_rope <= 64,
  * r_kv / L <= 512, n_heads / L <= 128 * 64.  Host only; no GPU needed. */
 mla_status mla_validate(const mla_dims* dims);
 
-/* Bytes of device workspace entry point `op` needs for `batch` sequences of
+/* Source: the library's own (caller-owned scratch; the pages allocate inside forward).
+ * Bytes of device workspace entry point `op` needs for `batch` sequences of
  * `seq_or_max_ctx` tokens (prefill: S; decode: the largest ctx_len; chunked prefill:
  * start_pos + T).  Returns 0 for invalid arguments and for ops that need none
  * (MLA_OP_CACHE_APPEND).  Host only. */
@@ -140,8 +152,10 @@ mla_status mla_cache_append(const mla_dims* dims, const mla_weights* w, const vo
                             int32_t B, int32_t T, const int32_t* start_pos_dev, int32_t max_start,
                             const mla_cache* cache, void* stream);
 
-/* Causal prefill of B sequences of S tokens at positions 0..S-1 (the pages'
- * ``forward(x)``): explicit K/V up-projection from the latent, flash-style causal
+/* Causal prefill of B sequences of S tokens at positions 0..S-1.
+ * Source: [MLA page] ``MLAAttention.forward``, [MLRA page] ``MLRAAttention.forward`` and
+ * [DSV2 page] ``MultiHeadLatentAttention.forward`` without a cache (start_pos 0), per
+ * family as listed at the top of this file: explicit K/V up-projection from the latent, flash-style causal
  * attention on bf16 MFMA (fp32 MFMA for MLA_DTYPE_F32), then W_O.
  *   x      [B][S][d_model]
  *   cache  optional (NULL allowed): rows 0..S-1 of each sequence are written
@@ -152,6 +166,11 @@ mla_status mla_prefill(const mla_dims* dims, const mla_weights* w, const void* x
                        void* workspace, size_t ws_bytes, void* stream);
 
 /* One decode step: one new token per sequence, absorbed form.
+ * Source: [DSV2 page] ``MultiHeadLatentAttention.forward``, cached path with start_pos:
+ * the new token's latent and rotary key are written at its row, and its query attends to
+ * every cached row up to and including its own (MLRA family: [MLRA page]
+ * ``MLRAAttention.forward`` restricted to the last row).  The absorption of W_UK into the
+ * query and of W_UV after the weighted latent sum is associativity of those products.
  * The new token of sequence b sits at position ctx_len_dev[b]: its latent and rotary key
  * are appended at that row, then it attends over rows 0..ctx_len[b] (ctx_len[b]+1 keys,
  * itself included) with W_UK folded into the query and W_UV applied to the
@@ -168,6 +187,10 @@ mla_status mla_decode(const mla_dims* dims, const mla_weights* w, const void* x,
 
 /* The attention core of one decode step over the latent cache (split-context kernel
  * plus log-sum-exp combine), for absorbed queries that the caller already formed.
+ * Source: the score q . k_j and softmax-weighted value sum of [DSV2 page]
+ * ``MultiHeadLatentAttention.forward`` (scores of the decompressed and rotary parts added,
+ * scaled by 1/sqrt(d_nope + d_rope)), rewritten over the cached latent rows by
+ * associativity: q_C . (W_UK c_j) = (W_UK^T q_C) . c_j.
  * Head h (latent block g = h / (H/L), width rb = r_kv/L) computes
  *   s_j = scale * (q_lat[b][h] . ckv[b][j][g*rb : (g+1)*rb] + q_rope[b][h] . kr[b][j]),
  *   z[b][h] = sum_j softmax_j(s) ckv[b][j][g*rb : (g+1)*rb],   j = 0 .. ctx_len[b]

@@ -88,17 +88,22 @@ def rope_interleaved(v: np.ndarray, pos: np.ndarray, base: float = 10000.0) -> n
 def rope_halfsplit(v: np.ndarray, pos: np.ndarray, base: float = 10000.0) -> np.ndarray:
     """Rotate the pairs (v[j], v[j + dim/2]) by angle pos * theta_j.
 
-    [MLA page] ``_apply_rope``: x1 = first half, x2 = second half,
-    result = [x1 cos - x2 sin, x1 sin + x2 cos].  Shapes as in rope_interleaved.
+    [MLA page] ``_apply_rope``: coordinate j of the first half and coordinate j of the
+    second half form one plane, rotated by the angle of frequency j.  Written here as the
+    complex number z_j = v[j] + i v[j + dim/2] multiplied by the unit phasor
+    exp(i pos theta_j); the real parts go back to the first half, the imaginary parts to
+    the second.  Shapes as in rope_interleaved.
     """
     v = np.asarray(v, dtype=F64)
     dim = v.shape[-1]
     half = dim // 2
     ang = np.asarray(pos, dtype=F64)[:, None] * rope_inv_freq(dim, base)[None, :]
     ang = ang.reshape((ang.shape[0],) + (1,) * (v.ndim - 2) + (half,))
-    c, s = np.cos(ang), np.sin(ang)
-    x1, x2 = v[..., :half], v[..., half:]
-    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+    z = (v[..., :half] + 1j * v[..., half:]) * np.exp(1j * ang)
+    out = np.empty_like(v)
+    out[..., :half] = z.real
+    out[..., half:] = z.imag
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -29,6 +29,28 @@ def test_exports_match_header():
         assert hasattr(L, name), name
 
 
+def _declaration_comments(text):
+    """{entry point: the block comment right above its declaration}"""
+    out = {}
+    for m in re.finditer(r"/\*((?:[^*]|\*(?!/))*)\*/\s*(?:const\s+)?\w+\*?\s+(mla_\w+)\s*\(", text):
+        out[m.group(2)] = m.group(1)
+    return out
+
+
+def test_every_declaration_cites_its_source():
+    """Each entry point's comment names the page section that defines the operation (a
+    [... page] tag followed by a ``function`` or ``Class.method``), or says that it is the
+    library's own."""
+    with open(M.HEADER_PATH) as f:
+        text = f.read()
+    comments = _declaration_comments(text)
+    assert set(comments) == set(M.EXPORTS)
+    cite = re.compile(r"\[(MLA|MLRA|DSV2|CCA) page\]\s+``[\w.]+``")
+    for name, body in comments.items():
+        flat = " ".join(re.sub(r"(?m)^\s*\*", " ", body).split())
+        assert cite.search(flat) or "library's own" in flat, f"{name}: no source passage"
+
+
 def test_status_strings():
     _lib_or_skip()
     for code in range(7):

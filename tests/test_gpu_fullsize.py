@@ -87,13 +87,15 @@ def test_decode_latent_head_full(gu):
         gu.assert_close(y[b], O.decode(seq, pg.weights, d), cfg.dtype, f"y b={b} ctx={ctx[b]}")
 
 
-@pytest.mark.parametrize("name,sample", [("dsv2_decode", [0, 63]), ("mlra_decode", [0, 77, 127])])
-def test_decode_attention_full(gu, name, sample):
+@pytest.mark.parametrize("name", ["dsv2_decode", "mlra_decode"])
+def test_decode_attention_full(gu, name):
     """mla_decode_attention at full size over the cache the library filled, with absorbed
-    queries made by the oracle; the oracle attends over the same (bf16) cache rows."""
+    queries made by the oracle; the oracle attends over the same (bf16) cache rows.  Every
+    sequence (every split work item of the launch) is compared: all heads of one latent
+    block at once, as the queries of one oracle call."""
     import head_latent_attention_dkv_amd as M
     cfg = S.CONFIGS[name]
-    gu.say(f"[decode-attention-full] {name} B={cfg.batch} sample={sample}")
+    gu.say(f"[decode-attention-full] {name} B={cfg.batch} every sequence")
     lay = gu.Layer(cfg)
     W = lay.prob.weights
     ctx = [int(c) for c in lay.prob.ctx_lens]
@@ -124,23 +126,30 @@ def test_decode_attention_full(gu, name, sample):
     M.mla_decode_attention(lay.dims, gu.to_dev(q_lat, cfg), None if q_rope is None else gu.to_dev(q_rope, cfg),
                            B, cl, max_ctx, lay.cache_view(ckv, kr, 0, B), z, ws, nbytes)
     z_h = gu.to_host(z)
-    for b in sample:
+    hpb = H // L
+    for b in range(B):
         n = ctx[b] + 1
         c_rows = gu.to_host(ckv[b, :n])
-        seq_last = S.make_x(cfg, b, n)[-1:]
-        c_new, _ = O.latent_rows(seq_last, W, d, np.array([ctx[b]]))
-        gu.assert_close(c_rows[-1], c_new[0], cfg.dtype, f"appended row b={b}")
+        if b in (0, B - 1):
+            c_new, _ = O.latent_rows(last[b][None], W, d, np.array([ctx[b]]))
+            gu.assert_close(c_rows[-1], c_new[0], cfg.dtype, f"appended row b={b}")
         kr_rows = gu.to_host(kr[b, :n]) if kr is not None else None
         want = np.zeros((H, rb))
-        for h in range(H):
-            g = h // (H // L)
-            want[h] = O.latent_attention(q_lat[b, h][None], None if q_rope is None else q_rope[b, h][None],
-                                         c_rows[:, g * rb:(g + 1) * rb], kr_rows, d.scale())[0]
+        for g in range(L):
+            hs = slice(g * hpb, (g + 1) * hpb)
+            want[hs] = O.latent_attention(q_lat[b, hs], None if q_rope is None else q_rope[b, hs],
+                                          c_rows[:, g * rb:(g + 1) * rb], kr_rows, d.scale())
         gu.assert_close(z_h[b], want, cfg.dtype, f"z b={b} ctx={ctx[b]}")
 
 
+# DeepSeek-V2 prefill: one row in each of the sixteen 256-query tiles of every sequence (the
+# flash kernel's block map differs per tile), at varying offsets inside the tile, plus both
+# ends of the sequence.
+DSV2_PREFILL_ROWS = sorted({0, 4095} | {256 * t + (37 * t + 1) % 256 for t in range(16)})
+
+
 @pytest.mark.parametrize("name,sample_b,rows", [
-    ("dsv2_prefill", [0, 3], [0, 1, 63, 64, 2047, 4095]),
+    ("dsv2_prefill", [0, 1, 2, 3], DSV2_PREFILL_ROWS),
     ("small_lm", [0, 5], None),
 ])
 def test_prefill_full(gu, name, sample_b, rows):
@@ -180,8 +189,9 @@ def test_prefill_chunk_full(gu):
     y = gu.to_host(lay.prefill_chunk(x, start, lay.cache_view(ckv, kr, 0, B)))
     assert np.all(np.isfinite(y))
     d = O.Dims.from_cfg(cfg)
-    rows = [0, 1, 63, 64, 511, 1023]
-    for b in [0, B - 1]:
+    # a row at a boundary of each of the sixteen 64-row groups of the new tokens
+    rows = [64 * g + (63 if g % 2 else 0) for g in range(16)]
+    for b in range(B):
         want = O.forward(xs[b], lay.prob.weights, d, q_rows=[start + r for r in rows])
         got = y[b][rows]
         for i, r in enumerate(rows):

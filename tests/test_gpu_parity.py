@@ -30,6 +30,9 @@ DSV2_PF = S.CONFIGS["dsv2_prefill"].replace(name="dsv2_prefill_s320", d_model=51
 SMALL_PF = S.CONFIGS["small_lm"].replace(name="small_lm_s320", batch=2, seq=320)
 MLRA_PF = S.CONFIGS["mlra_decode"].replace(name="mlra_prefill_s384", mode="prefill", d_model=512, batch=2,
                                            seq=384, ctx_lo=0, ctx_hi=0)
+# Few-row products (B*S <= 128 rows) of the full-RoPE family: the query and key rotations
+# run in the output stage of the few-row GEMM, whose tile must hold whole half-split heads.
+SMALL_FEW = S.CONFIGS["small_lm"].replace(name="small_lm_b1_s64", batch=1, seq=64)
 TINY_BF16_MLRA = S.MLAConfig("mlra_tiny", S.FAMILY_MLRA, "decode", 2, 40, d_model=64, n_heads=8,
                              d_nope=16, d_rope=0, r_kv=32, r_q=0, n_latent_heads=4, seed=77)
 
@@ -90,7 +93,7 @@ def test_cache_append(gu, cfg):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg", [TINY, SMALL, DSV2_P, MLRA.replace(name="mlra_prefill_s150", mode="prefill", batch=2,
                                                                   seq=150),
-                                 DSV2_PF, SMALL_PF, MLRA_PF],
+                                 DSV2_PF, SMALL_PF, MLRA_PF, SMALL_FEW],
                          ids=lambda c: c.name)
 @pytest.mark.parametrize("with_cache", [False, True])
 def test_prefill(gu, cfg, with_cache):
@@ -126,6 +129,8 @@ CHUNK_CASES = [
     (DSV2_P, 37, 50),        # generic path (offset not a multiple of 64), ragged tiles
     (DSV2_PF, 0, 320),       # start 0: the same as mla_prefill with a cache
     (TINY, 5, 3),            # fp32 workload
+    (SMALL, 100, 1),         # full-RoPE family, one new token per sequence (2 rows)
+    (SMALL, 64, 64),         # full-RoPE family, 128 new rows: few-row products with rotation
 ]
 
 
