@@ -196,6 +196,94 @@ def make_x_batch(cfg: MLAConfig, lens: Sequence[int], threads: int = 8) -> List[
         return list(ex.map(lambda bl: make_x(cfg, bl[0], int(bl[1])), enumerate(lens)))
 
 
+# ---------------------------------------------------------------------------
+# Compressed convolutional attention (CCA / CCGQA) workloads
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class CCAConfig:
+    """Shapes of the CCA page's layers.  CCA is the case n_kv_heads == n_heads.
+
+    Weights (drawn in this order, each N(0, 1/fan_in), [out x in] row-major):
+      w_qk     [(Hq + Hkv) dh][E]      packed q / k down-projection
+      w_v      [Hkv dh][E]             value projection; with value_shift its first
+                                       Hkv dh / 2 rows are the current-token projection
+                                       and the rest the previous-token projection
+      conv_seq [(Hq + Hkv) dh][k_seq]  depth-wise sequence convolution (fan_in k_seq)
+      conv_ch  [(Hq + Hkv) dh][dh][k_ch] head-wise grouped convolution (fan_in dh k_ch)
+      w_o      [E][Hq dh]              output up-projection
+    Activations as for MLAConfig (child generator PCG64([seed, b + 1])).  The key
+    temperature beta is a fixed value of the workload (the page initialises it to 0).
+    """
+    name: str
+    batch: int
+    seq: int
+    d_model: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    num_conv_layers: int = 2
+    conv_kernel_seq: int = 4
+    conv_kernel_ch: int = 3
+    qk_mean: bool = True
+    value_shift: bool = True
+    beta: float = 0.25
+    dtype: str = "bf16"
+    rope_base: float = 10000.0
+    seed: int = 0
+
+    def replace(self, **kw) -> "CCAConfig":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def q_latent(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def kv_latent(self) -> int:
+        return self.n_kv_heads * self.head_dim
+
+    def weight_shapes(self) -> Dict[str, tuple]:
+        cp = self.q_latent + self.kv_latent
+        return {"w_qk": (cp, self.d_model), "w_v": (self.kv_latent, self.d_model),
+                "conv_seq": (cp, self.conv_kernel_seq),
+                "conv_ch": (cp, self.head_dim, self.conv_kernel_ch),
+                "w_o": (self.d_model, self.q_latent)}
+
+
+CCA_WEIGHT_ORDER = ("w_qk", "w_v", "conv_seq", "conv_ch", "w_o")
+
+# Workloads at the page's defaults: CCA with compression C = 4 (latent E/4) and CCGQA with
+# C1 = 2, C2 = 8 and a quarter of the heads as KV heads; two convolutions (k_seq 4, k_ch 3),
+# q-k-mean and value shift on.
+CCA_CONFIGS: Dict[str, CCAConfig] = {
+    "cca_tiny_fp32": CCAConfig("cca_tiny_fp32", batch=2, seq=9, d_model=16, n_heads=4, n_kv_heads=4,
+                               head_dim=4, dtype="f32", beta=0.3, seed=1011),
+    "ccgqa_tiny_fp32": CCAConfig("ccgqa_tiny_fp32", batch=2, seq=9, d_model=16, n_heads=4, n_kv_heads=2,
+                                 head_dim=4, dtype="f32", beta=0.3, seed=1012),
+    "cca": CCAConfig("cca", batch=4, seq=2048, d_model=2048, n_heads=16, n_kv_heads=16, head_dim=32,
+                     seed=1013),
+    "ccgqa": CCAConfig("ccgqa", batch=4, seq=2048, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=64,
+                       seed=1014),
+}
+
+
+@dataclasses.dataclass
+class CCAProblem:
+    cfg: CCAConfig
+    weights: Dict[str, np.ndarray]
+
+
+def make_cca_problem(cfg: CCAConfig) -> CCAProblem:
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    weights: Dict[str, np.ndarray] = {}
+    for name, shp in zip(CCA_WEIGHT_ORDER, (cfg.weight_shapes()[n] for n in CCA_WEIGHT_ORDER)):
+        fan_in = int(np.prod(shp[1:]))
+        w = rng.standard_normal(shp, dtype=np.float32)
+        w *= np.float32(1.0 / np.sqrt(fan_in))
+        weights[name] = _finish(w, cfg.dtype)
+    return CCAProblem(cfg, weights)
+
+
 def scaled(cfg: MLAConfig, **kw) -> MLAConfig:
     """Same family and structure at other sizes (for quick parity cases)."""
     return cfg.replace(**kw)
@@ -213,4 +301,5 @@ __all__ = [
     "MLAConfig", "CONFIGS", "Problem", "make_problem", "make_x", "make_x_batch",
     "round_bf16", "bf16_bits", "scaled", "host_threads", "WEIGHT_ORDER",
     "FAMILY_DECOUPLED", "FAMILY_FULLROPE", "FAMILY_MLRA",
+    "CCAConfig", "CCA_CONFIGS", "CCAProblem", "make_cca_problem", "CCA_WEIGHT_ORDER",
 ]
