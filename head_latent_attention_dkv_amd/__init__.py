@@ -4,7 +4,8 @@ Argument marshalling only: every step of the computation runs in the library's H
 kernels.  PyTorch supplies device memory (tensor data pointers) and the current HIP
 stream.  The entry points keep the C names: mla_validate, mla_workspace_bytes,
 mla_cache_append, mla_prefill, mla_prefill_chunk, mla_decode, mla_decode_attention,
-mla_prefill_attention, mla_status_str.
+mla_prefill_attention, mla_status_str, and for compressed convolutional attention
+mla_cca_validate, mla_cca_workspace_bytes, mla_cca_prefill.
 
 If the shared library is missing, loading raises -- there is no fallback path.
 """
@@ -50,11 +51,22 @@ class mla_cache(ctypes.Structure):
                 ("max_batch", ctypes.c_int32), ("max_seq", ctypes.c_int32)]
 
 
+class mla_cca_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("d_model", "n_heads", "n_kv_heads", "head_dim", "num_conv_layers", "conv_kernel_seq",
+                 "conv_kernel_ch", "qk_mean", "value_shift", "dtype")] + [("rope_base", ctypes.c_float)]
+
+
+class mla_cca_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_qk", "w_v", "w_o", "conv_seq", "conv_ch")] + \
+               [("key_temperature", ctypes.c_float)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ("mla_status_str", "mla_validate", "mla_workspace_bytes", "mla_cache_append",
            "mla_prefill", "mla_decode", "mla_decode_attention", "mla_prefill_attention",
-           "mla_prefill_chunk")
+           "mla_prefill_chunk", "mla_cca_validate", "mla_cca_workspace_bytes", "mla_cca_prefill")
 
 
 def lib() -> ctypes.CDLL:
@@ -88,6 +100,13 @@ def lib() -> ctypes.CDLL:
         L.mla_prefill_attention.argtypes = [D, W, vp, i32, i32, C, vp, vp, sz, vp]
         L.mla_prefill_chunk.restype = ctypes.c_int
         L.mla_prefill_chunk.argtypes = [D, W, vp, i32, i32, i32, C, vp, vp, sz, vp]
+        CD, CW = ctypes.POINTER(mla_cca_dims), ctypes.POINTER(mla_cca_weights)
+        L.mla_cca_validate.restype = ctypes.c_int
+        L.mla_cca_validate.argtypes = [CD]
+        L.mla_cca_workspace_bytes.restype = sz
+        L.mla_cca_workspace_bytes.argtypes = [CD, i32, i32]
+        L.mla_cca_prefill.restype = ctypes.c_int
+        L.mla_cca_prefill.argtypes = [CD, CW, vp, i32, i32, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -196,6 +215,32 @@ def mla_prefill_attention(dims, weights: mla_weights, q, B: int, S: int, cache: 
                                        int(ws_bytes), _stream(stream)), "mla_prefill_attention")
 
 
+def cca_dims_from_cfg(cfg) -> mla_cca_dims:
+    return mla_cca_dims(cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.num_conv_layers,
+                        cfg.conv_kernel_seq, cfg.conv_kernel_ch, int(cfg.qk_mean), int(cfg.value_shift),
+                        MLA_DTYPE_BF16 if cfg.dtype == "bf16" else MLA_DTYPE_F32, cfg.rope_base)
+
+
+def cca_weights_struct(w: Dict[str, object], key_temperature: float) -> mla_cca_weights:
+    return mla_cca_weights(*[_ptr(w.get(n)) for n in ("w_qk", "w_v", "w_o", "conv_seq", "conv_ch")],
+                           float(key_temperature))
+
+
+def mla_cca_validate(dims: mla_cca_dims) -> int:
+    return lib().mla_cca_validate(ctypes.byref(dims))
+
+
+def mla_cca_workspace_bytes(dims: mla_cca_dims, B: int, S: int) -> int:
+    return lib().mla_cca_workspace_bytes(ctypes.byref(dims), int(B), int(S))
+
+
+def mla_cca_prefill(dims, weights: mla_cca_weights, x, B: int, S: int, y, workspace, ws_bytes: int,
+                    stream=None) -> None:
+    _check(lib().mla_cca_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, S, _ptr(y),
+                                 _ptr(workspace), int(ws_bytes), _stream(stream)), "mla_cca_prefill")
+
+
 __all__ = [n for n in dir() if n.startswith(("mla_", "MLA_"))] + [
+    "cca_dims_from_cfg", "cca_weights_struct", 
     "lib", "make_dims", "dims_from_cfg", "weights_struct", "cache_struct", "MLAError",
     "LIB_PATH", "HEADER_PATH", "EXPORTS"]

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmla.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["mla_api.hip", "gemm.hip", "gemm_big.hip", "skinny.hip", "gemm_kmajor.hip", "decode.hip", "decode_fast.hip", "prefill.hip", "prefill_fast.hip"]
+SOURCES = ["mla_api.hip", "gemm.hip", "gemm_big.hip", "skinny.hip", "gemm_kmajor.hip", "decode.hip", "decode_fast.hip",
+           "prefill.hip", "prefill_fast.hip", "cca.hip", "cca_api.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

@@ -173,6 +173,8 @@ struct PrefillParams {
   int B, S, H, dn, d_rope, dv;   // S keys per sequence (positions 0 .. S-1)
   int T, q_off;             // queries per sequence and the position of the first (T = S, 0: prefill)
   float scale_log2;
+  int kv_group;             // query heads per key / value head (0 or 1: one each); keys and values
+                            // then hold H / kv_group heads and head h reads head h / kv_group
 };
 
 hipError_t launch_prefill(const PrefillParams& p, bool use_bf16, int dq_pad, int dv_pad, hipStream_t s);
@@ -193,6 +195,29 @@ struct FlashParams {
 bool prefill_fast_supported(int dn, int d_rope, int dv, int S);
 hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s);
 bool prefill_supported(bool use_bf16, int dq, int dv, int* dq_pad, int* dv_pad);
+
+// ---------------------------------------------------------------------------
+// Compressed convolutional attention (CCA / CCGQA): the step between the packed down-
+// projection and attention (causal convolutions, q-k-mean, value shift, QK L2-norm with the
+// key temperature, half-split RoPE in the latent)
+// ---------------------------------------------------------------------------
+struct CcaPrepParams {
+  const float* P;           // [B*S][(Hq + Hkv) dh] packed q | k projections (fp32)
+  const float* V;           // [B*S][Hkv dh] value projections, unshifted (fp32)
+  const void* conv_seq;     // [(Hq + Hkv) dh][kseq]      (element type of the layer)
+  const void* conv_ch;      // [(Hq + Hkv) dh][dh][kch]
+  void* q;                  // [B*S][Hq][dh]
+  void* k;                  // [B*S][Hkv][dh]
+  void* v;                  // [B*S][Hkv][dh]
+  int B, S, Hq, Hkv, dh;
+  int layers, kseq, kch;    // convolutions (0, 1 or 2) and their kernels
+  int qk_mean, value_shift;
+  float sqrt_dh, key_gain;  // sqrt(d_h) and exp(beta)
+  RopeTable rope;           // half-split frequencies of width d_h
+};
+constexpr int kCcaMaxKernel = 8;
+constexpr int kCcaMaxHeadDim = 128;
+hipError_t launch_cca_prep(const CcaPrepParams& p, bool use_bf16, hipStream_t s);
 
 int device_cu_count();
 

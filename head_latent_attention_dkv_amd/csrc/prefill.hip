@@ -84,7 +84,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const long long hdn = (long long)p.H * p.dn, hdv = (long long)p.H * p.dv;
+  // key / value head of this query head (grouped-query attention when kv_group > 1)
+  const int kvg = p.kv_group > 1 ? p.kv_group : 1;
+  const int hk = h / kvg;
+  const long long hdn = (long long)(p.H / kvg) * p.dn, hdv = (long long)(p.H / kvg) * p.dv;
   Chunk<T> st[C::BPW];
   auto load_tile = [&](int k0) {
 #pragma unroll
@@ -106,7 +109,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
       if (!isv) {
         if (c >= C::CK) continue;
         if (d < p.dn) {
-          src = Kg + ((long long)b * p.S + key) * hdn + (long long)h * p.dn + d;
+          src = Kg + ((long long)b * p.S + key) * hdn + (long long)hk * p.dn + d;
           nv = p.dn - d;
         } else if (d - p.dn < p.d_rope) {
           src = KRg + ((long long)b * p.kr_bstride + key) * p.d_rope + (d - p.dn);
@@ -115,7 +118,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
       } else {
         if (c >= C::CV) continue;
         if (d < p.dv) {
-          src = Vg + ((long long)b * p.S + key) * hdv + (long long)h * p.dv + d;
+          src = Vg + ((long long)b * p.S + key) * hdv + (long long)hk * p.dv + d;
           nv = p.dv - d;
         }
       }

@@ -235,6 +235,69 @@ mla_status mla_prefill_chunk(const mla_dims* dims, const mla_weights* w, const v
                              int32_t B, int32_t T, int32_t start_pos, const mla_cache* cache,
                              float* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Compressed convolutional attention (CCA) and its grouped-query form (CCGQA): a related
+ * latent method in which queries, keys and values are down-projected into a compressed
+ * latent and attention runs entirely inside it ([CCA page] frankenstein-transformer docs,
+ * ``latent/cca_attn``).  CCA is the case n_kv_heads == n_heads.
+ * ------------------------------------------------------------------------------------- */
+
+/* Layer dimensions ([CCA page] ``CCAAttention.__init__`` / ``CCGQAAttention.__init__``).
+ *   d_model          E, input / output width
+ *   n_heads          Hq, query heads
+ *   n_kv_heads       Hkv, key / value heads (divides Hq; = Hq for CCA)
+ *   head_dim         d_h, latent width per head (even: RoPE in the latent)
+ *   num_conv_layers  0, 1 (the depth-wise sequence convolution) or 2 (then the head-grouped one)
+ *   conv_kernel_seq  kernel of the sequence convolution; conv_kernel_ch of the grouped one
+ *   qk_mean          1: add the pre-convolution q-k mean to q and k
+ *   value_shift      1: the first half of the value channels from the current token, the
+ *                    second half from the previous token (Hkv even)
+ *   dtype            mla_dtype of x, weights and the attention operands
+ *   rope_base        RoPE base (10000 on the page) */
+typedef struct {
+  int32_t d_model, n_heads, n_kv_heads, head_dim;
+  int32_t num_conv_layers, conv_kernel_seq, conv_kernel_ch;
+  int32_t qk_mean, value_shift, dtype;
+  float rope_base;
+} mla_cca_dims;
+
+/* Weights, row-major [out][in] in the element type of dims (device pointers).
+ *   w_qk      [(Hq + Hkv) d_h][E]     packed q / k down-projection
+ *   w_v       [Hkv d_h][E]            value projection; with value_shift the current-token
+ *                                     projection's Hkv d_h / 2 rows, then the previous-token one's
+ *   w_o       [E][Hq d_h]             output up-projection
+ *   conv_seq  [(Hq + Hkv) d_h][k_seq] depth-wise convolution filters (used if num_conv_layers >= 1)
+ *   conv_ch   [(Hq + Hkv) d_h][d_h][k_ch] head-grouped convolution filters (if num_conv_layers == 2)
+ *   key_temperature  beta (host value): the normalised keys are scaled by exp(beta) */
+typedef struct {
+  const void *w_qk, *w_v, *w_o, *conv_seq, *conv_ch;
+  float key_temperature;
+} mla_cca_weights;
+
+/* Checks CCA dims.  Source: the ValueErrors of [CCA page] ``CCAAttention.__init__`` and
+ * ``CCGQAAttention.__init__`` (E divisible by the heads, Hkv dividing Hq, an even d_h, 0-2
+ * convolution layers, an even Hkv for value shift); kernel limits (the library's own):
+ * d_h <= 128 (<= 64 for MLA_DTYPE_F32), kernels 1..8.
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_SHAPE or MLA_ERR_UNSUPPORTED.  Host only. */
+mla_status mla_cca_validate(const mla_cca_dims* dims);
+
+/* Source: the library's own.  Workspace bytes mla_cca_prefill needs for B sequences of S
+ * tokens (0 for invalid arguments).  Host only. */
+size_t mla_cca_workspace_bytes(const mla_cca_dims* dims, int32_t B, int32_t S);
+
+/* Causal forward of B sequences of S tokens at positions 0..S-1.
+ * Source: [CCA page] ``CCAAttention.forward`` (n_kv_heads == n_heads) and
+ * ``CCGQAAttention.forward`` (query head h attends with key / value head h / (Hq / Hkv)), in
+ * decoder mode without dropout: packed down-projection, ``_apply_causal_convs``, q-k-mean,
+ * value shift, QK L2-norm with key temperature, half-split RoPE, causal softmax attention
+ * with scale d_h^-1/2, output up-projection.
+ *   x  [B][S][E]          y  [B][S][E] float32, fully overwritten
+ * Errors: as the validation, INVALID_ARG for missing pointers, WORKSPACE if ws_bytes is below
+ * mla_cca_workspace_bytes(dims, B, S), HIP for a failed launch. */
+mla_status mla_cca_prefill(const mla_cca_dims* dims, const mla_cca_weights* w, const void* x,
+                           int32_t B, int32_t S, float* y, void* workspace, size_t ws_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -170,3 +170,66 @@ def test_workspace_grows_with_problem():
     assert 0 < c < a <= b
     assert M.mla_workspace_bytes(d, 99, 64, 4096) == 0
     assert M.mla_workspace_bytes(d, M.MLA_OP_DECODE, 0, 4096) == 0
+
+
+# ---------------------------------------------------------------------------
+# Compressed convolutional attention entry points
+# ---------------------------------------------------------------------------
+def _cca(**kw):
+    base = dict(d_model=64, n_heads=4, n_kv_heads=2, head_dim=16, num_conv_layers=2, conv_kernel_seq=4,
+                conv_kernel_ch=3, qk_mean=1, value_shift=1, dtype=M.MLA_DTYPE_BF16, rope_base=10000.0)
+    base.update(kw)
+    return M.mla_cca_dims(*[base[f] for f, _ in M.mla_cca_dims._fields_])
+
+
+@pytest.mark.parametrize("name", list(S.CCA_CONFIGS))
+def test_cca_configs_validate(name):
+    _lib_or_skip()
+    cfg = S.CCA_CONFIGS[name]
+    d = M.cca_dims_from_cfg(cfg)
+    assert M.mla_cca_validate(d) == M.MLA_OK
+    assert M.mla_cca_workspace_bytes(d, cfg.batch, cfg.seq) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_model=66), M.MLA_ERR_SHAPE),                 # E not divisible by the heads
+    (dict(n_kv_heads=3), M.MLA_ERR_SHAPE),               # key heads do not divide query heads
+    (dict(head_dim=15), M.MLA_ERR_SHAPE),                # odd latent head width (RoPE)
+    (dict(num_conv_layers=3), M.MLA_ERR_SHAPE),          # 0, 1 or 2 convolutions
+    (dict(n_kv_heads=1), M.MLA_ERR_SHAPE),               # value shift needs an even key-head count
+    (dict(head_dim=256), M.MLA_ERR_UNSUPPORTED),
+    (dict(conv_kernel_seq=9), M.MLA_ERR_UNSUPPORTED),
+    (dict(n_heads=0), M.MLA_ERR_INVALID_ARG),
+    (dict(dtype=9), M.MLA_ERR_INVALID_ARG),
+])
+def test_cca_validate_rejects(kw, code):
+    _lib_or_skip()
+    assert M.mla_cca_validate(_cca(**kw)) == code
+
+
+def test_cca_validate_accepts_variants():
+    _lib_or_skip()
+    assert M.mla_cca_validate(_cca(n_kv_heads=1, value_shift=0)) == M.MLA_OK      # odd key heads, no shift
+    assert M.mla_cca_validate(_cca(num_conv_layers=0, conv_kernel_seq=0, conv_kernel_ch=0)) == M.MLA_OK
+    assert M.mla_cca_validate(_cca(n_kv_heads=4)) == M.MLA_OK                       # CCA
+
+
+def test_cca_prefill_errors_before_launch():
+    L = _lib_or_skip()
+    d = _cca()
+    w = M.mla_cca_weights(FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
+    n = M.mla_cca_workspace_bytes(d, 2, 8)
+    assert n > 0
+
+    def call(dims, wts, x=FAKE, B=2, S_=8, y=FAKE, ws=FAKE, nb=n):
+        return L.mla_cca_prefill(ctypes.byref(dims), ctypes.byref(wts) if wts is not None else None, x, B, S_, y,
+                                 ws, nb, None)
+
+    assert call(d, w, nb=n - 1) == M.MLA_ERR_WORKSPACE
+    assert call(d, w, ws=None) == M.MLA_ERR_WORKSPACE
+    assert call(d, w, x=None) == M.MLA_ERR_INVALID_ARG
+    assert call(d, None) == M.MLA_ERR_INVALID_ARG
+    assert call(d, M.mla_cca_weights(FAKE, FAKE, FAKE, None, FAKE, 0.0)) == M.MLA_ERR_INVALID_ARG   # conv filters
+    assert call(d, M.mla_cca_weights(FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"))) == M.MLA_ERR_INVALID_ARG
+    assert call(d, w, S_=0) == M.MLA_ERR_INVALID_ARG
+    assert call(_cca(head_dim=15), w) == M.MLA_ERR_SHAPE
