@@ -66,7 +66,8 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ("mla_status_str", "mla_validate", "mla_workspace_bytes", "mla_cache_append",
            "mla_prefill", "mla_decode", "mla_decode_attention", "mla_prefill_attention",
-           "mla_prefill_chunk", "mla_cca_validate", "mla_cca_workspace_bytes", "mla_cca_prefill")
+           "mla_prefill_chunk", "mla_cca_validate", "mla_cca_workspace_bytes", "mla_cca_prefill",
+           "mla_decode_attention_noalloc", "mla_decode_attention_noalloc_max_bytes")
 
 
 def lib() -> ctypes.CDLL:
@@ -100,6 +101,10 @@ def lib() -> ctypes.CDLL:
         L.mla_prefill_attention.argtypes = [D, W, vp, i32, i32, C, vp, vp, sz, vp]
         L.mla_prefill_chunk.restype = ctypes.c_int
         L.mla_prefill_chunk.argtypes = [D, W, vp, i32, i32, i32, C, vp, vp, sz, vp]
+        L.mla_decode_attention_noalloc.restype = ctypes.c_int
+        L.mla_decode_attention_noalloc.argtypes = [D, vp, vp, i32, vp, i32, C, vp, vp]
+        L.mla_decode_attention_noalloc_max_bytes.restype = sz
+        L.mla_decode_attention_noalloc_max_bytes.argtypes = []
         CD, CW = ctypes.POINTER(mla_cca_dims), ctypes.POINTER(mla_cca_weights)
         L.mla_cca_validate.restype = ctypes.c_int
         L.mla_cca_validate.argtypes = [CD]
@@ -206,6 +211,17 @@ def mla_decode_attention(dims, q_lat, q_rope, B: int, ctx_len, max_ctx: int, cac
                                       _ptr(ctx_len), int(max_ctx), ctypes.byref(cache), _ptr(z),
                                       _ptr(workspace), int(ws_bytes), _stream(stream)),
            "mla_decode_attention")
+
+
+def mla_decode_attention_noalloc(dims, q_lat, q_rope, B: int, ctx_len, max_ctx: int, cache: mla_cache, z,
+                                 stream=None) -> None:
+    _check(lib().mla_decode_attention_noalloc(ctypes.byref(dims), _ptr(q_lat), _ptr(q_rope), B, _ptr(ctx_len),
+                                              int(max_ctx), ctypes.byref(cache), _ptr(z), _stream(stream)),
+           "mla_decode_attention_noalloc")
+
+
+def mla_decode_attention_noalloc_max_bytes() -> int:
+    return int(lib().mla_decode_attention_noalloc_max_bytes())
 
 
 def mla_prefill_attention(dims, weights: mla_weights, q, B: int, S: int, cache: mla_cache, o,

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mla.h"
 #include "common.h"
 #include "internal.h"
@@ -528,6 +530,41 @@ DecodeParams decode_params(const mla_dims* d, const mla_cache* cache, const int3
   return p;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of mla_decode_attention_noalloc: a file-scope device array of fixed size, one copy
+// per GPU, held until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is a stand-in, not a device address): its address on each device comes
+// from hipGetSymbolAddress, taken once per device on the entry point's first call there.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (nullptr and *err set on failure).
+void* scratch_for_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !ptr) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // v[i] = value for i < n (a device array of per-sequence start positions)
 __global__ void fill_i32_kernel(int32_t* v, int n, int32_t value) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -772,6 +809,27 @@ mla_status mla_prefill_chunk(const mla_dims* d, const mla_weights* w, const void
   if (e != hipSuccess) return MLA_ERR_HIP;
   return hip_status(run_out_proj(d, w, o, B * T, y, st));
 }
+
+mla_status mla_decode_attention_noalloc(const mla_dims* d, const void* q_lat, const void* q_rope, int32_t B,
+                                        const int32_t* ctx_len_dev, int32_t max_ctx, const mla_cache* cache,
+                                        void* z, void* stream) {
+  // the same checks as mla_decode_attention, then the scratch size, all before any HIP call
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (d->rope_mode == MLA_ROPE_FULL_HALFSPLIT) return MLA_ERR_UNSUPPORTED;
+  if (!q_lat || !z || !ctx_len_dev || B <= 0 || max_ctx < 0) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope > 0 && !q_rope) return MLA_ERR_INVALID_ARG;
+  if ((s = check_cache(d, cache)) != MLA_OK) return s;
+  if (B > cache->max_batch || (long long)max_ctx + 1 > cache->max_seq) return MLA_ERR_CAPACITY;
+  const size_t need = decode_layout(d, B, max_ctx, true).total;
+  if (need > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+  hipError_t e;
+  void* ws = scratch_for_current_device(&e);
+  if (!ws) return MLA_ERR_HIP;
+  return mla_decode_attention(d, q_lat, q_rope, B, ctx_len_dev, max_ctx, cache, z, ws, need, stream);
+}
+
+size_t mla_decode_attention_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 mla_status mla_decode_attention(const mla_dims* d, const void* q_lat, const void* q_rope, int32_t B,
                                 const int32_t* ctx_len_dev, int32_t max_ctx, const mla_cache* cache,

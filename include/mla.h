@@ -205,6 +205,23 @@ mla_status mla_decode_attention(const mla_dims* dims, const void* q_lat, const v
                                 const mla_cache* cache, void* z,
                                 void* workspace, size_t ws_bytes, void* stream);
 
+/* mla_decode_attention for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no workspace argument.  Source: the
+ * library's own.  The split partials live in a fixed device array inside the library, one
+ * per GPU, of mla_decode_attention_noalloc_max_bytes() bytes (96 MiB), held from the first
+ * call on that GPU until the process ends.  Arguments, results and errors as
+ * mla_decode_attention, plus MLA_ERR_WORKSPACE (before any launch) when the shapes need more
+ * than that: mla_workspace_bytes(dims, MLA_OP_DECODE_ATTENTION, B, max_ctx) must not exceed it.
+ * Every call on one GPU shares that array: calls on one GPU that overlap in time (other
+ * streams, other threads) race; calls on different GPUs do not.  The call makes no
+ * allocation (no hipMalloc / hipFree). */
+mla_status mla_decode_attention_noalloc(const mla_dims* dims, const void* q_lat, const void* q_rope,
+                                        int32_t B, const int32_t* ctx_len_dev, int32_t max_ctx,
+                                        const mla_cache* cache, void* z, void* stream);
+
+/* Source: the library's own.  Size in bytes of mla_decode_attention_noalloc's per-GPU array. */
+size_t mla_decode_attention_noalloc_max_bytes(void);
+
 /* The attention core of prefill: explicit K/V up-projection of the cached latent rows
  * 0..S-1 ([DSV2 page] ``forward``: UK_proj / UV_proj of C_KV) and flash-style causal
  * attention over them.

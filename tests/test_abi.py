@@ -233,3 +233,22 @@ def test_cca_prefill_errors_before_launch():
     assert call(d, M.mla_cca_weights(FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"))) == M.MLA_ERR_INVALID_ARG
     assert call(d, w, S_=0) == M.MLA_ERR_INVALID_ARG
     assert call(_cca(head_dim=15), w) == M.MLA_ERR_SHAPE
+
+
+def test_noalloc_decode_attention_rejects_before_any_device_call():
+    """The no-allocation entry point checks its fixed scratch size on the host: a shape that
+    needs more is refused with MLA_ERR_WORKSPACE before anything touches a device."""
+    L = _lib_or_skip()
+    cfg = S.CONFIGS["dsv2_decode"]
+    d = M.dims_from_cfg(cfg)
+    cap = M.mla_decode_attention_noalloc_max_bytes()
+    assert cap == 96 << 20
+    assert M.mla_workspace_bytes(d, M.MLA_OP_DECODE_ATTENTION, 64, 4096) <= cap    # the decode workload fits
+    B, max_ctx = 512, 100
+    assert M.mla_workspace_bytes(d, M.MLA_OP_DECODE_ATTENTION, B, max_ctx) > cap
+    c = M.mla_cache(FAKE, FAKE, B, max_ctx + 1)
+    st = L.mla_decode_attention_noalloc(ctypes.byref(d), FAKE, FAKE, B, FAKE, max_ctx, ctypes.byref(c), FAKE, None)
+    assert st == M.MLA_ERR_WORKSPACE
+    c = M.mla_cache(FAKE, FAKE, B, max_ctx)                                           # capacity checked first
+    assert L.mla_decode_attention_noalloc(ctypes.byref(d), FAKE, FAKE, B, FAKE, max_ctx, ctypes.byref(c), FAKE,
+                                          None) == M.MLA_ERR_CAPACITY
