@@ -1,0 +1,184 @@
+"""fp64 CPU oracle for training the MLA layer: dropout forward and backward -- TEST INFRASTRUCTURE.
+
+Only the test suite and bench.py's CPU-baseline leg may import this module; the GPU library
+shares no code with it.
+
+Pages followed (cited by title and section):
+  [DSV2 page]  bird-of-paradise/deepseek-mla ``src/mla.py``: ``MultiHeadLatentAttention``
+               (``__init__`` takes a dropout probability, default 0.1; ``forward`` applies
+               dropout to the attention weights after the softmax and before the product
+               with the values).
+  [MLA page]   frankenstein-transformer docs, ``latent/mla_attn``: ``MLAAttention`` (the same
+               dropout on the attention weights of a trainable module).
+The layer is the decoupled-RoPE family of mla_oracle (query latent, rotary key shared by
+the heads); its forward is mla_oracle.forward with the attention weights P replaced by
+P * keep / (1 - p).
+
+Dropout draws come from Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator: the keep decision of
+attention weight (sequence b, head h, query i, key j) is
+    r = Philox4x64-10(counter = (j // 4, i, b H + h, 0), key = (seed, 0))[j % 4]
+    keep  <=>  (r >> 32) >= floor(p 2^32)
+so any element can be drawn on its own, in any order, on either side.
+
+The backward is the chain rule through that forward, written out step by step (reverse
+order of the forward).  With o = Pd v and Pd = P keep / (1 - p):
+    dPd = do v^T,  dv = Pd^T do,  dP = dPd keep / (1 - p),
+    ds = P (dP - rowsum(P dP)),  dq = tau ds k,  dk = tau ds^T q
+and rowsum(P dP) = rowsum(do o) (the dropout factors cancel).  The rotations are orthogonal,
+so their backward is the rotation by the negative angle.
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+
+from . import mla_oracle as O
+
+F64 = np.float64
+U64 = np.uint64
+_M32 = U64(0xFFFFFFFF)
+PHILOX_M = (U64(0xD2E7470EE14C6C93), U64(0xCA5A826395121157))   # round multipliers
+PHILOX_W = (U64(0x9E3779B97F4A7C15), U64(0xBB67AE8584CAA73B))   # key increments (Weyl)
+
+
+def _mulhilo(a: np.ndarray, b) -> tuple:
+    """Full 128-bit product of 64-bit words: (high, low) halves (numpy uint64 arrays)."""
+    a = np.asarray(a, dtype=U64)
+    b = U64(b)
+    a0, a1 = a & _M32, a >> U64(32)
+    b0, b1 = b & _M32, b >> U64(32)
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
+    mid = (p00 >> U64(32)) + (p01 & _M32) + (p10 & _M32)
+    hi = p11 + (p01 >> U64(32)) + (p10 >> U64(32)) + (mid >> U64(32))
+    return hi, a * b
+
+
+def philox4x64(c0, c1, c2, c3, k0, k1, rounds: int = 10):
+    """Philox4x64-R on arrays of counters (broadcast): ten rounds of two 64 x 64 -> 128-bit
+    products, the high halves xored with the other counter words and the key, the key
+    bumped by the Weyl constants between rounds."""
+    c0, c1, c2, c3 = (np.asarray(c, dtype=U64) for c in (c0, c1, c2, c3))
+    k0, k1 = U64(k0), U64(k1)
+    with np.errstate(over="ignore"):
+        for _ in range(rounds):
+            hi0, lo0 = _mulhilo(c0, PHILOX_M[0])
+            hi1, lo1 = _mulhilo(c2, PHILOX_M[1])
+            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+            k0, k1 = k0 + PHILOX_W[0], k1 + PHILOX_W[1]
+    return c0, c1, c2, c3
+
+
+def keep_threshold(p: float) -> int:
+    """A weight is kept when the upper 32 bits of its draw are >= floor(p 2^32)."""
+    if not (0.0 <= p < 1.0):
+        raise ValueError("dropout probability must be in [0, 1)")
+    return int(np.floor(p * 4294967296.0))
+
+
+def dropout_keep(seed: int, b: int, H: int, h: int, n_q: int, n_k: int, p: float) -> np.ndarray:
+    """Keep mask [n_q, n_k] of head h of sequence b (queries 0..n_q-1, keys 0..n_k-1)."""
+    i = np.arange(n_q, dtype=U64)[:, None]
+    j = np.arange(n_k, dtype=U64)[None, :]
+    words = philox4x64(j >> U64(2), i, U64(b * H + h), U64(0), U64(seed), U64(0))
+    sel = (j & U64(3)).astype(np.int64)
+    r = np.choose(np.broadcast_to(sel, (n_q, n_k)), [np.broadcast_to(w, (n_q, n_k)) for w in words])
+    return (r >> U64(32)) >= U64(keep_threshold(p))
+
+
+def _check_family(d: O.Dims):
+    if d.family != O.FAMILY_DECOUPLED or d.r_q <= 0 or d.d_rope <= 0:
+        raise ValueError("training oracle: decoupled-RoPE family with a query latent")
+
+
+def train_forward(x: np.ndarray, W: Dict[str, np.ndarray], d: O.Dims, p: float, seed: int, b: int):
+    """[DSV2 page] ``MultiHeadLatentAttention.forward`` with dropout p on the attention weights,
+    for sequence b of the batch (its index enters the dropout counter).  Returns (y, saved)."""
+    _check_family(d)
+    x = np.asarray(x, dtype=F64)
+    S, H, dn, dr = x.shape[0], d.n_heads, d.d_nope, d.d_rope
+    pos = np.arange(S)
+    Wf = {k: np.asarray(v, dtype=F64) for k, v in W.items()}
+    cq = x @ Wf["w_dq"].T
+    q_c = (cq @ Wf["w_uq"].T).reshape(S, H, dn)
+    q_r = O.rope_interleaved((cq @ Wf["w_qr"].T).reshape(S, H, dr), pos, d.rope_base)
+    c = x @ Wf["w_dkv"].T
+    k_r = O.rope_interleaved(x @ Wf["w_kr"].T, pos, d.rope_base)
+    k_c = (c @ Wf["w_uk"].T).reshape(S, H, dn)
+    v = (c @ Wf["w_uv"].T).reshape(S, H, dn)
+    q = np.concatenate([q_c, q_r], axis=-1)
+    k = np.concatenate([k_c, np.broadcast_to(k_r[:, None, :], (S, H, dr))], axis=-1)
+    tau = d.scale()
+    causal = pos[None, :] <= pos[:, None]
+    P = np.zeros((H, S, S))
+    keep = np.zeros((H, S, S), dtype=bool)
+    o = np.zeros((S, H, dn))
+    for h in range(H):
+        s = np.where(causal, tau * (q[:, h] @ k[:, h].T), -np.inf)
+        P[h] = O.softmax_last(s)
+        keep[h] = dropout_keep(seed, b, H, h, S, S, p)
+        o[:, h] = (P[h] * keep[h] / (1.0 - p)) @ v[:, h]
+    y = o.reshape(S, H * dn) @ Wf["w_o"].T
+    saved = dict(x=x, cq=cq, c=c, q=q, k=k, v=v, o=o, P=P, keep=keep, pos=pos)
+    return y, saved
+
+
+def train_backward(dy: np.ndarray, W: Dict[str, np.ndarray], d: O.Dims, p: float, saved) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dy * y) for the forward above: dx and one entry per weight."""
+    Wf = {k: np.asarray(v, dtype=F64) for k, v in W.items()}
+    dy = np.asarray(dy, dtype=F64)
+    x, cq, c, q, k, v, o, P, keep, pos = (saved[n] for n in ("x", "cq", "c", "q", "k", "v", "o", "P", "keep", "pos"))
+    S, H, dn, dr = x.shape[0], d.n_heads, d.d_nope, d.d_rope
+    tau = d.scale()
+    g: Dict[str, np.ndarray] = {}
+    # output projection y = o_cat W_o^T
+    o_cat = o.reshape(S, H * dn)
+    g["w_o"] = dy.T @ o_cat
+    do = (dy @ Wf["w_o"]).reshape(S, H, dn)
+    # attention, head by head
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(H):
+        Pd = P[h] * keep[h] / (1.0 - p)
+        dPd = do[:, h] @ v[:, h].T
+        dv[:, h] = Pd.T @ do[:, h]
+        dP = dPd * keep[h] / (1.0 - p)
+        ds = P[h] * (dP - np.sum(P[h] * dP, axis=1, keepdims=True))
+        dq[:, h] = tau * (ds @ k[:, h])
+        dk[:, h] = tau * (ds.T @ q[:, h])
+    # split of q and k into their decompressed and rotary parts
+    dq_c, dq_r = dq[..., :dn], dq[..., dn:]
+    dk_c, dk_r = dk[..., :dn], dk[..., dn:].sum(axis=1)       # k_R is shared by the heads
+    dq_r0 = O.rope_interleaved(dq_r, -pos, d.rope_base)        # rotation by the negative angle
+    dk_r0 = O.rope_interleaved(dk_r, -pos, d.rope_base)
+    dq_c, dq_r0 = dq_c.reshape(S, H * dn), dq_r0.reshape(S, H * dr)
+    dk_c, dv = dk_c.reshape(S, H * dn), dv.reshape(S, H * dn)
+    # query path
+    g["w_uq"] = dq_c.T @ cq
+    g["w_qr"] = dq_r0.T @ cq
+    dcq = dq_c @ Wf["w_uq"] + dq_r0 @ Wf["w_qr"]
+    g["w_dq"] = dcq.T @ x
+    # key / value path
+    g["w_uk"] = dk_c.T @ c
+    g["w_uv"] = dv.T @ c
+    dc = dk_c @ Wf["w_uk"] + dv @ Wf["w_uv"]
+    g["w_dkv"] = dc.T @ x
+    g["w_kr"] = dk_r0.T @ x
+    g["x"] = dcq @ Wf["w_dq"] + dc @ Wf["w_dkv"] + dk_r0 @ Wf["w_kr"]
+    return g
+
+
+def lse_log2(saved, d: O.Dims) -> np.ndarray:
+    """log2 of each softmax row's normaliser sum_j exp(s_ij) (scores in natural units), [H, S]:
+    the per-row statistic a flash forward keeps for its backward."""
+    q, k, pos = saved["q"], saved["k"], saved["pos"]
+    S, H = q.shape[0], q.shape[1]
+    out = np.zeros((H, S))
+    causal = pos[None, :] <= pos[:, None]
+    for h in range(H):
+        s = np.where(causal, d.scale() * (q[:, h] @ k[:, h].T), -np.inf)
+        m = s.max(axis=1)
+        out[h] = (m + np.log(np.exp(s - m[:, None]).sum(axis=1))) / np.log(2.0)
+    return out
