@@ -67,7 +67,14 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTS = ("mla_status_str", "mla_validate", "mla_workspace_bytes", "mla_cache_append",
            "mla_prefill", "mla_decode", "mla_decode_attention", "mla_prefill_attention",
            "mla_prefill_chunk", "mla_cca_validate", "mla_cca_workspace_bytes", "mla_cca_prefill",
-           "mla_decode_attention_noalloc", "mla_decode_attention_noalloc_max_bytes")
+           "mla_decode_attention_noalloc", "mla_decode_attention_noalloc_max_bytes", "mla_train_saved_bytes",
+           "mla_train_workspace_bytes", "mla_train_forward", "mla_train_backward")
+
+GRAD_ORDER = ("dx", "dw_dq", "dw_uq", "dw_qr", "dw_dkv", "dw_kr", "dw_uk", "dw_uv", "dw_o")
+
+
+class mla_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_ORDER]
 
 
 def lib() -> ctypes.CDLL:
@@ -105,6 +112,15 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_attention_noalloc.argtypes = [D, vp, vp, i32, vp, i32, C, vp, vp]
         L.mla_decode_attention_noalloc_max_bytes.restype = sz
         L.mla_decode_attention_noalloc_max_bytes.argtypes = []
+        L.mla_train_saved_bytes.restype = sz
+        L.mla_train_saved_bytes.argtypes = [D, i32, i32]
+        L.mla_train_workspace_bytes.restype = sz
+        L.mla_train_workspace_bytes.argtypes = [D, i32, i32]
+        u64, f32 = ctypes.c_uint64, ctypes.c_float
+        L.mla_train_forward.restype = ctypes.c_int
+        L.mla_train_forward.argtypes = [D, W, vp, i32, i32, f32, u64, vp, vp, sz, vp]
+        L.mla_train_backward.restype = ctypes.c_int
+        L.mla_train_backward.argtypes = [D, W, vp, i32, i32, f32, u64, vp, vp, sz, ctypes.POINTER(mla_grads), vp, sz, vp]
         CD, CW = ctypes.POINTER(mla_cca_dims), ctypes.POINTER(mla_cca_weights)
         L.mla_cca_validate.restype = ctypes.c_int
         L.mla_cca_validate.argtypes = [CD]
@@ -231,6 +247,32 @@ def mla_prefill_attention(dims, weights: mla_weights, q, B: int, S: int, cache: 
                                        int(ws_bytes), _stream(stream)), "mla_prefill_attention")
 
 
+def mla_train_saved_bytes(dims, B: int, S: int) -> int:
+    return int(lib().mla_train_saved_bytes(ctypes.byref(dims), int(B), int(S)))
+
+
+def mla_train_workspace_bytes(dims, B: int, S: int) -> int:
+    return int(lib().mla_train_workspace_bytes(ctypes.byref(dims), int(B), int(S)))
+
+
+def mla_train_forward(dims, weights: mla_weights, x, B: int, S: int, dropout_p: float, seed: int, y, saved,
+                      saved_bytes: int, stream=None) -> None:
+    _check(lib().mla_train_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, S, float(dropout_p),
+                                   int(seed), _ptr(y), _ptr(saved), int(saved_bytes), _stream(stream)),
+           "mla_train_forward")
+
+
+def grads_struct(g: Dict[str, object]) -> mla_grads:
+    return mla_grads(*[_ptr(g.get(n)) for n in GRAD_ORDER])
+
+
+def mla_train_backward(dims, weights: mla_weights, x, B: int, S: int, dropout_p: float, seed: int, dy, saved,
+                       saved_bytes: int, grads: mla_grads, workspace, ws_bytes: int, stream=None) -> None:
+    _check(lib().mla_train_backward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, S, float(dropout_p),
+                                    int(seed), _ptr(dy), _ptr(saved), int(saved_bytes), ctypes.byref(grads),
+                                    _ptr(workspace), int(ws_bytes), _stream(stream)), "mla_train_backward")
+
+
 def cca_dims_from_cfg(cfg) -> mla_cca_dims:
     return mla_cca_dims(cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.num_conv_layers,
                         cfg.conv_kernel_seq, cfg.conv_kernel_ch, int(cfg.qk_mean), int(cfg.value_shift),
@@ -257,6 +299,6 @@ def mla_cca_prefill(dims, weights: mla_cca_weights, x, B: int, S: int, y, worksp
 
 
 __all__ = [n for n in dir() if n.startswith(("mla_", "MLA_"))] + [
-    "cca_dims_from_cfg", "cca_weights_struct", 
+    "cca_dims_from_cfg", "cca_weights_struct", "grads_struct", "GRAD_ORDER", 
     "lib", "make_dims", "dims_from_cfg", "weights_struct", "cache_struct", "MLAError",
     "LIB_PATH", "HEADER_PATH", "EXPORTS"]

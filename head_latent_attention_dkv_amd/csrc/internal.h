@@ -175,6 +175,12 @@ struct PrefillParams {
   float scale_log2;
   int kv_group;             // query heads per key / value head (0 or 1: one each); keys and values
                             // then hold H / kv_group heads and head h reads head h / kv_group
+  // training: dropout of the attention weights (keep_thr = 0: none) and the per-row log2
+  // normaliser lse[(b H + h) T + i] = log2 sum_j exp2(scale_log2 s_ij) (lse NULL: not written)
+  uint32_t keep_thr;        // floor(p 2^32)
+  float keep_scale;         // 1 / (1 - p)
+  unsigned long long seed;
+  float* lse;
 };
 
 hipError_t launch_prefill(const PrefillParams& p, bool use_bf16, int dq_pad, int dv_pad, hipStream_t s);
@@ -218,6 +224,47 @@ struct CcaPrepParams {
 constexpr int kCcaMaxKernel = 8;
 constexpr int kCcaMaxHeadDim = 128;
 hipError_t launch_cca_prep(const CcaPrepParams& p, bool use_bf16, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Training backward
+// ---------------------------------------------------------------------------
+// C[z] = alpha A[z] B[z] + beta C[z] for Z batches (z = z0 zdiv + z1), element (m, k) of A at
+// A + z0 sAz0 + z1 sAz1 + m sAm + k sAk (likewise B (k, n), C (m, n)); A and B fp32 (x_f32 = 1)
+// or bf16; products on the MFMA of the launch's element type, fp32 accumulation, fp32 C.
+struct SgemmParams {
+  const void* A;
+  const void* B;
+  float* C;
+  int M, N, K, Z, zdiv;
+  long long sAm, sAk, sBk, sBn, sCm, sCn;
+  long long sAz0, sAz1, sBz0, sBz1, sCz0, sCz1;
+  int a_f32, b_f32;
+  float alpha, beta;
+};
+hipError_t launch_sgemm(const SgemmParams& p, bool use_bf16, hipStream_t s);
+
+// One query block of the attention backward (queries i0 .. i0+Tq-1 against keys 0 .. Kn-1,
+// for the Z = B H (sequence, head) pairs): [z][Tq][Kn] buffers.
+struct AttnBwdParams {
+  const float* S_;          // scores (bwd_p) or dPd (bwd_ds), fp32
+  void* P;                  // softmax weights (element type)
+  void* Pd;                 // dropped-out weights (element type)
+  void* dS;                 // score gradients times the softmax scale (element type)
+  const float* lse;         // [z][S] log2 normalisers from the forward
+  const float* D;           // [z][S] rowsum(dO o)
+  int Z, S, i0, Tq, Kn;
+  float scale_log2, scale;  // softmax scale times log2(e), and the softmax scale
+  uint32_t keep_thr;
+  float keep_scale;
+  unsigned long long seed;
+};
+hipError_t launch_bwd_p(const AttnBwdParams& p, bool use_bf16, hipStream_t s);
+hipError_t launch_bwd_ds(const AttnBwdParams& p, bool use_bf16, hipStream_t s);
+hipError_t launch_rowdot(const float* dO, const void* o, float* D, int B, int S, int H, int dv, bool use_bf16,
+                         hipStream_t s);
+hipError_t launch_rope_bwd(const float* dqr, const float* dkr, float* dqr0, float* dkr0, int B, int S, int H, int dr,
+                           const RopeTable& rope, hipStream_t s);
+hipError_t launch_fill_f32(float* p, long long n, float v, hipStream_t s);
 
 int device_cu_count();
 

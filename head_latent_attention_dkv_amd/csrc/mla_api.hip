@@ -914,3 +914,303 @@ mla_status mla_decode(const mla_dims* d, const mla_weights* w, const void* x, in
 }
 
 }  // extern "C"
+
+// ===========================================================================================
+// Training: forward with dropout on the attention weights, and its backward ([DSV2 page]
+// MultiHeadLatentAttention, [MLA page] MLAAttention: trainable modules with dropout after the
+// softmax).  Decoupled-RoPE family with a query latent.
+// ===========================================================================================
+namespace {
+
+struct TrainSaved {
+  size_t cq, q, c, kr, kc, v, o, lse, total;
+};
+
+TrainSaved train_saved_layout(const mla_dims* d, int B, int S) {
+  TrainSaved t{};
+  const size_t rows = (size_t)B * S, es = esize(d);
+  const int H = d->n_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  t.cq = take(rows * d->r_q * es);
+  t.q = take(rows * H * dq_of(d) * es);
+  t.c = take(rows * d->r_kv * es);
+  t.kr = take(rows * d->d_rope * es);
+  t.kc = take(rows * H * d->d_nope * es);
+  t.v = take(rows * H * d->d_v * es);
+  t.o = take(rows * H * d->d_v * es);
+  t.lse = take((size_t)B * H * S * 4);
+  t.total = off;
+  return t;
+}
+
+// Queries per block of the attention backward: at most 256, and the [B H][Tq][S] fp32 score
+// block within ~2 GiB.
+int train_query_block(const mla_dims* d, int B, int S) {
+  const long long z = (long long)B * d->n_heads;
+  long long tq = (2ll << 30) / (4ll * z * S);
+  tq = tq >= 64 ? tq / 64 * 64 : (tq < 1 ? 1 : tq);
+  if (tq > 256) tq = 256;
+  return (int)(tq < S ? tq : S);
+}
+
+struct TrainWs {
+  size_t dO, D, dqc, dqr, dkc, dkr, dv, dqr0, dkr0, dcq, dc, sbuf, pbuf, pdbuf, dsbuf, total;
+  int tq;
+};
+
+TrainWs train_ws_layout(const mla_dims* d, int B, int S) {
+  TrainWs w{};
+  const size_t rows = (size_t)B * S, es = esize(d);
+  const int H = d->n_heads, dn = d->d_nope, dr = d->d_rope, dv = d->d_v;
+  w.tq = train_query_block(d, B, S);
+  const size_t blk = (size_t)B * H * w.tq * S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  w.dO = take(rows * H * dv * 4);
+  w.D = take((size_t)B * H * S * 4);
+  w.dqc = take(rows * H * dn * 4);
+  w.dqr = take(rows * H * dr * 4);
+  w.dkc = take(rows * H * dn * 4);
+  w.dkr = take(rows * H * dr * 4);
+  w.dv = take(rows * H * dv * 4);
+  w.dqr0 = take(rows * H * dr * 4);
+  w.dkr0 = take(rows * dr * 4);
+  w.dcq = take(rows * d->r_q * 4);
+  w.dc = take(rows * d->r_kv * 4);
+  w.sbuf = take(blk * 4);
+  w.pbuf = take(blk * es);
+  w.pdbuf = take(blk * es);
+  w.dsbuf = take(blk * es);
+  w.total = off;
+  return w;
+}
+
+mla_status train_check(const mla_dims* d, float p) {
+  mla_status s = mla_validate(d);
+  if (s != MLA_OK) return s;
+  if (d->rope_mode != MLA_ROPE_DECOUPLED_INTERLEAVED || d->r_q <= 0 || d->n_latent_heads != 1) return MLA_ERR_UNSUPPORTED;
+  if (!(p >= 0.f && p < 1.f)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+uint32_t keep_threshold(float p) {
+  const double t = floor((double)p * 4294967296.0);
+  return t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+}
+
+// one strided product (batch 1) of the backward
+SgemmParams sg(const void* A, bool a_f32, long long sAm, long long sAk, const void* Bm, bool b_f32, long long sBk,
+               long long sBn, float* C, long long sCm, int M, int N, int K, float beta) {
+  SgemmParams g;
+  memset(&g, 0, sizeof(g));
+  g.A = A;
+  g.B = Bm;
+  g.C = C;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.Z = 1;
+  g.zdiv = 1;
+  g.sAm = sAm;
+  g.sAk = sAk;
+  g.sBk = sBk;
+  g.sBn = sBn;
+  g.sCm = sCm;
+  g.sCn = 1;
+  g.a_f32 = a_f32 ? 1 : 0;
+  g.b_f32 = b_f32 ? 1 : 0;
+  g.alpha = 1.f;
+  g.beta = beta;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_train_saved_bytes(const mla_dims* d, int32_t B, int32_t S) {
+  if (train_check(d, 0.f) != MLA_OK || B <= 0 || S <= 0) return 0;
+  return train_saved_layout(d, B, S).total;
+}
+
+size_t mla_train_workspace_bytes(const mla_dims* d, int32_t B, int32_t S) {
+  if (train_check(d, 0.f) != MLA_OK || B <= 0 || S <= 0) return 0;
+  return train_ws_layout(d, B, S).total;
+}
+
+mla_status mla_train_forward(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t S,
+                             float dropout_p, uint64_t seed, float* y, void* saved, size_t saved_bytes, void* stream) {
+  mla_status s = train_check(d, dropout_p);
+  if (s != MLA_OK) return s;
+  if (!x || !y || B <= 0 || S <= 0) return MLA_ERR_INVALID_ARG;
+  if ((s = check_weights(d, w, true, true, true)) != MLA_OK) return s;
+  const TrainSaved sv = train_saved_layout(d, B, S);
+  if (!saved || saved_bytes < sv.total) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int M = B * S;
+  if (run_queries(d, w, x, M, S, nullptr, at(saved, sv.cq), at(saved, sv.q), st) != hipSuccess) return MLA_ERR_HIP;
+  if (run_latent(d, w, x, B, S, nullptr, nullptr, at(saved, sv.c), at(saved, sv.kr), st) != hipSuccess) return MLA_ERR_HIP;
+  if (run_kv_up(d, w, at(saved, sv.c), false, 0, B, S, at(saved, sv.kc), at(saved, sv.v), st, false) != hipSuccess)
+    return MLA_ERR_HIP;
+  int dqp, dvp;
+  if (!prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp)) return MLA_ERR_UNSUPPORTED;
+  PrefillParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.q = at(saved, sv.q);
+  pp.k = at(saved, sv.kc);
+  pp.kr = at(saved, sv.kr);
+  pp.kr_bstride = S;
+  pp.v = at(saved, sv.v);
+  pp.o = at(saved, sv.o);
+  pp.B = B;
+  pp.S = S;
+  pp.T = S;
+  pp.H = d->n_heads;
+  pp.dn = d->d_nope;
+  pp.d_rope = d->d_rope;
+  pp.dv = d->d_v;
+  pp.scale_log2 = softmax_scale(d) * kLog2e;
+  pp.keep_thr = keep_threshold(dropout_p);
+  pp.keep_scale = (float)(1.0 / (1.0 - (double)dropout_p));
+  pp.seed = seed;
+  pp.lse = reinterpret_cast<float*>(at(saved, sv.lse));
+  if (launch_prefill(pp, is_bf16(d), dqp, dvp, st) != hipSuccess) return MLA_ERR_HIP;
+  return hip_status(run_out_proj(d, w, at(saved, sv.o), M, y, st));
+}
+
+mla_status mla_train_backward(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t S,
+                              float dropout_p, uint64_t seed, const float* dy, const void* saved, size_t saved_bytes,
+                              const mla_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  mla_status s = train_check(d, dropout_p);
+  if (s != MLA_OK) return s;
+  if (!x || !dy || !g || B <= 0 || S <= 0) return MLA_ERR_INVALID_ARG;
+  if (!g->dx || !g->dw_dq || !g->dw_uq || !g->dw_qr || !g->dw_dkv || !g->dw_kr || !g->dw_uk || !g->dw_uv || !g->dw_o)
+    return MLA_ERR_INVALID_ARG;
+  if ((s = check_weights(d, w, true, true, true)) != MLA_OK) return s;
+  const TrainSaved sv = train_saved_layout(d, B, S);
+  if (!saved || saved_bytes < sv.total) return MLA_ERR_WORKSPACE;
+  const TrainWs lw = train_ws_layout(d, B, S);
+  if (!ws || ws_bytes < lw.total) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = is_bf16(d);
+  const size_t es = esize(d);
+  const int H = d->n_heads, dn = d->d_nope, dr = d->d_rope, dv = d->d_v, dq = dq_of(d);
+  const int E = d->d_model, rq = d->r_q, rkv = d->r_kv;
+  const int M = B * S;
+  const long long HD = (long long)H * dn, HR = (long long)H * dr, HV = (long long)H * dv, HQ = (long long)H * dq;
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(at(ws, off)); };
+  const char* sd = static_cast<const char*>(saved);
+  const void *cq = sd + sv.cq, *q = sd + sv.q, *c = sd + sv.c, *kr = sd + sv.kr, *kc = sd + sv.kc;
+  const void *v = sd + sv.v, *o = sd + sv.o;
+  const float* lse = reinterpret_cast<const float*>(sd + sv.lse);
+  float *dO = F(lw.dO), *D = F(lw.D), *dqc = F(lw.dqc), *dqr = F(lw.dqr), *dkc = F(lw.dkc), *dkr = F(lw.dkr);
+  float *dV = F(lw.dv), *dqr0 = F(lw.dqr0), *dkr0 = F(lw.dkr0), *dcq = F(lw.dcq), *dc = F(lw.dc);
+#define MLA_TRY(expr) \
+  do {                \
+    if ((expr) != hipSuccess) return MLA_ERR_HIP; \
+  } while (0)
+  auto GEMM = [&](const SgemmParams& p) { return launch_sgemm(p, bf, st); };
+  const bool tf = !bf;   // storage flag of weights and saved tensors: fp32 when the layer is fp32
+
+  // output projection y = o W_o^T:  dW_o = dy^T o,  dO = dy W_o
+  MLA_TRY(GEMM(sg(dy, true, 1, E, o, tf, HV, 1, g->dw_o, HV, E, (int)HV, M, 0.f)));
+  MLA_TRY(GEMM(sg(dy, true, E, 1, w->w_o, tf, HV, 1, dO, HV, M, (int)HV, E, 0.f)));
+  MLA_TRY(launch_rowdot(dO, o, D, B, S, H, dv, bf, st));
+  MLA_TRY(launch_fill_f32(dkc, (long long)M * HD, 0.f, st));
+  MLA_TRY(launch_fill_f32(dkr, (long long)M * HR, 0.f, st));
+  MLA_TRY(launch_fill_f32(dV, (long long)M * HV, 0.f, st));
+
+  // attention, one block of queries at a time for every (sequence, head) pair z = b H + h
+  const int tq = lw.tq;
+  const float tau = softmax_scale(d);
+  AttnBwdParams ab;
+  memset(&ab, 0, sizeof(ab));
+  ab.S_ = F(lw.sbuf);
+  ab.P = at(ws, lw.pbuf);
+  ab.Pd = at(ws, lw.pdbuf);
+  ab.dS = at(ws, lw.dsbuf);
+  ab.lse = lse;
+  ab.D = D;
+  ab.Z = B * H;
+  ab.S = S;
+  ab.scale_log2 = tau * kLog2e;
+  ab.scale = tau;
+  ab.keep_thr = keep_threshold(dropout_p);
+  ab.keep_scale = (float)(1.0 / (1.0 - (double)dropout_p));
+  ab.seed = seed;
+  // batched operand views: a [rows][H][width] tensor has batch strides (S H width, width)
+  auto batched = [&](SgemmParams p, long long az0, long long az1, long long bz0, long long bz1, long long cz0,
+                     long long cz1) {
+    p.Z = B * H;
+    p.zdiv = H;
+    p.sAz0 = az0;
+    p.sAz1 = az1;
+    p.sBz0 = bz0;
+    p.sBz1 = bz1;
+    p.sCz0 = cz0;
+    p.sCz1 = cz1;
+    return p;
+  };
+  for (int i0 = 0; i0 < S; i0 += tq) {
+    const int T = S - i0 < tq ? S - i0 : tq;          // queries of this block
+    const int Kn = i0 + T;                            // keys they can see
+    const long long blk = (long long)tq * Kn;         // [Tq][Kn] block of one (sequence, head)
+    const char* qb = static_cast<const char*>(q) + (size_t)i0 * HQ * es;
+    ab.i0 = i0;
+    ab.Tq = tq;
+    ab.Kn = Kn;
+    // scores S = q_C k_C^T + q_R k_R^T (unscaled)
+    MLA_TRY(GEMM(batched(sg(qb, tf, HQ, 1, kc, tf, 1, HD, F(lw.sbuf), Kn, T, Kn, dn, 0.f),
+                         (long long)S * HQ, dq, (long long)S * HD, dn, (long long)H * blk, blk)));
+    MLA_TRY(GEMM(batched(sg(static_cast<const char*>(qb) + (size_t)dn * es, tf, HQ, 1, kr, tf, 1, dr, F(lw.sbuf), Kn,
+                            T, Kn, dr, 1.f),
+                         (long long)S * HQ, dq, (long long)S * dr, 0, (long long)H * blk, blk)));
+    MLA_TRY(launch_bwd_p(ab, bf, st));
+    // dV[0:Kn] += Pd^T dO_blk
+    const float* dOb = dO + (size_t)i0 * HV;
+    MLA_TRY(GEMM(batched(sg(ab.Pd, tf, 1, Kn, dOb, true, HV, 1, dV, HV, Kn, dv, T, 1.f), (long long)H * blk, blk,
+                         (long long)S * HV, dv, (long long)S * HV, dv)));
+    // dPd = dO_blk V^T  (into the score buffer)
+    MLA_TRY(GEMM(batched(sg(dOb, true, HV, 1, v, tf, 1, HV, F(lw.sbuf), Kn, T, Kn, dv, 0.f), (long long)S * HV, dv,
+                         (long long)S * HV, dv, (long long)H * blk, blk)));
+    MLA_TRY(launch_bwd_ds(ab, bf, st));
+    // dq_blk = dS k:  decompressed part and rotary part (k_R shared by the heads)
+    MLA_TRY(GEMM(batched(sg(ab.dS, tf, Kn, 1, kc, tf, HD, 1, dqc + (size_t)i0 * HD, HD, T, dn, Kn, 0.f),
+                         (long long)H * blk, blk, (long long)S * HD, dn, (long long)S * HD, dn)));
+    MLA_TRY(GEMM(batched(sg(ab.dS, tf, Kn, 1, kr, tf, dr, 1, dqr + (size_t)i0 * HR, HR, T, dr, Kn, 0.f),
+                         (long long)H * blk, blk, (long long)S * dr, 0, (long long)S * HR, dr)));
+    // dk[0:Kn] += dS^T q_blk (per head; the rotary parts are summed over heads below)
+    MLA_TRY(GEMM(batched(sg(ab.dS, tf, 1, Kn, qb, tf, HQ, 1, dkc, HD, Kn, dn, T, 1.f), (long long)H * blk, blk,
+                         (long long)S * HQ, dq, (long long)S * HD, dn)));
+    MLA_TRY(GEMM(batched(sg(ab.dS, tf, 1, Kn, static_cast<const char*>(qb) + (size_t)dn * es, tf, HQ, 1, dkr, HR,
+                            Kn, dr, T, 1.f),
+                         (long long)H * blk, blk, (long long)S * HQ, dq, (long long)S * HR, dr)));
+  }
+
+  // rotary parts back through the rotations (negative angle); k_R summed over heads
+  RopeTable rope;
+  make_rope_table(&rope, dr, d->rope_base);
+  MLA_TRY(launch_rope_bwd(dqr, dkr, dqr0, dkr0, B, S, H, dr, rope, st));
+  // query path: q_C = c_Q W_UQ^T, q_R0 = c_Q W_QR^T, c_Q = x W_DQ^T
+  MLA_TRY(GEMM(sg(dqc, true, 1, HD, cq, tf, rq, 1, g->dw_uq, rq, (int)HD, rq, M, 0.f)));
+  MLA_TRY(GEMM(sg(dqr0, true, 1, HR, cq, tf, rq, 1, g->dw_qr, rq, (int)HR, rq, M, 0.f)));
+  MLA_TRY(GEMM(sg(dqc, true, HD, 1, w->w_uq, tf, rq, 1, dcq, rq, M, rq, (int)HD, 0.f)));
+  MLA_TRY(GEMM(sg(dqr0, true, HR, 1, w->w_qr, tf, rq, 1, dcq, rq, M, rq, (int)HR, 1.f)));
+  MLA_TRY(GEMM(sg(dcq, true, 1, rq, x, tf, E, 1, g->dw_dq, E, rq, E, M, 0.f)));
+  // key / value path: k_C = c W_UK^T, v = c W_UV^T, c = x W_DKV^T, k_R0 = x W_KR^T
+  MLA_TRY(GEMM(sg(dkc, true, 1, HD, c, tf, rkv, 1, g->dw_uk, rkv, (int)HD, rkv, M, 0.f)));
+  MLA_TRY(GEMM(sg(dV, true, 1, HV, c, tf, rkv, 1, g->dw_uv, rkv, (int)HV, rkv, M, 0.f)));
+  MLA_TRY(GEMM(sg(dkc, true, HD, 1, w->w_uk, tf, rkv, 1, dc, rkv, M, rkv, (int)HD, 0.f)));
+  MLA_TRY(GEMM(sg(dV, true, HV, 1, w->w_uv, tf, rkv, 1, dc, rkv, M, rkv, (int)HV, 1.f)));
+  MLA_TRY(GEMM(sg(dc, true, 1, rkv, x, tf, E, 1, g->dw_dkv, E, rkv, E, M, 0.f)));
+  MLA_TRY(GEMM(sg(dkr0, true, 1, dr, x, tf, E, 1, g->dw_kr, E, dr, E, M, 0.f)));
+  // dx = dc_Q W_DQ + dc W_DKV + dk_R0 W_KR
+  MLA_TRY(GEMM(sg(dcq, true, rq, 1, w->w_dq, tf, E, 1, g->dx, E, M, E, rq, 0.f)));
+  MLA_TRY(GEMM(sg(dc, true, rkv, 1, w->w_dkv, tf, E, 1, g->dx, E, M, E, rkv, 1.f)));
+  MLA_TRY(GEMM(sg(dkr0, true, dr, 1, w->w_kr, tf, E, 1, g->dx, E, M, E, dr, 1.f)));
+#undef MLA_TRY
+  return MLA_OK;
+}
+
+}  // extern "C"

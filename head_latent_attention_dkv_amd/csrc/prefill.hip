@@ -195,6 +195,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
         ps += pv[i];
       }
       l_run += ps;
+      if (p.keep_thr) {
+        // dropout after the softmax: the normaliser keeps every weight, the value product
+        // only the kept ones, scaled by 1 / (1 - p).  A lane's keys come in aligned runs of
+        // four (keys 8 (i/4) + 4 half + i%4 of each 32-key block): one draw per run.
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int key4 = k0 + (r >> 2) * 32 + 8 * (r & 3) + 4 * half;
+          const unsigned bits = dropout_keep4(p.seed, p.keep_thr, key4 >> 2, qabs, b * p.H + h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[4 * r + e] = ((bits >> e) & 1u) ? pv[4 * r + e] * p.keep_scale : 0.f;
+        }
+      }
       Frag<T> pf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) pf[ks] = frag_from_f32<T>(pv + 8 * ks);
@@ -214,6 +226,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
   const float l_tot = wave_sum32(l_run);
   if (query >= p.T) return;
   const float inv = 1.f / l_tot;
+  if (p.lse && half == 0) p.lse[((long long)b * p.H + h) * p.T + query] = m_run + log2f(l_tot);
   T* O = reinterpret_cast<T*>(p.o) + (((long long)b * p.T + query) * p.H + h) * p.dv;
 #pragma unroll
   for (int mb = 0; mb < DVP / 32; ++mb)

@@ -253,6 +253,54 @@ mla_status mla_prefill_chunk(const mla_dims* dims, const mla_weights* w, const v
                              float* y, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Training: the layer as a trainable module with dropout on the attention weights
+ * ([DSV2 page] ``MultiHeadLatentAttention.__init__`` / ``forward``: dropout after the
+ * softmax, before the product with the values; [MLA page] ``MLAAttention``: the same).
+ * Family: MLA_ROPE_DECOUPLED_INTERLEAVED with a query latent (r_q > 0), one latent head.
+ * Dropout draws: Philox4x64-10 (Salmon et al., SC 2011); the weight of query i on key j in
+ * head h of sequence b is kept when the upper 32 bits of word j % 4 of the block at counter
+ * (j / 4, i, b * n_heads + h, 0), key (seed, 0) are >= floor(p * 2^32); a kept weight is
+ * scaled by 1 / (1 - p).  The same (seed, p) must be passed to the forward and the backward.
+ * ------------------------------------------------------------------------------------- */
+
+/* Gradients of sum(dy * y) with respect to x and the weights (float32, shapes as the inputs /
+ * mla_weights; every array fully overwritten).  The family's unused matrices have none. */
+typedef struct {
+  float *dx, *dw_dq, *dw_uq, *dw_qr, *dw_dkv, *dw_kr, *dw_uk, *dw_uv, *dw_o;
+} mla_grads;
+
+/* Source: the library's own.  Bytes of the state mla_train_forward keeps for the backward
+ * (query latent, queries, latent, rotary keys, keys, values, attention outputs, per-row
+ * log-sum-exp) for B sequences of S tokens; 0 for unsupported dims.  Host only. */
+size_t mla_train_saved_bytes(const mla_dims* dims, int32_t B, int32_t S);
+
+/* Source: the library's own.  Workspace bytes of mla_train_backward.  Host only. */
+size_t mla_train_workspace_bytes(const mla_dims* dims, int32_t B, int32_t S);
+
+/* Causal forward with dropout p in [0, 1) on the attention weights.
+ * Source: [DSV2 page] ``MultiHeadLatentAttention.forward`` (training mode, no cache).
+ *   x [B][S][d_model]; y [B][S][d_model] float32 (overwritten); saved: caller-owned device
+ *   buffer of mla_train_saved_bytes, filled for mla_train_backward.  p = 0 gives mla_prefill's
+ *   result (up to rounding).
+ * Errors: UNSUPPORTED outside the family above, INVALID_ARG for p outside [0, 1) or missing
+ * pointers, WORKSPACE if saved_bytes is too small, HIP for a failed launch. */
+mla_status mla_train_forward(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B, int32_t S,
+                             float dropout_p, uint64_t seed, float* y, void* saved, size_t saved_bytes,
+                             void* stream);
+
+/* Backward of mla_train_forward: the chain rule through the output projection, the dropped-
+ * out softmax attention (per-row log-sum-exp and dropout mask recomputed), the rotations
+ * (by the negative angle; the rotary key's gradient summed over heads) and the projections.
+ * Source: [DSV2 page] ``MultiHeadLatentAttention.forward`` differentiated.
+ *   dy [B][S][d_model] float32; saved: as filled by mla_train_forward with the same x, w, p,
+ *   seed; g: gradient arrays (float32, fully overwritten).
+ * Errors as mla_train_forward; WORKSPACE if ws_bytes < mla_train_workspace_bytes. */
+mla_status mla_train_backward(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B, int32_t S,
+                              float dropout_p, uint64_t seed, const float* dy, const void* saved,
+                              size_t saved_bytes, const mla_grads* g, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Compressed convolutional attention (CCA) and its grouped-query form (CCGQA): a related
  * latent method in which queries, keys and values are down-projected into a compressed
  * latent and attention runs entirely inside it ([CCA page] frankenstein-transformer docs,

@@ -79,6 +79,8 @@ def keep_threshold(p: float) -> int:
 
 def dropout_keep(seed: int, b: int, H: int, h: int, n_q: int, n_k: int, p: float) -> np.ndarray:
     """Keep mask [n_q, n_k] of head h of sequence b (queries 0..n_q-1, keys 0..n_k-1)."""
+    if keep_threshold(p) == 0:
+        return np.ones((n_q, n_k), dtype=bool)          # every draw passes a zero threshold
     i = np.arange(n_q, dtype=U64)[:, None]
     j = np.arange(n_k, dtype=U64)[None, :]
     words = philox4x64(j >> U64(2), i, U64(b * H + h), U64(0), U64(seed), U64(0))
@@ -109,26 +111,28 @@ def train_forward(x: np.ndarray, W: Dict[str, np.ndarray], d: O.Dims, p: float, 
     v = (c @ Wf["w_uv"].T).reshape(S, H, dn)
     q = np.concatenate([q_c, q_r], axis=-1)
     k = np.concatenate([k_c, np.broadcast_to(k_r[:, None, :], (S, H, dr))], axis=-1)
-    tau = d.scale()
-    causal = pos[None, :] <= pos[:, None]
-    P = np.zeros((H, S, S))
-    keep = np.zeros((H, S, S), dtype=bool)
     o = np.zeros((S, H, dn))
     for h in range(H):
-        s = np.where(causal, tau * (q[:, h] @ k[:, h].T), -np.inf)
-        P[h] = O.softmax_last(s)
-        keep[h] = dropout_keep(seed, b, H, h, S, S, p)
-        o[:, h] = (P[h] * keep[h] / (1.0 - p)) @ v[:, h]
+        P, keep = _weights_of_head(q, k, d, p, seed, b, h)
+        o[:, h] = (P * keep / (1.0 - p)) @ v[:, h]
     y = o.reshape(S, H * dn) @ Wf["w_o"].T
-    saved = dict(x=x, cq=cq, c=c, q=q, k=k, v=v, o=o, P=P, keep=keep, pos=pos)
+    saved = dict(x=x, cq=cq, c=c, q=q, k=k, v=v, o=o, pos=pos, seed=seed, b=b)
     return y, saved
+
+
+def _weights_of_head(q, k, d: O.Dims, p: float, seed: int, b: int, h: int):
+    """Causal softmax weights P [S, S] of head h and their dropout keep mask."""
+    S, H = q.shape[0], q.shape[1]
+    pos = np.arange(S)
+    s = np.where(pos[None, :] <= pos[:, None], d.scale() * (q[:, h] @ k[:, h].T), -np.inf)
+    return O.softmax_last(s), dropout_keep(seed, b, H, h, S, S, p)
 
 
 def train_backward(dy: np.ndarray, W: Dict[str, np.ndarray], d: O.Dims, p: float, saved) -> Dict[str, np.ndarray]:
     """Gradients of sum(dy * y) for the forward above: dx and one entry per weight."""
     Wf = {k: np.asarray(v, dtype=F64) for k, v in W.items()}
     dy = np.asarray(dy, dtype=F64)
-    x, cq, c, q, k, v, o, P, keep, pos = (saved[n] for n in ("x", "cq", "c", "q", "k", "v", "o", "P", "keep", "pos"))
+    x, cq, c, q, k, v, o, pos = (saved[n] for n in ("x", "cq", "c", "q", "k", "v", "o", "pos"))
     S, H, dn, dr = x.shape[0], d.n_heads, d.d_nope, d.d_rope
     tau = d.scale()
     g: Dict[str, np.ndarray] = {}
@@ -141,11 +145,12 @@ def train_backward(dy: np.ndarray, W: Dict[str, np.ndarray], d: O.Dims, p: float
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for h in range(H):
-        Pd = P[h] * keep[h] / (1.0 - p)
+        P, keep = _weights_of_head(q, k, d, p, saved["seed"], saved["b"], h)   # recomputed per head
+        Pd = P * keep / (1.0 - p)
         dPd = do[:, h] @ v[:, h].T
         dv[:, h] = Pd.T @ do[:, h]
-        dP = dPd * keep[h] / (1.0 - p)
-        ds = P[h] * (dP - np.sum(P[h] * dP, axis=1, keepdims=True))
+        dP = dPd * keep / (1.0 - p)
+        ds = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
         dq[:, h] = tau * (ds @ k[:, h])
         dk[:, h] = tau * (ds.T @ q[:, h])
     # split of q and k into their decompressed and rotary parts
