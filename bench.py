@@ -156,6 +156,7 @@ UNIT_SOURCES = {
     "dsv2_prefill_attention": ("prefill_fast.hip", "prefill.hip", "gemm.hip", "gemm_big.hip", "gemm_epilogue.h",
                                "lds_dma.h", "common.h", "internal.h"),
     "mlra_decode_attention": ("decode_fast.hip", "decode.hip", "lds_dma.h", "common.h", "internal.h"),
+    "mlra_latent_head_decode_attention": ("decode_fast.hip", "decode.hip", "lds_dma.h", "common.h", "internal.h"),
 }
 
 
@@ -265,7 +266,7 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None, ctx_from=No
     return res, d
 
 
-def bench_prefill(cfg, steps, warmup):
+def bench_prefill(cfg, steps, warmup, parts=("call", "attention", "chunk")):
     torch = __import__("torch")
     d = Dev(cfg)
     M = d.M
@@ -284,9 +285,16 @@ def bench_prefill(cfg, steps, warmup):
     def call(i):
         M.mla_prefill(d.dims, d.wst, x, B, S_, cs, y, ws, nws)
 
-    log(f"[bench] {cfg.name}: timing mla_prefill")
     st_call = {}
-    ms = timed(torch, call, steps, warmup, st_call)
+    ms = float("nan")
+    if "call" in parts:
+        log(f"[bench] {cfg.name}: timing mla_prefill")
+        ms = timed(torch, call, steps, warmup, st_call)
+    else:
+        # the latent cache must hold the workload's rows (a zero cache gives all-zero keys and
+        # values, whose products draw less power and run at a higher clock)
+        call(0)
+        torch.cuda.synchronize()
     H, dn, dr, dv = cfg.n_heads, cfg.d_nope, cfg.d_rope, cfg.d_v
     g = torch.Generator(device="cpu").manual_seed(cfg.seed)
     q = torch.randn((B, S_, H, dn + dr), generator=g).to(d.dt).cuda()
@@ -315,7 +323,7 @@ def bench_prefill(cfg, steps, warmup):
     # quarters (the cache already holds every row; the call rewrites rows start.. with the
     # same values)
     start, T = (3 * S_ // 4) // 64 * 64, S_ - (3 * S_ // 4) // 64 * 64
-    if 0 < start < S_:
+    if 0 < start < S_ and "chunk" in parts:
         xc = x[:, start:].contiguous()
         yc = torch.empty((B, T, cfg.d_model), dtype=torch.float32, device="cuda")
         wsc, nwsc = d.workspace(M.MLA_OP_PREFILL_CHUNK, B, S_)
@@ -333,6 +341,84 @@ def bench_prefill(cfg, steps, warmup):
                         "flop": flop_c, "TFLOPs": flop_c / ms_chunk / 1e9,
                         "new_tokens_per_s": B * T / ms_chunk * 1e3}
     return res
+
+
+def bench_cca(cfg, steps, warmup):
+    """mla_cca_prefill on the page-default CCA / CCGQA workload (B=4, S=2048)."""
+    torch = __import__("torch")
+    import head_latent_attention_dkv_amd as M
+    prob = S.make_cca_problem(cfg)
+    dims = M.cca_dims_from_cfg(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    w = {k: torch.from_numpy(np.ascontiguousarray(v, np.float32)).to("cuda").to(dt) for k, v in prob.weights.items()}
+    wst = M.cca_weights_struct(w, cfg.beta)
+    B, S_ = cfg.batch, cfg.seq
+    xs = S.make_x_batch(cfg, [S_] * B, threads=host_threads())
+    x = torch.from_numpy(np.stack(xs)).to("cuda").to(dt)
+    y = torch.empty((B, S_, cfg.d_model), dtype=torch.float32, device="cuda")
+    n = M.mla_cca_workspace_bytes(dims, B, S_)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        M.mla_cca_prefill(dims, wst, x, B, S_, y, ws, n)
+
+    log(f"[bench] {cfg.name}: timing mla_cca_prefill")
+    st = {}
+    ms = timed(torch, call, steps, warmup, st)
+    Hq, Hkv, dh, E = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_model
+    rows = B * S_
+    proj = 2.0 * rows * E * (Hq * dh + 2 * Hkv * dh) + 2.0 * rows * Hq * dh * E
+    conv = 2.0 * rows * (Hq + Hkv) * dh * (cfg.conv_kernel_seq + dh * cfg.conv_kernel_ch)
+    core = 2.0 * B * Hq * (S_ * (S_ + 1) / 2) * (2 * dh)
+    flop = proj + conv + core
+    return {"workload": cfg.name, "ms_per_call": ms, "timing": st, "flop": flop, "TFLOPs": flop / ms / 1e9,
+            "frac_of_mfma_peak": flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, "attention_core_flop": core,
+            "tokens_per_s": rows / (ms * 1e-3)}
+
+
+def bench_train(cfg, steps, warmup, p=0.1, seed=1234):
+    """One training step of the DeepSeek-V2-shaped layer: mla_train_forward (dropout p on the
+    attention weights) then mla_train_backward for dy ~ N(0, 1)."""
+    torch = __import__("torch")
+    d = Dev(cfg)
+    M = d.M
+    B, S_ = cfg.batch, cfg.seq
+    xs = S.make_x_batch(cfg, [S_] * B, threads=host_threads())
+    x = d.up(np.stack(xs))
+    del xs
+    g = torch.Generator(device="cpu").manual_seed(cfg.seed)
+    dy = torch.randn((B, S_, cfg.d_model), generator=g).cuda()
+    y = torch.empty((B, S_, cfg.d_model), dtype=torch.float32, device="cuda")
+    ns, nw = M.mla_train_saved_bytes(d.dims, B, S_), M.mla_train_workspace_bytes(d.dims, B, S_)
+    saved = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nw, dtype=torch.uint8, device="cuda")
+    grads = {"dx": torch.empty((B, S_, cfg.d_model), dtype=torch.float32, device="cuda")}
+    grads.update({"d" + k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in d.prob.weights.items()})
+    gst = M.grads_struct(grads)
+
+    def fwd(i):
+        M.mla_train_forward(d.dims, d.wst, x, B, S_, p, seed, y, saved, ns)
+
+    def bwd(i):
+        M.mla_train_backward(d.dims, d.wst, x, B, S_, p, seed, dy, saved, ns, gst, ws, nw)
+
+    log(f"[bench] {cfg.name}: timing mla_train_forward / mla_train_backward (p={p})")
+    st_f, st_b = {}, {}
+    ms_f = timed(torch, fwd, steps, warmup, st_f)
+    ms_b = timed(torch, bwd, steps, warmup, st_b)
+    w = d.prob.weights
+    H, dn, dr, dv = cfg.n_heads, cfg.d_nope, cfg.d_rope, cfg.d_v
+    core = 2.0 * B * H * (S_ * (S_ + 1) / 2) * (dn + dr + dv)
+    proj = 2.0 * B * S_ * sum(v.size for v in w.values())
+    fwd_flop = core + proj
+    bwd_flop = 2.0 * fwd_flop          # two products per forward product (input and weight gradients)
+    return {"workload": f"{cfg.name} training step (dropout p={p}), B={B}, S={S_}", "fwd_ms": ms_f, "bwd_ms": ms_b,
+            "fwd_timing": st_f, "bwd_timing": st_b, "fwd_flop": fwd_flop, "bwd_flop": bwd_flop,
+            "fwd_TFLOPs": fwd_flop / ms_f / 1e9, "bwd_TFLOPs": bwd_flop / ms_b / 1e9,
+            "step_TFLOPs": (fwd_flop + bwd_flop) / (ms_f + ms_b) / 1e9,
+            "frac_of_mfma_peak": (fwd_flop + bwd_flop) / (ms_f + ms_b) / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "saved_bytes": ns, "workspace_bytes": nw,
+            "tokens_per_s": B * S_ / ((ms_f + ms_b) * 1e-3)}
 
 
 def cpu_baseline(cfg, budget_s=15.0, max_seqs=64):
@@ -396,15 +482,48 @@ def cpu_baseline_prefill(cfg, budget_s=12.0, rows_per_seq=32):
                       f"{t_tot:.1f} s; value = that sample's attention-unit flops / time"}
 
 
-def summarize_profiles(d):
-    """Turn rocprofv3 CSV output under directory d into the committed summaries.
+# Units the profile summaries cover: the `bench.py --only` mode that runs the unit alone,
+# the kernels one call launches (name fragments, in launch order), the algorithmic work of one
+# call and its peak, and the summary file.
+PROFILE_UNITS = {
+    "decode_attention": dict(title="mla_decode_attention, DeepSeek-V2 decode (B=64, 4096 cached + 1, H=128, "
+                                   "latent 512 + rotary 64)", kernels=("decode_h128_kernel", "combine_uv_kernel"),
+                             work=lambda: S.CONFIGS["dsv2_decode"], bound="hbm", file="dsv2_decode_attention"),
+    "mlra_attention": dict(title="mla_decode_attention, MLRA decode (B=128, contexts U[512, 16384], 4 latent "
+                                 "heads x rank 128)", kernels=("decode_fast_kernel", "combine_kernel"),
+                           work=lambda: S.CONFIGS["mlra_decode"], bound="hbm", file="mlra_decode_attention"),
+    "lh_attention": dict(title="mla_decode_attention, one MLRA latent head (rank 128, 4 query heads, the MLRA "
+                               "contexts)", kernels=("decode_fast_kernel", "combine_kernel"),
+                         work=lambda: MLRA_LATENT_HEAD, bound="hbm", file="mlra_latent_head_decode_attention"),
+    "prefill_attention": dict(title="mla_prefill_attention, DeepSeek-V2 prefill (B=4, S=4096, H=128): K/V "
+                                    "up-projection + flash causal attention",
+                              kernels=("gemm_big_kernel", "prefill_flash_kernel"),
+                              work=lambda: S.CONFIGS["dsv2_prefill"], bound="mfma", file="dsv2_prefill_attention"),
+}
 
-    d/stats/*kernel_stats.csv        (--kernel-trace --stats of `bench.py --only decode`)
-    d/fetch/*counter_collection.csv  (--pmc FETCH_SIZE of `bench.py --only decode_attention`)
-    d/write/*counter_collection.csv  (--pmc WRITE_SIZE of the same)
-    d/copy_fetch, d/copy_write       (the same counters on `bench.py --only copy`)
-    Writes profiles/dsv2_decode_attention_traffic.json (bytes per launch of the unit,
-    scaled by the copy kernel's bytes-per-counter-KiB) for the current kernel sources.
+
+def unit_work(unit):
+    """Algorithmic bytes (decode) or flops (prefill) of one call of a profiled unit."""
+    cfg = PROFILE_UNITS[unit]["work"]()
+    if PROFILE_UNITS[unit]["bound"] == "hbm":
+        ctx = problem(S.CONFIGS["mlra_decode"]).ctx_lens if unit == "lh_attention" else problem(cfg).ctx_lens
+        return float(sum((int(c) + 1) * (cfg.r_kv + cfg.d_rope) * 2 for c in ctx))
+    B, S_, H = cfg.batch, cfg.seq, cfg.n_heads
+    core = 2.0 * B * H * (S_ * (S_ + 1) / 2) * (cfg.d_nope + cfg.d_rope + cfg.d_v)
+    return core + 2.0 * B * S_ * cfg.r_kv * H * (cfg.d_nope + cfg.d_v) / cfg.n_latent_heads
+
+
+def summarize_profiles(d):
+    """Turn rocprofv3 CSV output under directory d into the committed summaries (profiles/).
+
+    For each unit U of PROFILE_UNITS (run alone by `bench.py --only U`):
+      d/U_trace   --kernel-trace --stats
+      d/U_fetch   --pmc FETCH_SIZE            d/U_write  --pmc WRITE_SIZE
+      d/U_mfma    --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+    and d/copy_fetch, d/copy_write (the same counters on `bench.py --only copy`, a 1 GiB copy)
+    for the bytes-per-counter scale.  d/decode_trace (`bench.py --only decode`) gives the
+    kernels of one whole decode step.  Writes profiles/<file>_kernels.md per unit and
+    profiles/<file>_traffic.json (read by the bench while the kernel sources match).
     """
     import csv
     import glob
@@ -416,167 +535,235 @@ def summarize_profiles(d):
                 out.extend(csv.DictReader(fh))
         return out
 
-    def per_dispatch(sub, counter, match):
-        vals = {}
-        for r in rows(sub, "*counter_collection.csv"):
-            name = r.get("Kernel_Name", "")
-            if r.get("Counter_Name") != counter or not match(name):
-                continue
-            key = (name, r.get("Dispatch_Id"))
-            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-        return vals
+    demangled = {}
 
-    def unit_kib(sub, counter):
-        v = per_dispatch(sub, counter, lambda n: "decode_h128_kernel" in n or "combine_kernel" in n
-                         or "combine_uv_kernel" in n)
-        by = {}
-        for (name, _), x in v.items():
-            by.setdefault("combine" if "combine" in name else "split", []).append(x)
-        return {k: float(np.median(x)) for k, x in by.items()}
+    def short(name):
+        if name.startswith("_Z"):
+            # mangled names of this library's kernels (binutils' c++filt does not know the
+            # bfloat16 code DF16b): namespace prefixes, the kernel name, its element type
+            if name not in demangled:
+                m = re.match(r"_ZN(?:3mla)?(?:12_GLOBAL__N_1)?(\d+)", name)
+                out = name
+                if m:
+                    n = int(m.group(1))
+                    base = name[m.end():m.end() + n]
+                    rest = name[m.end() + n:]
+                    typ = {"IDF16b": "<bf16>", "If": "<float>"}
+                    out = base + next((t for k, t in typ.items() if rest.startswith(k)), "")
+                demangled[name] = out
+            name = demangled[name]
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "").replace("mla::", "")
+        name = re.sub(r"\(.*$", "", name).replace("__hip_bfloat16", "bf16")
+        return name[:90]
+
+    def grid_of(r):
+        wg = max(1, int(r.get("Workgroup_Size_X") or 1))
+        return f"{int(r.get('Grid_Size_X') or 0) // wg}x{int(r.get('Grid_Size_Y') or 1)}x{int(r.get('Grid_Size_Z') or 1)}"
+
+    def dur(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+
+    def kernel_table(trace, limit=None):
+        """Per (kernel, grid) launch counts and durations, longest total first."""
+        per = {}
+        for r in trace:
+            per.setdefault((short(r["Kernel_Name"]), grid_of(r)), []).append(dur(r))
+        out = ["| kernel | grid (workgroups) | launches | total ms | avg µs | min µs | max µs |",
+               "|---|---|---|---|---|---|---|"]
+        for (k, g), v in sorted(per.items(), key=lambda kv: -sum(kv[1]))[:limit]:
+            out.append(f"| {k} | {g} | {len(v)} | {sum(v) / 1e3:.2f} | {np.mean(v):.1f} | {np.min(v):.1f} | "
+                       f"{np.max(v):.1f} |")
+        return out, per
+
+    def per_dispatch(sub, counters):
+        """{dispatch id: (kernel name, {counter: value summed over the device})}"""
+        out = {}
+        for r in rows(sub, "*counter_collection.csv"):
+            if r.get("Counter_Name") not in counters:
+                continue
+            key = r.get("Dispatch_Id")
+            name, vals = out.setdefault(key, (r.get("Kernel_Name", ""), {}))
+            vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return out
 
     def copy_kib(sub, counter):
-        v = per_dispatch(sub, counter, lambda n: "copy" in n.lower() or "elementwise" in n.lower())
-        xs = [x for x in v.values() if x > 1e5]
+        xs = [v[counter] for n, v in per_dispatch(sub, {counter}).values()
+              if ("copy" in n.lower() or "elementwise" in n.lower()) and v.get(counter, 0) > 1e5]
         return float(np.median(xs)) if xs else None
 
     n_copy = 1 << 30
     cf, cw = copy_kib("copy_fetch", "FETCH_SIZE"), copy_kib("copy_write", "WRITE_SIZE")
-    uf, uw = unit_kib("fetch", "FETCH_SIZE"), unit_kib("write", "WRITE_SIZE")
-    rec = {"unit": "mla_decode_attention: split kernel + combine kernel, DeepSeek-V2 decode shape",
-           "copy_bytes": n_copy, "copy_fetch_kib": cf, "copy_write_kib": cw,
-           "fetch_kib": uf, "write_kib": uw}
-    if cf and cw and uf and uw:
-        ff, fw = n_copy / (cf * 1024.0), n_copy / (cw * 1024.0)
-        rec["fetch_scale"], rec["write_scale"] = ff, fw
-        rec["hbm_read_bytes_per_launch"] = sum(uf.values()) * 1024.0 * ff
-        rec["hbm_write_bytes_per_launch"] = sum(uw.values()) * 1024.0 * fw
-        rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
-    rec["src_digest"] = src_digest(*UNIT_SOURCES["dsv2_decode_attention"])
-    out = os.path.join(PROFILES, "dsv2_decode_attention_traffic.json")
-    with open(out, "w") as fh:
-        json.dump(rec, fh, indent=1)
-    print(json.dumps(rec, indent=1))
+    fscale = n_copy / (cf * 1024.0) if cf else None
+    wscale = n_copy / (cw * 1024.0) if cw else None
+    cmd = ("rocprofv3 {opt} --output-format csv -d <dir>/{sub} -o run -- python3 bench.py --only {unit} "
+           "--steps {steps} --warmup 2")
+    for unit, spec in PROFILE_UNITS.items():
+        trace = rows(f"{unit}_trace", "*kernel_trace.csv")
+        if not trace:
+            continue
+        trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+        first, last = spec["kernels"][0], spec["kernels"][-1]
+        # calls: a dispatch of the first kernel opens a call, the next dispatch of the last kernel
+        # closes it.  The bench times a loop of back-to-back calls with events, so its time per
+        # call is the steady-state period between the starts of consecutive calls (kernels plus
+        # the launch gaps between them); the first call after the set-up is left out.
+        calls = []
+        i = 0
+        while i < len(trace):
+            if first in trace[i]["Kernel_Name"] or first in short(trace[i]["Kernel_Name"]):
+                j = i + 1
+                while j < len(trace) and last not in short(trace[j]["Kernel_Name"]) \
+                        and first not in short(trace[j]["Kernel_Name"]):
+                    j += 1
+                if j < len(trace) and last in short(trace[j]["Kernel_Name"]):
+                    calls.append(trace[i:j + 1])
+                    i = j + 1
+                    continue
+            i += 1
+        if len(calls) < 3:
+            continue
+        starts = [int(c[0]["Start_Timestamp"]) for c in calls]
+        periods = np.diff(starts)[1:] / 1e3
+        spans = [(int(c[-1]["End_Timestamp"]) - int(c[0]["Start_Timestamp"])) / 1e3 for c in calls[1:]]
+        table, per_kernel = kernel_table([r for c in calls[1:] for r in c])
+        work = unit_work(unit)
+        period = float(np.median(periods))
+        peak = HBM_PEAK_GBS if spec["bound"] == "hbm" else MFMA_BF16_PEAK_TFLOPS
+        div = 1e3 if spec["bound"] == "hbm" else 1e6
+        achieved = work / period / div
+        unit_s = "GB/s" if spec["bound"] == "hbm" else "TFLOP/s"
+        kern_sum = sum(float(np.mean(v)) for v in per_kernel.values())
+        lines = [f"# Kernel times and counters: {spec['title']}", "",
+                 "Commands (from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first, then "
+                 "`python3 bench.py --summarize <dir>`):", "", "```",
+                 cmd.format(opt="--kernel-trace --stats", sub=f"{unit}_trace", unit=unit, steps=20),
+                 cmd.format(opt="--pmc FETCH_SIZE", sub=f"{unit}_fetch", unit=unit, steps=3),
+                 cmd.format(opt="--pmc WRITE_SIZE", sub=f"{unit}_write", unit=unit, steps=3),
+                 cmd.format(opt="--pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE", sub=f"{unit}_mfma",
+                            unit=unit, steps=3),
+                 cmd.format(opt="--pmc FETCH_SIZE", sub="copy_fetch", unit="copy", steps=3),
+                 cmd.format(opt="--pmc WRITE_SIZE", sub="copy_write", unit="copy", steps=3),
+                 "```", "",
+                 f"One call = {' + '.join(spec['kernels'])}.  {len(calls) - 1} back-to-back calls traced (the first, "
+                 "after the set-up, left out).", ""] + table + [
+                 "", f"- sum of the kernels' average times: **{kern_sum:.1f} µs**",
+                 f"- per-call period (start of a call to the start of the next; what the bench's events time over "
+                 f"a loop of calls): median **{period:.1f} µs** (min {np.min(periods):.1f}, max {np.max(periods):.1f})",
+                 f"- per-call span (first kernel's start to last kernel's end): median {np.median(spans):.1f} µs",
+                 f"- algorithmic work per call: {work / 1e6:.2f} MB" if spec["bound"] == "hbm" else
+                 f"- algorithmic work per call: {work / 1e12:.4f} TFLOP",
+                 f"- achieved over the period: **{achieved:.1f} {unit_s}**, fraction of the {peak:.0f} {unit_s} peak "
+                 f"= **{achieved / peak:.3f}** (over the kernel sum: {work / kern_sum / div / peak:.3f})", ""]
+        rec = {"unit": spec["title"], "src_digest": src_digest(*UNIT_SOURCES[spec["file"]]),
+               "period_us": period, "kernel_sum_us": kern_sum, "work_per_call": work,
+               "frac_over_period": achieved / peak}
+        fet = per_dispatch(f"{unit}_fetch", {"FETCH_SIZE"})
+        wri = per_dispatch(f"{unit}_write", {"WRITE_SIZE"})
+        if fet and wri and fscale and wscale:
+            tot_r = tot_w = 0.0
+            lines += ["HBM traffic per call (median per dispatch; FETCH_SIZE scaled by "
+                      f"{fscale:.3f} and WRITE_SIZE by {wscale:.3f}, the factors that make a 1 GiB device copy read "
+                      "and write 1 GiB):", ""]
+            for kf in spec["kernels"]:
+                fr = [v["FETCH_SIZE"] for n, v in fet.values() if kf in n]
+                wr = [v["WRITE_SIZE"] for n, v in wri.values() if kf in n]
+                if fr and wr:
+                    rb, wb = float(np.median(fr)) * 1024 * fscale, float(np.median(wr)) * 1024 * wscale
+                    tot_r += rb
+                    tot_w += wb
+                    lines.append(f"- {kf}: read {rb / 1e6:.1f} MB, write {wb / 1e6:.1f} MB")
+            lines += [f"- unit total: **{(tot_r + tot_w) / 1e6:.1f} MB** per call"
+                      + (f" against {work / 1e6:.1f} MB algorithmic ({(tot_r + tot_w) / work:.2f}x)"
+                         if spec["bound"] == "hbm" else ""), ""]
+            rec.update({"fetch_scale": fscale, "write_scale": wscale, "hbm_read_bytes_per_launch": tot_r,
+                        "hbm_write_bytes_per_launch": tot_w, "hbm_bytes_per_launch": tot_r + tot_w})
+        mf = per_dispatch(f"{unit}_mfma", {"MfmaUtil", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES"})
+        if mf:
+            lines += ["MFMA utilisation (median per dispatch; MfmaUtil = sum of SQ_VALU_MFMA_BUSY_CYCLES over the "
+                      "SIMDs / (GRBM_GUI_ACTIVE x SIMD count); clock = GRBM_GUI_ACTIVE summed over the 8 XCDs / 8 / "
+                      "the kernel's average time above):", "",
+                      "| kernel | MfmaUtil % | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | clock GHz |", "|---|---|---|---|---|"]
+            for kf in spec["kernels"]:
+                vs = [v for n, v in mf.values() if kf in n]
+                if not vs:
+                    continue
+                med = {c: float(np.median([v.get(c, np.nan) for v in vs])) for c in
+                       ("MfmaUtil", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")}
+                t_us = np.mean([np.mean(v) for (k, g), v in per_kernel.items() if kf in k] or [np.nan])
+                # (kernels under 50 µs: the counter window's own overhead dominates, no clock shown)
+                clk = med["GRBM_GUI_ACTIVE"] / 8 / (t_us * 1e-6) / 1e9 if t_us >= 50 else float("nan")
+                lines.append(f"| {kf} | {med['MfmaUtil']:.1f} | {med['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | "
+                             f"{med['GRBM_GUI_ACTIVE']:.4g} | " + (f"{clk:.2f} |" if clk == clk else "— |"))
+                rec.setdefault("mfma_util_pct", {})[kf] = med["MfmaUtil"]
+            lines.append("")
+        lines.append(f"Kernel sources digest: {rec['src_digest']}")
+        with open(os.path.join(PROFILES, f"{spec['file']}_kernels.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        with open(os.path.join(PROFILES, f"{spec['file']}_traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(f"{unit}: period {period:.1f} us, frac {achieved / peak:.3f}")
 
-    # kernel-time summary of `bench.py --only decode`
-    def short(name):
-        name = name.replace("mla::(anonymous namespace)::", "").replace("(mla::GemmParams)", "")
-        name = name.replace("(mla::DecodeParams)", "").replace("void ", "")
-        if name.startswith("_ZN3mla"):
-            m = re.match(r"_ZN3mla12_GLOBAL__N_114combine_kernelI(DF16b|f)Li(\d+)E", name)
-            if m:
-                return f"combine_kernel<{'bf16' if m.group(1) == 'DF16b' else 'float'},{m.group(2)}>"
-            name = {"_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi64ELi64EEEvNS_10GemmParamsE": "gemm_kernel<bf16,64,64>",
-                    "_ZN3mla12_GLOBAL__N_111gemm_kernelIDF16bLi128ELi128EEEvNS_10GemmParamsE":
-                        "gemm_kernel<bf16,128,128>"}.get(name, name)
-        name = re.sub(r"\(.*$", "", name)             # argument list
-        return name[:70]
-
-    lines = ["# Kernel times: DeepSeek-V2-shaped decode step (B=64, 4096 cached tokens, H=128)", "",
-             "Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
-             "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/stats -o run -- "
-             "python3 bench.py --only decode --steps 20 --warmup 5",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- "
-             "python3 bench.py --only decode_attention --steps 3",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- "
-             "python3 bench.py --only decode_attention --steps 3",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/copy_fetch -o run -- "
-             "python3 bench.py --only copy --steps 3 --warmup 1",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/copy_write -o run -- "
-             "python3 bench.py --only copy --steps 3 --warmup 1",
-             "python3 bench.py --summarize <dir>",
-             "```", ""]
-    trace = rows("stats", "*kernel_trace.csv")
+    # the kernels of one whole decode step (bench.py --only decode)
+    trace = rows("decode_trace", "*kernel_trace.csv")
     if trace:
         trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-        # one timed mla_decode step.  Launch order inside the call: W_DQ (+reduce), queries
-        # (+reduce), latent (+reduce), absorbed query, attention, the combine fused with W_UV,
-        # W_O (+reduce); the first timing loop runs whole calls, so a step ends after the W_O
-        # product that follows the fused combine, and starts after the previous step's end.
         names = [short(r["Kernel_Name"]) for r in trace]
-
-        def step_end(c):
-            j = c + 1                                   # W_O
-            if j + 1 < len(names) and names[j + 1] == "split_reduce_kernel":
-                j += 1
-            return j
-
-        combines = [i for i, n in enumerate(names) if n.startswith("combine_uv_kernel") and "false" not in n]
-        ends = [step_end(c) for c in combines if c + 1 < len(names) and names[c + 1].startswith("skinny")]
-        step = (ends[-2] + 1, ends[-1]) if len(ends) >= 2 else None
-        if step:
-            lines += ["One timed mla_decode step (kernel trace):", "",
-                      "| kernel | blocks (grid x) | µs |", "|---|---|---|"]
+        # a step ends with the output projection (plus its split reduce) after the fused combine
+        ends = []
+        for c, n in enumerate(names):
+            if n.startswith("combine_uv_kernel") and "false" not in n and c + 1 < len(names):
+                j = c + 1
+                if j + 1 < len(names) and names[j + 1].startswith("split_reduce"):
+                    j += 1
+                ends.append(j)
+        lines = ["# Kernel times: one mla_decode step, DeepSeek-V2 decode (B=64, 4096 cached tokens, H=128, "
+                 "d_model 5120)", "",
+                 "Command (from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "", "```",
+                 "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/decode_trace -o run -- python3 bench.py "
+                 "--only decode --steps 20 --warmup 5", "python3 bench.py --summarize <dir>", "```", ""]
+        steps = [(ends[k] + 1, ends[k + 1]) for k in range(len(ends) - 1)]
+        if steps:
+            n_k = int(np.median([b - a + 1 for a, b in steps]))
+            steps = [(a, b) for a, b in steps if b - a + 1 == n_k]
+        if len(steps) >= 3:
+            a0, b0 = steps[-1]
+            lines += [f"{len(steps)} steps of {n_k} kernels traced (eager calls and graph replays); median per "
+                      "kernel:", "", "| kernel | grid (workgroups) | median µs |", "|---|---|---|"]
             tot = 0.0
-            for r in trace[step[0]:step[1] + 1]:
-                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            for pos in range(n_k):
+                us = float(np.median([dur(trace[a + pos]) for a, b in steps]))
                 tot += us
-                blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]) if "Grid_Size_X" in r else r.get("Grid_Size")
-                lines.append(f"| {short(r['Kernel_Name'])} | {blocks} | {us:.1f} |")
-            lines += [f"| **sum** | | **{tot:.1f}** |", ""]
-    stats = rows("stats", "*kernel_stats.csv")
-    if stats:
-        lines += ["rocprofv3 --stats (whole command, including the cache fill's append GEMMs):", "",
-                  "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
-        for r in stats[:14]:
-            lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-        lines.append("")
-    lines += ["HBM traffic of the mla_decode_attention unit (median per dispatch; FETCH_SIZE scaled by "
-              f"{rec.get('fetch_scale', float('nan')):.3f}, WRITE_SIZE by {rec.get('write_scale', float('nan')):.3f}, "
-              "the factors that make a 1 GiB device copy read and write 1 GiB):", "",
-              f"- split kernel: read {uf.get('split', 0) * 1024 * rec.get('fetch_scale', 0) / 1e6:.1f} MB, "
-              f"write {uw.get('split', 0) * 1024 * rec.get('write_scale', 0) / 1e6:.1f} MB",
-              f"- combine kernel: read {uf.get('combine', 0) * 1024 * rec.get('fetch_scale', 0) / 1e6:.1f} MB, "
-              f"write {uw.get('combine', 0) * 1024 * rec.get('write_scale', 0) / 1e6:.1f} MB",
-              f"- unit total: {rec.get('hbm_bytes_per_launch', 0) / 1e6:.1f} MB per launch vs 302.1 MB algorithmic "
-              "(latent + rotary cache)", "",
-              f"Kernel sources digest: {rec['src_digest']}", ""]
-    with open(os.path.join(PROFILES, "dsv2_decode_step_kernels.md"), "w") as fh:
-        fh.write("\n".join(lines))
+                lines.append(f"| {short(trace[a0 + pos]['Kernel_Name'])} | {grid_of(trace[a0 + pos])} | {us:.1f} |")
+            spans = [(int(trace[b]["End_Timestamp"]) - int(trace[a]["Start_Timestamp"])) / 1e3 for a, b in steps]
+            per = [(int(trace[steps[k + 1][0]]["Start_Timestamp"]) - int(trace[steps[k][0]]["Start_Timestamp"])) / 1e3
+                   for k in range(len(steps) - 1)]
+            per = [x for x in per if x < 2 * np.median(spans)]          # back-to-back steps only
+            lines += [f"| **sum** | | **{tot:.1f}** |", "",
+                      f"- step span (first kernel's start to last kernel's end): median {np.median(spans):.1f} µs",
+                      f"- step period (start of a step to the start of the next, back-to-back steps): median "
+                      f"**{np.median(per):.1f} µs**; latent cache 302.06 MB per period: "
+                      f"{302.06e6 / np.median(per) / 1e3:.1f} GB/s", ""]
+        with open(os.path.join(PROFILES, "dsv2_decode_step_kernels.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
 
-    # kernel times of `bench.py --only prefill_attention` (d/prefill_stats)
-    pstats = rows("prefill_stats", "*kernel_stats.csv")
-    if pstats:
-        pl = ["# Kernel times: DeepSeek-V2-shaped prefill attention (B=4, S=4096, H=128, d_nope=128, "
-              "d_rope=64, r_kv=512)", "",
-              "Command (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
-              "```",
-              "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/prefill_stats -o run -- "
-              "python3 bench.py --only prefill_attention --steps 8 --warmup 2",
-              "python3 bench.py --summarize <dir>",
-              "```", "",
-              "mla_prefill_attention = K/V up-projection GEMM (gemm_big_kernel, writes head-major K and "
-              "token-permuted V^T) + flash causal attention (prefill_flash_kernel).", "",
-              "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
-        for r in pstats[:8]:
-            pl.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-        pl += ["", f"Kernel sources digest: {src_digest(*UNIT_SOURCES['dsv2_prefill_attention'])}", ""]
-        with open(os.path.join(PROFILES, "dsv2_prefill_attention_kernels.md"), "w") as fh:
-            fh.write("\n".join(pl))
-
-    # kernel times of `bench.py --only mlra` (d/mlra_stats)
-    mstats = rows("mlra_stats", "*kernel_stats.csv")
-    if mstats:
-        ml = ["# Kernel times: MLRA decode (B=128, contexts U[512, 16384], 4 latent blocks x rank 128, "
-              "H=16, d_model=2048) and one of its latent heads on its own (rank 128, 4 query heads)", "",
-              "Command (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
-              "```",
-              "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/mlra_stats -o run -- "
-              "python3 bench.py --only mlra --steps 20 --warmup 5",
-              "python3 bench.py --summarize <dir>",
-              "```", "",
-              "mla_decode_attention = split kernel (decode_fast_kernel; `true` = the token-split form of the "
-              "latent-head workload) + combine kernel; the calls also run the few-row projections and the "
-              "cache append.", "",
-              "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
-        for r in mstats[:14]:
-            ml.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-        ml += ["", f"Kernel sources digest: {src_digest(*UNIT_SOURCES['mlra_decode_attention'])}", ""]
-        with open(os.path.join(PROFILES, "mlra_decode_attention_kernels.md"), "w") as fh:
-            fh.write("\n".join(ml))
+    # kernels of the CCA / CCGQA prefill and of the training step (bench.py --only cca / train)
+    for sub, title, fname, steps in (
+            ("cca_trace", "mla_cca_prefill, CCA and CCGQA at the page defaults (B=4, S=2048, E=2048, 16 query heads; "
+                          "CCA 16 key/value heads of 32, CCGQA 4 of 64)", "cca_prefill_kernels.md", 3),
+            ("train_trace", "mla_train_forward + mla_train_backward, DeepSeek-V2 prefill shape (B=4, S=4096), "
+                            "dropout 0.1", "dsv2_train_step_kernels.md", 3)):
+        trace = rows(sub, "*kernel_trace.csv")
+        if not trace:
+            continue
+        unit = sub.split("_")[0]
+        table, _ = kernel_table([r for r in trace if not short(r["Kernel_Name"]).startswith(("at::", "__amd"))])
+        lines = [f"# Kernel times: {title}", "", "Command (from the repository root on one MI355X; "
+                 "`cd /tmp && export TMPDIR=/tmp` first):", "", "```",
+                 f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/{sub} -o run -- python3 bench.py "
+                 f"--only {unit} --steps {steps} --warmup 1", "python3 bench.py --summarize <dir>", "```", "",
+                 "Library kernels of every call in the run (warm-up included), per grid shape:", ""] + table
+        with open(os.path.join(PROFILES, fname), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
 
 
 def main():
@@ -586,7 +773,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
                     choices=["all", "decode", "decode_attention", "prefill", "prefill_attention", "mlra",
-                             "small", "copy"])
+                             "mlra_attention", "lh_attention", "small", "cca", "train", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="write profile summaries from rocprofv3 output in DIR")
     args = ap.parse_args()
@@ -615,7 +802,22 @@ def main():
         print(json.dumps(r))
         return
     if args.only == "prefill_attention":
-        print(json.dumps(bench_prefill(S.CONFIGS["dsv2_prefill"], args.steps, args.warmup)))
+        print(json.dumps(bench_prefill(S.CONFIGS["dsv2_prefill"], args.steps, args.warmup, parts=("attention",))))
+        return
+    if args.only == "mlra_attention":
+        r, _ = bench_decode(S.CONFIGS["mlra_decode"], 0, 0, copies=1, attention_steps=args.steps)
+        print(json.dumps(r))
+        return
+    if args.only == "lh_attention":
+        r, _ = bench_decode(MLRA_LATENT_HEAD, 0, 0, copies=2, attention_steps=args.steps,
+                            ctx_from=S.CONFIGS["mlra_decode"])
+        print(json.dumps(r))
+        return
+    if args.only == "cca":
+        print(json.dumps({n: bench_cca(S.CCA_CONFIGS[n], args.steps, args.warmup) for n in ("cca", "ccgqa")}))
+        return
+    if args.only == "train":
+        print(json.dumps(bench_train(S.CONFIGS["dsv2_prefill"], args.steps, args.warmup)))
         return
 
     out = {}
@@ -631,6 +833,10 @@ def main():
                                          ctx_from=S.CONFIGS["mlra_decode"])
     if args.only in ("all", "small"):
         out["small"] = bench_prefill(S.CONFIGS["small_lm"], args.steps, args.warmup)
+    if args.only == "all":
+        out["cca"] = {n: bench_cca(S.CCA_CONFIGS[n], max(3, args.steps // 4), max(1, args.warmup // 2))
+                      for n in ("cca", "ccgqa")}
+        out["train"] = bench_train(S.CONFIGS["dsv2_prefill"], max(2, args.steps // 8), 1)
     if args.only != "all":
         print(json.dumps(out))
         return
@@ -725,6 +931,13 @@ def main():
     line["small_lm_prefill"] = {"workload": "small-LM MLA prefill B=8, S=1024, d_model=512, H=8, r_kv=256",
                                 "ms_per_call": sm["ms_per_call"], "layer_TFLOPs": sm["layer_TFLOPs"],
                                 "attention_TFLOPs": sm["attention_TFLOPs"]}
+    line["cca_prefill"] = {n: {**r, "roofline": {"bound": "mfma", "achieved": r["TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                                                 "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"]}}
+                           for n, r in out["cca"].items()}
+    tr = out["train"]
+    line["train_step"] = {**tr, "roofline": {"bound": "mfma", "achieved": tr["step_TFLOPs"],
+                                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                             "frac": tr["frac_of_mfma_peak"]}}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(S.CONFIGS["dsv2_decode"])

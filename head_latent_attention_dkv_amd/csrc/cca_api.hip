@@ -2,7 +2,8 @@
 // launch sequence (no allocation, no host synchronisation; everything on the caller's stream).
 //   1. packed q | k projections and value projections of x in one GEMM (fp32 outputs);
 //   2. cca_prep_kernel: convolutions, q-k-mean, value shift, L2-norm, key temperature, RoPE;
-//   3. causal attention (the generic flash prefill kernel, key / value heads grouped);
+//   3. causal attention, key / value heads grouped: the flash prefill kernel for bf16 heads of
+//      32, 64 or 128 features over whole 64-token tiles, the generic prefill kernel otherwise;
 //   4. output up-projection.
 #include <math.h>
 #include <string.h>
@@ -20,20 +21,33 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct CcaWs {
   size_t P, V, q, k, v, o, total;
+  int dqp;      // > 0: attention on the flash prefill kernel, heads padded to dqp features
 };
+
+// The flash prefill kernel takes bf16 heads of 64 or 128 features and whole 64-token tiles;
+// heads of 32 features are zero-padded to 64 (the padding adds nothing to the scores, and
+// the padded value features are not stored).  Other shapes use the generic kernel.
+int flash_width(const mla_cca_dims* d, int S) {
+  if (d->dtype != MLA_DTYPE_BF16 || S <= 0) return 0;
+  const int dqp = d->head_dim == 32 ? 64 : d->head_dim;
+  return prefill_fast_supported(dqp, 0, dqp, S) ? dqp : 0;
+}
 
 CcaWs cca_layout(const mla_cca_dims* d, int B, int S) {
   CcaWs w{};
   const size_t rows = (size_t)B * S;
   const size_t es = d->dtype == MLA_DTYPE_BF16 ? 2 : 4;
   const size_t Lq = (size_t)d->n_heads * d->head_dim, Lkv = (size_t)d->n_kv_heads * d->head_dim;
+  w.dqp = flash_width(d, S);
+  const size_t wq = (size_t)d->n_heads * (w.dqp ? w.dqp : d->head_dim);
+  const size_t wkv = (size_t)d->n_kv_heads * (w.dqp ? w.dqp : d->head_dim);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
   w.P = take(rows * (Lq + Lkv) * 4);
   w.V = take(rows * Lkv * 4);
-  w.q = take(rows * Lq * es);
-  w.k = take(rows * Lkv * es);
-  w.v = take(rows * Lkv * es);
+  w.q = take(rows * wq * es);
+  w.k = take(rows * wkv * es);
+  w.v = take(rows * wkv * es);
   w.o = take(rows * Lq * es);
   w.total = off;
   return w;
@@ -147,9 +161,35 @@ mla_status mla_cca_prefill(const mla_cca_dims* d, const mla_cca_weights* w, cons
   cp.sqrt_dh = (float)sqrt((double)dh);
   cp.key_gain = (float)exp((double)w->key_temperature);
   make_rope_table(&cp.rope, dh, d->rope_base);
+  cp.flash = lay.dqp > 0 ? 1 : 0;
+  cp.dqp = lay.dqp;
   if (launch_cca_prep(cp, bf, st) != hipSuccess) return MLA_ERR_HIP;
 
   // 3. causal softmax attention inside the latent, scale d_h^-1/2
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+  if (lay.dqp) {
+    FlashParams fp;
+    memset(&fp, 0, sizeof(fp));
+    fp.q = cp.q;
+    fp.k = cp.k;
+    fp.kr = nullptr;
+    fp.vt = cp.v;
+    fp.o = at(ws, lay.o);
+    fp.B = B;
+    fp.S = S;
+    fp.T = S;
+    fp.q_off = 0;
+    fp.H = Hq;
+    fp.dn = lay.dqp;
+    fp.d_rope = 0;
+    fp.scale_log2 = scale_log2;
+    fp.kv_group = Hq / Hkv;
+    fp.dv_out = dh;
+    if (launch_prefill_fast(fp, st) != hipSuccess) return MLA_ERR_HIP;
+    GemmParams go = gemm_rows(fp.o, Lq, M, Lq);
+    go.seg[0] = seg(w->w_o, Lq, E, y, E, true);
+    return launch_gemm(go, 1, bf, st) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
   int dqp, dvp;
   prefill_supported(bf, dh, dh, &dqp, &dvp);
   PrefillParams pp;
@@ -168,7 +208,7 @@ mla_status mla_cca_prefill(const mla_cca_dims* d, const mla_cca_weights* w, cons
   pp.d_rope = 0;
   pp.dv = dh;
   pp.kv_group = Hq / Hkv;
-  pp.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+  pp.scale_log2 = scale_log2;
   if (launch_prefill(pp, bf, dqp, dvp, st) != hipSuccess) return MLA_ERR_HIP;
 
   // 4. y = o W_o^T

@@ -197,6 +197,10 @@ struct FlashParams {
   int T, q_off;             // queries per sequence and the position of the first (T = S, 0: prefill)
   float scale_log2;
   int ntq;                  // query tiles per (sequence, head); set by the launcher
+  int kv_group;             // query heads per key / value head (0 or 1: one each); k and vt
+                            // then hold H / kv_group heads
+  int dv_out;               // value features stored per head in o (0: all dn; else a multiple of
+                            // 32 -- the rest are zero-padding of narrower heads)
 };
 bool prefill_fast_supported(int dn, int d_rope, int dv, int S);
 hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s);
@@ -220,6 +224,10 @@ struct CcaPrepParams {
   int qk_mean, value_shift;
   float sqrt_dh, key_gain;  // sqrt(d_h) and exp(beta)
   RopeTable rope;           // half-split frequencies of width d_h
+  // 0: q / k / v rows [B*S][heads][d_h].  1: the flash prefill layouts with heads padded with
+  // zeros to dqp features: q [B*S][Hq][dqp], k head-major [B][Hkv][S][dqp], values transposed
+  // per head [B][Hkv][dqp][S] with the tokens of each 16-group in the order 0-3, 8-11, 4-7, 12-15
+  int flash, dqp;
 };
 constexpr int kCcaMaxKernel = 8;
 constexpr int kCcaMaxHeadDim = 128;

@@ -23,7 +23,29 @@ void make_rope_table(RopeTable* t, int dim, float base) {
   }
 }
 
-int device_cu_count() { return 256; }
+// Compute units of the current device, queried once per device.  The split plans (and so
+// the workspace sizes) follow it; mla_workspace_bytes and the launch that uses the workspace
+// must therefore run with the same device current.  Without a usable device (a host that
+// only sizes buffers) the plans take the 256 compute units of one MI355X.
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 }  // namespace mla
 
@@ -33,9 +55,6 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr float kLog2e = 1.4426950408889634f;
-// Compute units of one MI355X; the split plan (and hence the workspace size) is a pure
-// function of the shapes so that mla_workspace_bytes() needs no device query.
-constexpr int kCUs = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -79,6 +98,7 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
   if (!sp.ok) return sp;
   sp.head_tiles = cdiv(hpb, 32 * sp.nw);
   sp.fast_variant = fast_variant_for(d);
+  const int kCUs = device_cu_count();
   const int ntok = max_ctx + 1;
   int chunk;
   if (sp.fast_variant >= 0) {

@@ -101,7 +101,9 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
   const int qwa = p.q_off + qw;                         // its position
   const int kend = min(S, p.q_off + q0 + FQ);           // keys 0 .. kend-1 (multiple of 64)
   const int ntiles = kend / FK;
-  const long long bh = (long long)b * p.H + h;
+  // key / value head of this query head (grouped heads share one)
+  const int kvg = p.kv_group > 1 ? p.kv_group : 1;
+  const long long bh = (long long)b * (p.H / kvg) + h / kvg;
 
   // ---- Q^T fragments: query 32 qb + col of the wave, features 16 ks + 8 half .. +7 ----
   Frag<bf16> qf[QB][C::KS];
@@ -401,11 +403,13 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
     const float inv = 1.f / lt;
     const int qi = qw + 32 * qb + col;
     if (qi >= p.T) continue;
-    bf16* op = reinterpret_cast<bf16*>(p.o) + (((long long)b * p.T + qi) * p.H + h) * C::DV + 4 * half;
+    const int dvo = p.dv_out > 0 ? p.dv_out : C::DV;
+    bf16* op = reinterpret_cast<bf16*>(p.o) + (((long long)b * p.T + qi) * p.H + h) * dvo + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        if (32 * db >= dvo) continue;
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][qb][4 * g + e] * inv);
@@ -433,6 +437,9 @@ hipError_t launch_flash(const FlashParams& pin, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s) {
+  const int kvg = p.kv_group > 1 ? p.kv_group : 1;
+  if (p.H % kvg) return hipErrorInvalidValue;
+  if (p.dv_out < 0 || p.dv_out > p.dn || p.dv_out % 32) return hipErrorInvalidValue;
   if (p.dn == 128 && p.d_rope == 64) return launch_flash<128, 64, kFlashQB>(p, s);
   if (p.dn == 128 && p.d_rope == 0) return launch_flash<128, 0, kFlashQB>(p, s);
   if (p.dn == 64 && p.d_rope == 0) return launch_flash<64, 0, kFlashQB>(p, s);

@@ -365,7 +365,6 @@ void plan_splits(int M, int N, int K, int groups, int cols, int slots, int unit,
 }
 
 constexpr int kStreamKT = 64;
-constexpr int kMinBlocks = 384;          // enough resident blocks to keep HBM busy
 constexpr int kMinStagesPerSlab = 4;
 
 bool use_stream(int K) { return K % kStreamKT == 0; }
@@ -375,7 +374,6 @@ struct SkinnyPlan {
   bool deep = false;   // one block per CU: 128-row tiles take four stages instead of three
 };
 
-constexpr int kCUs = 256;                 // compute units of one MI355X
 constexpr int kLongSlab = 2048;           // K per block from which one block per CU pays
 
 // Streaming plan: the weight-row tile (32, 64 or 128 rows) and the number of K slabs that
@@ -387,6 +385,8 @@ constexpr int kLongSlab = 2048;           // K per block from which one block pe
 // inside one tile, whose epilogue reads the partner column from LDS (64 when a segment is
 // rotated half-split, 32 otherwise).
 SkinnyPlan plan_stream(int M, int N, int K, int groups, int min_rows = 32) {
+  const int kCUs = device_cu_count();
+  const int kMinBlocks = kCUs * 3 / 2;    // enough resident blocks to keep HBM busy
   SkinnyPlan best{M > 64 ? 64 : 128, 1, K};
   double best_cost = 1e300;
   int best_blocks = 0;

@@ -2,7 +2,8 @@
 
 [CCA page] frankenstein-transformer docs, ``latent/cca_attn``: ``CCAAttention.forward`` and
 ``CCGQAAttention.forward`` in decoder mode.  The library's mla_cca_prefill runs on seeded
-inputs; the oracle (oracle/cca_oracle.py) recomputes whole sequences.  Tolerances as for
+inputs; the oracle (oracle/cca_oracle.py) recomputes whole sequences.  Sequences of whole 64-token
+tiles run attention on the flash prefill kernel, others on the generic one.  Tolerances as for
 the MLA workloads: fp32 rel-L2 <= 1e-5; bf16-in / fp32-accumulate rel-L2 <= 1e-2 and
 max-abs <= 3e-2 per sequence.  Sizes span several 16-token preparation blocks, 128-query
 attention tiles and 64-key tiles with ragged tails.
@@ -56,6 +57,12 @@ VARIANTS = [
     (GQA_S, dict(num_conv_layers=1, qk_mean=False)), (CCA_S, dict(value_shift=False, num_conv_layers=0)),
     (GQA_S.replace(name="ccgqa_dh32", head_dim=32), {}),
     (CCA_S.replace(name="cca_s1", seq=1), {}),
+    # whole 64-token tiles: attention on the flash prefill kernel (heads of 32 features padded
+    # to 64; 64 and 128 as they are), a partial second 256-query tile
+    (CCA_S.replace(name="cca_s320", seq=320), {}),
+    (GQA_S.replace(name="ccgqa_s320", seq=320), {}),
+    (GQA_S.replace(name="ccgqa_dh128_s256", head_dim=128, seq=256), {}),
+    (GQA_S.replace(name="ccgqa_dh32_s64", head_dim=32, seq=64), dict(num_conv_layers=1, value_shift=False)),
 ]
 
 
@@ -70,10 +77,11 @@ def test_cca_prefill(gu, cfg, kw):
         gu.assert_close(y[b], C.forward(xs[b], prob.weights, cfg), cfg.dtype, f"y b={b}")
 
 
-def test_cca_prefill_is_causal(gu):
+@pytest.mark.parametrize("seq", [300, 320], ids=["generic", "flash"])
+def test_cca_prefill_is_causal(gu, seq):
     """Perturbing the last tokens leaves every earlier output row unchanged (bitwise: the
     earlier rows' arithmetic does not read the later tokens)."""
-    cfg = GQA_S
+    cfg = GQA_S.replace(seq=seq)
     xs = [S.make_x(cfg, b, cfg.seq) for b in range(cfg.batch)]
     y1, _ = _run(gu, cfg, xs)
     xs2 = [x.copy() for x in xs]
