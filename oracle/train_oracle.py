@@ -14,12 +14,14 @@ The layer is the decoupled-RoPE family of mla_oracle (query latent, rotary key s
 the heads); its forward is mla_oracle.forward with the attention weights P replaced by
 P * keep / (1 - p).
 
-Dropout draws come from Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
-numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator: the keep decision of
+Dropout draws come from SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014), used as a counter-based generator: the keep decision of
 attention weight (sequence b, head h, query i, key j) is
-    r = Philox4x64-10(counter = (j // 4, i, b H + h, 0), key = (seed, 0))[j % 4]
+    n = (b H + h) 2^40 + i 2^20 + j
+    r = mix64(seed + (n + 1) gamma)            (the (n+1)-th output of SplitMix64 from state seed)
     keep  <=>  (r >> 32) >= floor(p 2^32)
-so any element can be drawn on its own, in any order, on either side.
+with gamma = 0x9E3779B97F4A7C15 and mix64 the generator's output function, so any element
+can be drawn on its own, in any order, on either side.  (The pages name no generator.)
 
 The backward is the chain rule through that forward, written out step by step (reverse
 order of the forward).  With o = Pd v and Pd = P keep / (1 - p):
@@ -38,36 +40,24 @@ from . import mla_oracle as O
 
 F64 = np.float64
 U64 = np.uint64
-_M32 = U64(0xFFFFFFFF)
-PHILOX_M = (U64(0xD2E7470EE14C6C93), U64(0xCA5A826395121157))   # round multipliers
-PHILOX_W = (U64(0x9E3779B97F4A7C15), U64(0xBB67AE8584CAA73B))   # key increments (Weyl)
+SM_GAMMA = U64(0x9E3779B97F4A7C15)                               # state increment
+SM_MUL = (U64(0xBF58476D1CE4E5B9), U64(0x94D049BB133111EB))      # output-function multipliers
 
 
-def _mulhilo(a: np.ndarray, b) -> tuple:
-    """Full 128-bit product of 64-bit words: (high, low) halves (numpy uint64 arrays)."""
-    a = np.asarray(a, dtype=U64)
-    b = U64(b)
-    a0, a1 = a & _M32, a >> U64(32)
-    b0, b1 = b & _M32, b >> U64(32)
-    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
-    mid = (p00 >> U64(32)) + (p01 & _M32) + (p10 & _M32)
-    hi = p11 + (p01 >> U64(32)) + (p10 >> U64(32)) + (mid >> U64(32))
-    return hi, a * b
-
-
-def philox4x64(c0, c1, c2, c3, k0, k1, rounds: int = 10):
-    """Philox4x64-R on arrays of counters (broadcast): ten rounds of two 64 x 64 -> 128-bit
-    products, the high halves xored with the other counter words and the key, the key
-    bumped by the Weyl constants between rounds."""
-    c0, c1, c2, c3 = (np.asarray(c, dtype=U64) for c in (c0, c1, c2, c3))
-    k0, k1 = U64(k0), U64(k1)
+def splitmix64(state, n):
+    """Output n + 1 of SplitMix64 started at `state` (arrays broadcast): the state advanced
+    n + 1 times by gamma, then the output function: two xor-shift-multiply steps and a final
+    xor-shift, all modulo 2^64."""
     with np.errstate(over="ignore"):
-        for _ in range(rounds):
-            hi0, lo0 = _mulhilo(c0, PHILOX_M[0])
-            hi1, lo1 = _mulhilo(c2, PHILOX_M[1])
-            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
-            k0, k1 = k0 + PHILOX_W[0], k1 + PHILOX_W[1]
-    return c0, c1, c2, c3
+        z = np.asarray(state, dtype=U64) + (np.asarray(n, dtype=U64) + U64(1)) * SM_GAMMA
+        z = (z ^ (z >> U64(30))) * SM_MUL[0]
+        z = (z ^ (z >> U64(27))) * SM_MUL[1]
+        return z ^ (z >> U64(31))
+
+
+def element_counter(b: int, H: int, h: int, i, j):
+    """Counter of attention weight (b, h, i, j): (b H + h) 2^40 + i 2^20 + j (S < 2^20)."""
+    return (U64(b * H + h) << U64(40)) + (np.asarray(i, dtype=U64) << U64(20)) + np.asarray(j, dtype=U64)
 
 
 def keep_threshold(p: float) -> int:
@@ -81,11 +71,8 @@ def dropout_keep(seed: int, b: int, H: int, h: int, n_q: int, n_k: int, p: float
     """Keep mask [n_q, n_k] of head h of sequence b (queries 0..n_q-1, keys 0..n_k-1)."""
     if keep_threshold(p) == 0:
         return np.ones((n_q, n_k), dtype=bool)          # every draw passes a zero threshold
-    i = np.arange(n_q, dtype=U64)[:, None]
-    j = np.arange(n_k, dtype=U64)[None, :]
-    words = philox4x64(j >> U64(2), i, U64(b * H + h), U64(0), U64(seed), U64(0))
-    sel = (j & U64(3)).astype(np.int64)
-    r = np.choose(np.broadcast_to(sel, (n_q, n_k)), [np.broadcast_to(w, (n_q, n_k)) for w in words])
+    n = element_counter(b, H, h, np.arange(n_q)[:, None], np.arange(n_k)[None, :])
+    r = splitmix64(U64(seed), n)
     return (r >> U64(32)) >= U64(keep_threshold(p))
 
 
