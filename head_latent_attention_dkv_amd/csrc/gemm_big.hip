@@ -73,8 +73,22 @@ __global__ void __launch_bounds__(64 * NW, BigCfg<NW>::MINB) gemm_big_kernel(Gem
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / (NW / 4), wn = wave % (NW / 4);   // 64-row block wm, 128-column block wn
   const int col = lane & 31, half = lane >> 5;
-  const int n0 = blockIdx.x * C::BN;
-  const int m0 = blockIdx.y * GBM;
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (DIRECT && gridDim.z == 1 && gridDim.x % 8 == 0) {
+    // Workgroups go to the 8 XCDs in turn (linear block L to XCD L % 8).  XCD k takes the
+    // column tiles k NT/8 .. (k+1) NT/8 - 1, in phases of up to 16 tiles, each phase over all
+    // row tiles: a phase's weight rows (16 x 128 x K bf16, 2 MB at K = 512) stay in the
+    // XCD's L2 while its row tiles stream past, instead of every row tile re-reading the
+    // whole weight from beyond L2.
+    const int NT = gridDim.x, MT = gridDim.y, per = NT / 8;
+    const int pw = per % 16 == 0 ? 16 : per;
+    const int L = by * NT + bx, xcd = L & 7, slot = L >> 3;
+    const int ph = slot / (MT * pw), rem = slot - ph * (MT * pw);
+    by = rem / pw;
+    bx = xcd * per + ph * pw + (rem - by * pw);
+  }
+  const int n0 = bx * C::BN;
+  const int m0 = by * GBM;
   const int z = blockIdx.z;
   const int zo = z / p.zdiv, zi = z - zo * p.zdiv;
   const long long a_goff = zo * p.a_goff[0] + zi * p.a_goff[1];
