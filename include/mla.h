@@ -257,10 +257,12 @@ mla_status mla_prefill_chunk(const mla_dims* dims, const mla_weights* w, const v
  * ([DSV2 page] ``MultiHeadLatentAttention.__init__`` / ``forward``: dropout after the
  * softmax, before the product with the values; [MLA page] ``MLAAttention``: the same).
  * Family: MLA_ROPE_DECOUPLED_INTERLEAVED with a query latent (r_q > 0), one latent head.
- * Dropout draws: Philox4x64-10 (Salmon et al., SC 2011); the weight of query i on key j in
- * head h of sequence b is kept when the upper 32 bits of word j % 4 of the block at counter
- * (j / 4, i, b * n_heads + h, 0), key (seed, 0) are >= floor(p * 2^32); a kept weight is
- * scaled by 1 / (1 - p).  The same (seed, p) must be passed to the forward and the backward.
+ * Dropout draws: SplitMix64 (Steele, Lea, Flood, OOPSLA 2014); the weight of query i on key
+ * j in head h of sequence b is kept when bits 16 (j % 4) .. 16 (j % 4) + 15 of the
+ * generator's output n + 1 from state seed, n = (b * n_heads + h) * 2^38 + i * 2^18 + j / 4,
+ * are >= floor(p * 2^16); a kept weight is scaled by 1 / (1 - p).  The same (seed, p) must be
+ * passed to the forward and the backward.  B * n_heads <= 2^24 and S <= 2^20 (else
+ * MLA_ERR_SHAPE).
  * ------------------------------------------------------------------------------------- */
 
 /* Gradients of sum(dy * y) with respect to x and the weights (float32, shapes as the inputs /

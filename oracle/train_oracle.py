@@ -15,13 +15,16 @@ the heads); its forward is mla_oracle.forward with the attention weights P repla
 P * keep / (1 - p).
 
 Dropout draws come from SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom
-number generators", OOPSLA 2014), used as a counter-based generator: the keep decision of
-attention weight (sequence b, head h, query i, key j) is
-    n = (b H + h) 2^40 + i 2^20 + j
+number generators", OOPSLA 2014), used as a counter-based generator.  One 64-bit draw
+serves four consecutive keys, 16 bits each: for attention weight (sequence b, head h,
+query i, key j)
+    n = (b H + h) 2^38 + i 2^18 + floor(j / 4)
     r = mix64(seed + (n + 1) gamma)            (the (n+1)-th output of SplitMix64 from state seed)
-    keep  <=>  (r >> 32) >= floor(p 2^32)
-with gamma = 0x9E3779B97F4A7C15 and mix64 the generator's output function, so any element
-can be drawn on its own, in any order, on either side.  (The pages name no generator.)
+    u = bits 16 (j mod 4) .. 16 (j mod 4) + 15 of r
+    keep  <=>  u >= floor(p 2^16)
+with gamma = 0x9E3779B97F4A7C15 and mix64 the generator's output function, so any group
+of four keys can be drawn on its own, in any order, on either side.  (The pages name no
+generator; the keep probability is 1 - floor(p 2^16) / 2^16, within 2^-16 of 1 - p.)
 
 The backward is the chain rule through that forward, written out step by step (reverse
 order of the forward).  With o = Pd v and Pd = P keep / (1 - p):
@@ -56,24 +59,27 @@ def splitmix64(state, n):
 
 
 def element_counter(b: int, H: int, h: int, i, j):
-    """Counter of attention weight (b, h, i, j): (b H + h) 2^40 + i 2^20 + j (S < 2^20)."""
-    return (U64(b * H + h) << U64(40)) + (np.asarray(i, dtype=U64) << U64(20)) + np.asarray(j, dtype=U64)
+    """Counter of the draw of attention weight (b, h, i, j): (b H + h) 2^38 + i 2^18 + j // 4
+    (S <= 2^20, B H <= 2^24)."""
+    return ((U64(b * H + h) << U64(38)) + (np.asarray(i, dtype=U64) << U64(18))
+            + (np.asarray(j, dtype=U64) >> U64(2)))
 
 
 def keep_threshold(p: float) -> int:
-    """A weight is kept when the upper 32 bits of its draw are >= floor(p 2^32)."""
+    """A weight is kept when its 16-bit field of the draw is >= floor(p 2^16)."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must be in [0, 1)")
-    return int(np.floor(p * 4294967296.0))
+    return int(np.floor(p * 65536.0))
 
 
 def dropout_keep(seed: int, b: int, H: int, h: int, n_q: int, n_k: int, p: float) -> np.ndarray:
     """Keep mask [n_q, n_k] of head h of sequence b (queries 0..n_q-1, keys 0..n_k-1)."""
     if keep_threshold(p) == 0:
         return np.ones((n_q, n_k), dtype=bool)          # every draw passes a zero threshold
-    n = element_counter(b, H, h, np.arange(n_q)[:, None], np.arange(n_k)[None, :])
-    r = splitmix64(U64(seed), n)
-    return (r >> U64(32)) >= U64(keep_threshold(p))
+    i, j = np.arange(n_q)[:, None], np.arange(n_k)[None, :]
+    r = splitmix64(U64(seed), element_counter(b, H, h, i, j))
+    field = (r >> (U64(16) * (np.asarray(j, dtype=U64) & U64(3)))) & U64(0xFFFF)
+    return field >= U64(keep_threshold(p))
 
 
 def _check_family(d: O.Dims):

@@ -67,16 +67,18 @@ def test_keep_fraction_is_binomial(p):
 
 
 def test_keep_mask_element_addressing():
-    """Element (i, j) of head h of sequence b uses output n + 1 of SplitMix64 from the seed,
-    n = (b H + h) 2^40 + i 2^20 + j (the state advanced with Python integers here)."""
+    """Element (i, j) of head h of sequence b uses bits 16 (j % 4) .. + 15 of output n + 1 of
+    SplitMix64 from the seed, n = (b H + h) 2^38 + i 2^18 + j // 4 (the state advanced with
+    Python integers here)."""
     p, seed, b, H, h = 0.4, 99, 1, 3, 2
     keep = T.dropout_keep(seed, b, H, h, 6, 13, p)
     thr = T.keep_threshold(p)
+    assert thr == int(0.4 * 65536)
     gamma, mask = 0x9E3779B97F4A7C15, (1 << 64) - 1
-    for i, j in [(0, 0), (5, 12), (3, 7), (2, 4)]:
-        n = ((b * H + h) << 40) + (i << 20) + j
+    for i, j in np.ndindex(*keep.shape):
+        n = ((b * H + h) << 38) + (i << 18) + (j // 4)
         w = int(T.splitmix64(np.uint64((seed + n * gamma) & mask), np.uint64(0)))
-        assert keep[i, j] == (w >> 32 >= thr)
+        assert keep[i, j] == (((w >> (16 * (j % 4))) & 0xFFFF) >= thr)
 
 
 @pytest.mark.parametrize("cfg", [TINY, SMALL_DEC], ids=lambda c: c.name)
