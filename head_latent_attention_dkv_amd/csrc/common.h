@@ -208,36 +208,27 @@ __device__ __forceinline__ float wave_sum32(float v) { return v + __shfl_xor(v, 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int round_up(int a, int b) { return cdiv(a, b) * b; }
 
-// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011): ten rounds of two 64 x 64 -> 128-bit
-// products of counter words by fixed multipliers, the high halves xored into the other
-// words with the key, the key bumped by Weyl constants between rounds.  Returns the block's
-// four words in c[0..3].
-__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
-  const uint64_t m0 = 0xD2E7470EE14C6C93ull, m1 = 0xCA5A826395121157ull;
-  const uint64_t w0 = 0x9E3779B97F4A7C15ull, w1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(m0, c[0]), lo0 = m0 * c[0];
-    const uint64_t hi1 = __umul64hi(m1, c[2]), lo1 = m1 * c[2];
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
-    k0 += w0;
-    k1 += w1;
-  }
+// Dropout draws: SplitMix64 (Steele, Lea, Flood, OOPSLA 2014) used as a counter-based
+// generator.  One draw serves the four attention weights (query i, keys 4 j4 .. 4 j4 + 3) of
+// head stream zh = b H + h: the generator's output n + 1 from state seed, n = zh 2^38 +
+// i 2^18 + j4, i.e. the state seed + (n + 1) gamma through the output function (two
+// xor-shift-multiply steps, a final xor-shift).  Key 4 j4 + e uses bits 16 e .. 16 e + 15 and
+// is kept when they are >= thr = floor(p 2^16).
+__device__ __forceinline__ uint64_t dropout_draw(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
 }
-
-// Dropout keep bits of the four attention weights (query i, keys 4 j4 .. 4 j4 + 3) of head
-// stream zh (= b H + h): bit e set when key 4 j4 + e is kept, i.e. when the upper 32 bits of
-// word e of Philox4x64-10(counter (j4, i, zh, 0), key (seed, 0)) are >= thr.
+__device__ __forceinline__ uint64_t dropout_counter4(int zh, int i, int j4) {
+  return ((uint64_t)(uint32_t)zh << 38) + ((uint64_t)(uint32_t)i << 18) + (uint64_t)(uint32_t)j4;
+}
+// Keep bits of the four weights (query i, keys 4 j4 .. 4 j4 + 3): bit e for key 4 j4 + e.
 __device__ __forceinline__ unsigned dropout_keep4(uint64_t seed, uint32_t thr, int j4, int i, int zh) {
-  uint64_t c[4] = {(uint64_t)j4, (uint64_t)i, (uint64_t)zh, 0ull};
-  philox4x64_10(c, seed, 0ull);
+  const uint64_t r = dropout_draw(seed, dropout_counter4(zh, i, j4));
   unsigned bits = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) bits |= ((uint32_t)(c[e] >> 32) >= thr ? 1u : 0u) << e;
+  for (int e = 0; e < 4; ++e) bits |= ((uint32_t)(r >> (16 * e)) & 0xFFFFu) >= thr ? (1u << e) : 0u;
   return bits;
 }
 

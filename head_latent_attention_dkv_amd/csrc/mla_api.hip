@@ -1006,17 +1006,20 @@ TrainWs train_ws_layout(const mla_dims* d, int B, int S) {
   return w;
 }
 
-mla_status train_check(const mla_dims* d, float p) {
+mla_status train_check(const mla_dims* d, float p, int B, int S) {
   mla_status s = mla_validate(d);
   if (s != MLA_OK) return s;
   if (d->rope_mode != MLA_ROPE_DECOUPLED_INTERLEAVED || d->r_q <= 0 || d->n_latent_heads != 1) return MLA_ERR_UNSUPPORTED;
   if (!(p >= 0.f && p < 1.f)) return MLA_ERR_INVALID_ARG;
+  // the dropout counter packs (b H + h, query, key / 4) into 26, 20 and 18 bits
+  if ((long long)B * d->n_heads > (1ll << 24) || S > (1 << 20)) return MLA_ERR_SHAPE;
   return MLA_OK;
 }
 
+// keep when the 16-bit field of the draw is >= floor(p 2^16)
 uint32_t keep_threshold(float p) {
-  const double t = floor((double)p * 4294967296.0);
-  return t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+  const double t = floor((double)p * 65536.0);
+  return t >= 65535.0 ? 65535u : (uint32_t)t;
 }
 
 // one strided product (batch 1) of the backward
@@ -1050,18 +1053,18 @@ SgemmParams sg(const void* A, bool a_f32, long long sAm, long long sAk, const vo
 extern "C" {
 
 size_t mla_train_saved_bytes(const mla_dims* d, int32_t B, int32_t S) {
-  if (train_check(d, 0.f) != MLA_OK || B <= 0 || S <= 0) return 0;
+  if (B <= 0 || S <= 0 || train_check(d, 0.f, B, S) != MLA_OK) return 0;
   return train_saved_layout(d, B, S).total;
 }
 
 size_t mla_train_workspace_bytes(const mla_dims* d, int32_t B, int32_t S) {
-  if (train_check(d, 0.f) != MLA_OK || B <= 0 || S <= 0) return 0;
+  if (B <= 0 || S <= 0 || train_check(d, 0.f, B, S) != MLA_OK) return 0;
   return train_ws_layout(d, B, S).total;
 }
 
 mla_status mla_train_forward(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t S,
                              float dropout_p, uint64_t seed, float* y, void* saved, size_t saved_bytes, void* stream) {
-  mla_status s = train_check(d, dropout_p);
+  mla_status s = train_check(d, dropout_p, B, S);
   if (s != MLA_OK) return s;
   if (!x || !y || B <= 0 || S <= 0) return MLA_ERR_INVALID_ARG;
   if ((s = check_weights(d, w, true, true, true)) != MLA_OK) return s;
@@ -1102,7 +1105,7 @@ mla_status mla_train_forward(const mla_dims* d, const mla_weights* w, const void
 mla_status mla_train_backward(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t S,
                               float dropout_p, uint64_t seed, const float* dy, const void* saved, size_t saved_bytes,
                               const mla_grads* g, void* ws, size_t ws_bytes, void* stream) {
-  mla_status s = train_check(d, dropout_p);
+  mla_status s = train_check(d, dropout_p, B, S);
   if (s != MLA_OK) return s;
   if (!x || !dy || !g || B <= 0 || S <= 0) return MLA_ERR_INVALID_ARG;
   if (!g->dx || !g->dw_dq || !g->dw_uq || !g->dw_qr || !g->dw_dkv || !g->dw_kr || !g->dw_uk || !g->dw_uv || !g->dw_o)

@@ -6,7 +6,7 @@
 //     block for all (sequence, head) pairs at once, and the weight and input gradients;
 //   * bwd_p_kernel / bwd_ds_kernel: the softmax and dropout steps of the attention backward
 //     between those products (P from the saved log-sum-exp, the dropout mask redrawn from
-//     the same Philox counters as the forward);
+//     the same generator counters as the forward);
 //   * rowdot_kernel (rowsum(dO o)), rope_bwd_kernel (rotations by the negative angle, the
 //     rotary key's gradient summed over heads), fill_f32_kernel.
 #include "common.h"
