@@ -19,7 +19,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmla.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["mla_api.hip", "gemm.hip", "gemm_big.hip", "skinny.hip", "gemm_kmajor.hip", "decode.hip", "decode_fast.hip",
-           "prefill.hip", "prefill_fast.hip", "cca.hip", "cca_api.hip", "train.hip"]
+           "prefill.hip", "prefill_fast.hip", "cca.hip", "cca_api.hip", "train.hip", "train_flash.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

@@ -201,6 +201,11 @@ struct FlashParams {
                             // then hold H / kv_group heads
   int dv_out;               // value features stored per head in o (0: all dn; else a multiple of
                             // 32 -- the rest are zero-padding of narrower heads)
+  // training forward (dropout on the attention weights, per-row log-sum-exp); zero otherwise
+  uint32_t keep_thr;        // keep when a draw's 16-bit field is >= keep_thr (0: no dropout)
+  float keep_scale;         // 1 / (1 - p)
+  unsigned long long seed;
+  float* lse;               // [B][H][T] log2 of each row's softmax normaliser (scaled scores), or NULL
 };
 bool prefill_fast_supported(int dn, int d_rope, int dv, int S);
 hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s);
@@ -232,6 +237,34 @@ struct CcaPrepParams {
 constexpr int kCcaMaxKernel = 8;
 constexpr int kCcaMaxHeadDim = 128;
 hipError_t launch_cca_prep(const CcaPrepParams& p, bool use_bf16, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Flash-style attention backward of the training step (bf16, decoupled-RoPE heads of
+// 128 + 64 query / key features and 128 value features, S a multiple of 64)
+// ---------------------------------------------------------------------------
+struct TrainBwdParams {
+  const bf16* q;            // [B*S][H][192] queries (rotary part rotated)
+  const bf16* kf;           // [B][H][S][128] decompressed keys, head-major
+  const bf16* kr;           // [B*S][64] rotated rotary keys (shared by the heads)
+  const bf16* vt;           // [B][H][128][S] values transposed per head (16-token groups 0-3, 8-11, 4-7, 12-15)
+  const bf16* dO;           // [B*S][H][128] output gradient (bf16)
+  const float* lse;         // [B][H][S] log2 of each row's softmax normaliser (scaled scores)
+  const float* D;           // [B][H][S] rowsum(dO o)
+  float* dkc;               // [B*S][H][128] key gradient, decompressed part
+  float* dkr;               // [B*S][H][64] key gradient, rotary part, per head
+  float* dv;                // [B*S][H][128]
+  float* dqc;               // [B*S][H][128]
+  float* dqr;               // [B*S][H][64]
+  int B, S, H;
+  float scale_log2, tau;    // tau log2(e), tau (the softmax scale)
+  uint32_t keep_thr;        // dropout (0: none)
+  float keep_scale;
+  unsigned long long seed;
+};
+bool train_flash_supported(int dn, int d_rope, int dv, int S);
+hipError_t launch_train_bwd(const TrainBwdParams& p, hipStream_t s);
+hipError_t launch_train_do_prep(const float* dO, const void* o, void* dO16, float* D, int B, int S, int H,
+                                hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Training backward

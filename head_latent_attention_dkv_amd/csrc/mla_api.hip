@@ -974,8 +974,18 @@ int train_query_block(const mla_dims* d, int B, int S) {
   return (int)(tq < S ? tq : S);
 }
 
+// The bf16 decoupled-RoPE heads of 128 + 64 features over whole 64-token tiles train on the
+// flash kernels: the forward on the flash prefill kernel with dropout (keys and values saved
+// in its head-major / transposed layouts), the attention backward on train_bwd_kv_kernel and
+// train_bwd_q_kernel.  Other shapes use the generic prefill kernel and the blockwise
+// backward below.
+bool train_flash(const mla_dims* d, int S) {
+  return is_bf16(d) && train_flash_supported(d->d_nope, d->d_rope, d->d_v, S) &&
+         prefill_fast_supported(d->d_nope, d->d_rope, d->d_v, S);
+}
+
 struct TrainWs {
-  size_t dO, D, dqc, dqr, dkc, dkr, dv, dqr0, dkr0, dcq, dc, sbuf, pbuf, pdbuf, dsbuf, total;
+  size_t dO, D, dqc, dqr, dkc, dkr, dv, dqr0, dkr0, dcq, dc, sbuf, pbuf, pdbuf, dsbuf, dO16, total;
   int tq;
 };
 
@@ -983,8 +993,9 @@ TrainWs train_ws_layout(const mla_dims* d, int B, int S) {
   TrainWs w{};
   const size_t rows = (size_t)B * S, es = esize(d);
   const int H = d->n_heads, dn = d->d_nope, dr = d->d_rope, dv = d->d_v;
+  const bool flash = train_flash(d, S);
   w.tq = train_query_block(d, B, S);
-  const size_t blk = (size_t)B * H * w.tq * S;
+  const size_t blk = flash ? 0 : (size_t)B * H * w.tq * S;   // score blocks of the blockwise backward
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
   w.dO = take(rows * H * dv * 4);
@@ -1002,6 +1013,7 @@ TrainWs train_ws_layout(const mla_dims* d, int B, int S) {
   w.pbuf = take(blk * es);
   w.pdbuf = take(blk * es);
   w.dsbuf = take(blk * es);
+  w.dO16 = take(flash ? rows * H * dv * 2 : 0);
   w.total = off;
   return w;
 }
@@ -1074,8 +1086,33 @@ mla_status mla_train_forward(const mla_dims* d, const mla_weights* w, const void
   const int M = B * S;
   if (run_queries(d, w, x, M, S, nullptr, at(saved, sv.cq), at(saved, sv.q), st) != hipSuccess) return MLA_ERR_HIP;
   if (run_latent(d, w, x, B, S, nullptr, nullptr, at(saved, sv.c), at(saved, sv.kr), st) != hipSuccess) return MLA_ERR_HIP;
-  if (run_kv_up(d, w, at(saved, sv.c), false, 0, B, S, at(saved, sv.kc), at(saved, sv.v), st, false) != hipSuccess)
+  const bool flash = train_flash(d, S);
+  if (run_kv_up(d, w, at(saved, sv.c), false, 0, B, S, at(saved, sv.kc), at(saved, sv.v), st, flash) != hipSuccess)
     return MLA_ERR_HIP;
+  if (flash) {
+    FlashParams fp;
+    memset(&fp, 0, sizeof(fp));
+    fp.q = at(saved, sv.q);
+    fp.k = at(saved, sv.kc);
+    fp.kr = at(saved, sv.kr);
+    fp.kr_bstride = S;
+    fp.vt = at(saved, sv.v);
+    fp.o = at(saved, sv.o);
+    fp.B = B;
+    fp.S = S;
+    fp.T = S;
+    fp.q_off = 0;
+    fp.H = d->n_heads;
+    fp.dn = d->d_nope;
+    fp.d_rope = d->d_rope;
+    fp.scale_log2 = softmax_scale(d) * kLog2e;
+    fp.keep_thr = keep_threshold(dropout_p);
+    fp.keep_scale = (float)(1.0 / (1.0 - (double)dropout_p));
+    fp.seed = seed;
+    fp.lse = reinterpret_cast<float*>(at(saved, sv.lse));
+    if (launch_prefill_fast(fp, st) != hipSuccess) return MLA_ERR_HIP;
+    return hip_status(run_out_proj(d, w, at(saved, sv.o), M, y, st));
+  }
   int dqp, dvp;
   if (!prefill_supported(is_bf16(d), dq_of(d), d->d_v, &dqp, &dvp)) return MLA_ERR_UNSUPPORTED;
   PrefillParams pp;
@@ -1139,76 +1176,106 @@ mla_status mla_train_backward(const mla_dims* d, const mla_weights* w, const voi
   // output projection y = o W_o^T:  dW_o = dy^T o,  dO = dy W_o
   MLA_TRY(GEMM(sg(dy, true, 1, E, o, tf, HV, 1, g->dw_o, HV, E, (int)HV, M, 0.f)));
   MLA_TRY(GEMM(sg(dy, true, E, 1, w->w_o, tf, HV, 1, dO, HV, M, (int)HV, E, 0.f)));
-  MLA_TRY(launch_rowdot(dO, o, D, B, S, H, dv, bf, st));
-  MLA_TRY(launch_fill_f32(dkc, (long long)M * HD, 0.f, st));
-  MLA_TRY(launch_fill_f32(dkr, (long long)M * HR, 0.f, st));
-  MLA_TRY(launch_fill_f32(dV, (long long)M * HV, 0.f, st));
-
-  // attention, one block of queries at a time for every (sequence, head) pair z = b H + h
-  const int tq = lw.tq;
   const float tau = softmax_scale(d);
-  AttnBwdParams ab;
-  memset(&ab, 0, sizeof(ab));
-  ab.S_ = F(lw.sbuf);
-  ab.P = at(ws, lw.pbuf);
-  ab.Pd = at(ws, lw.pdbuf);
-  ab.dS = at(ws, lw.dsbuf);
-  ab.lse = lse;
-  ab.D = D;
-  ab.Z = B * H;
-  ab.S = S;
-  ab.scale_log2 = tau * kLog2e;
-  ab.scale = tau;
-  ab.keep_thr = keep_threshold(dropout_p);
-  ab.keep_scale = (float)(1.0 / (1.0 - (double)dropout_p));
-  ab.seed = seed;
-  // batched operand views: a [rows][H][width] tensor has batch strides (S H width, width)
-  auto batched = [&](SgemmParams p, long long az0, long long az1, long long bz0, long long bz1, long long cz0,
-                     long long cz1) {
-    p.Z = B * H;
-    p.zdiv = H;
-    p.sAz0 = az0;
-    p.sAz1 = az1;
-    p.sBz0 = bz0;
-    p.sBz1 = bz1;
-    p.sCz0 = cz0;
-    p.sCz1 = cz1;
-    return p;
-  };
-  for (int i0 = 0; i0 < S; i0 += tq) {
-    const int T = S - i0 < tq ? S - i0 : tq;          // queries of this block
-    const int Kn = i0 + T;                            // keys they can see
-    const long long blk = (long long)tq * Kn;         // [Tq][Kn] block of one (sequence, head)
-    const char* qb = static_cast<const char*>(q) + (size_t)i0 * HQ * es;
-    ab.i0 = i0;
-    ab.Tq = tq;
-    ab.Kn = Kn;
-    // scores S = q_C k_C^T + q_R k_R^T (unscaled)
-    MLA_TRY(GEMM(batched(sg(qb, tf, HQ, 1, kc, tf, 1, HD, F(lw.sbuf), Kn, T, Kn, dn, 0.f),
-                         (long long)S * HQ, dq, (long long)S * HD, dn, (long long)H * blk, blk)));
-    MLA_TRY(GEMM(batched(sg(static_cast<const char*>(qb) + (size_t)dn * es, tf, HQ, 1, kr, tf, 1, dr, F(lw.sbuf), Kn,
-                            T, Kn, dr, 1.f),
-                         (long long)S * HQ, dq, (long long)S * dr, 0, (long long)H * blk, blk)));
-    MLA_TRY(launch_bwd_p(ab, bf, st));
-    // dV[0:Kn] += Pd^T dO_blk
-    const float* dOb = dO + (size_t)i0 * HV;
-    MLA_TRY(GEMM(batched(sg(ab.Pd, tf, 1, Kn, dOb, true, HV, 1, dV, HV, Kn, dv, T, 1.f), (long long)H * blk, blk,
-                         (long long)S * HV, dv, (long long)S * HV, dv)));
-    // dPd = dO_blk V^T  (into the score buffer)
-    MLA_TRY(GEMM(batched(sg(dOb, true, HV, 1, v, tf, 1, HV, F(lw.sbuf), Kn, T, Kn, dv, 0.f), (long long)S * HV, dv,
-                         (long long)S * HV, dv, (long long)H * blk, blk)));
-    MLA_TRY(launch_bwd_ds(ab, bf, st));
-    // dq_blk = dS k:  decompressed part and rotary part (k_R shared by the heads)
-    MLA_TRY(GEMM(batched(sg(ab.dS, tf, Kn, 1, kc, tf, HD, 1, dqc + (size_t)i0 * HD, HD, T, dn, Kn, 0.f),
-                         (long long)H * blk, blk, (long long)S * HD, dn, (long long)S * HD, dn)));
-    MLA_TRY(GEMM(batched(sg(ab.dS, tf, Kn, 1, kr, tf, dr, 1, dqr + (size_t)i0 * HR, HR, T, dr, Kn, 0.f),
-                         (long long)H * blk, blk, (long long)S * dr, 0, (long long)S * HR, dr)));
-    // dk[0:Kn] += dS^T q_blk (per head; the rotary parts are summed over heads below)
-    MLA_TRY(GEMM(batched(sg(ab.dS, tf, 1, Kn, qb, tf, HQ, 1, dkc, HD, Kn, dn, T, 1.f), (long long)H * blk, blk,
-                         (long long)S * HQ, dq, (long long)S * HD, dn)));
-    MLA_TRY(GEMM(batched(sg(ab.dS, tf, 1, Kn, static_cast<const char*>(qb) + (size_t)dn * es, tf, HQ, 1, dkr, HR,
-                            Kn, dr, T, 1.f),
-                         (long long)H * blk, blk, (long long)S * HQ, dq, (long long)S * HR, dr)));
+  if (train_flash(d, S)) {
+    // flash backward: keys / values as saved in the flash layouts (head-major keys, values
+    // transposed per head)
+    void* dO16 = at(ws, lw.dO16);
+    MLA_TRY(launch_train_do_prep(dO, o, dO16, D, B, S, H, st));
+    TrainBwdParams tb;
+    memset(&tb, 0, sizeof(tb));
+    tb.q = static_cast<const bf16*>(q);
+    tb.kf = static_cast<const bf16*>(kc);
+    tb.kr = static_cast<const bf16*>(kr);
+    tb.vt = static_cast<const bf16*>(v);
+    tb.dO = static_cast<const bf16*>(dO16);
+    tb.lse = lse;
+    tb.D = D;
+    tb.dkc = dkc;
+    tb.dkr = dkr;
+    tb.dv = dV;
+    tb.dqc = dqc;
+    tb.dqr = dqr;
+    tb.B = B;
+    tb.S = S;
+    tb.H = H;
+    tb.scale_log2 = tau * kLog2e;
+    tb.tau = tau;
+    tb.keep_thr = keep_threshold(dropout_p);
+    tb.keep_scale = (float)(1.0 / (1.0 - (double)dropout_p));
+    tb.seed = seed;
+    MLA_TRY(launch_train_bwd(tb, st));
+  } else {
+    MLA_TRY(launch_rowdot(dO, o, D, B, S, H, dv, bf, st));
+    MLA_TRY(launch_fill_f32(dkc, (long long)M * HD, 0.f, st));
+    MLA_TRY(launch_fill_f32(dkr, (long long)M * HR, 0.f, st));
+    MLA_TRY(launch_fill_f32(dV, (long long)M * HV, 0.f, st));
+
+    // attention, one block of queries at a time for every (sequence, head) pair z = b H + h
+    const int tq = lw.tq;
+    AttnBwdParams ab;
+    memset(&ab, 0, sizeof(ab));
+    ab.S_ = F(lw.sbuf);
+    ab.P = at(ws, lw.pbuf);
+    ab.Pd = at(ws, lw.pdbuf);
+    ab.dS = at(ws, lw.dsbuf);
+    ab.lse = lse;
+    ab.D = D;
+    ab.Z = B * H;
+    ab.S = S;
+    ab.scale_log2 = tau * kLog2e;
+    ab.scale = tau;
+    ab.keep_thr = keep_threshold(dropout_p);
+    ab.keep_scale = (float)(1.0 / (1.0 - (double)dropout_p));
+    ab.seed = seed;
+    // batched operand views: a [rows][H][width] tensor has batch strides (S H width, width)
+    auto batched = [&](SgemmParams p, long long az0, long long az1, long long bz0, long long bz1, long long cz0,
+                       long long cz1) {
+      p.Z = B * H;
+      p.zdiv = H;
+      p.sAz0 = az0;
+      p.sAz1 = az1;
+      p.sBz0 = bz0;
+      p.sBz1 = bz1;
+      p.sCz0 = cz0;
+      p.sCz1 = cz1;
+      return p;
+    };
+    for (int i0 = 0; i0 < S; i0 += tq) {
+      const int T = S - i0 < tq ? S - i0 : tq;          // queries of this block
+      const int Kn = i0 + T;                            // keys they can see
+      const long long blk = (long long)tq * Kn;         // [Tq][Kn] block of one (sequence, head)
+      const char* qb = static_cast<const char*>(q) + (size_t)i0 * HQ * es;
+      ab.i0 = i0;
+      ab.Tq = tq;
+      ab.Kn = Kn;
+      // scores S = q_C k_C^T + q_R k_R^T (unscaled)
+      MLA_TRY(GEMM(batched(sg(qb, tf, HQ, 1, kc, tf, 1, HD, F(lw.sbuf), Kn, T, Kn, dn, 0.f),
+                           (long long)S * HQ, dq, (long long)S * HD, dn, (long long)H * blk, blk)));
+      MLA_TRY(GEMM(batched(sg(static_cast<const char*>(qb) + (size_t)dn * es, tf, HQ, 1, kr, tf, 1, dr, F(lw.sbuf), Kn,
+                              T, Kn, dr, 1.f),
+                           (long long)S * HQ, dq, (long long)S * dr, 0, (long long)H * blk, blk)));
+      MLA_TRY(launch_bwd_p(ab, bf, st));
+      // dV[0:Kn] += Pd^T dO_blk
+      const float* dOb = dO + (size_t)i0 * HV;
+      MLA_TRY(GEMM(batched(sg(ab.Pd, tf, 1, Kn, dOb, true, HV, 1, dV, HV, Kn, dv, T, 1.f), (long long)H * blk, blk,
+                           (long long)S * HV, dv, (long long)S * HV, dv)));
+      // dPd = dO_blk V^T  (into the score buffer)
+      MLA_TRY(GEMM(batched(sg(dOb, true, HV, 1, v, tf, 1, HV, F(lw.sbuf), Kn, T, Kn, dv, 0.f), (long long)S * HV, dv,
+                           (long long)S * HV, dv, (long long)H * blk, blk)));
+      MLA_TRY(launch_bwd_ds(ab, bf, st));
+      // dq_blk = dS k:  decompressed part and rotary part (k_R shared by the heads)
+      MLA_TRY(GEMM(batched(sg(ab.dS, tf, Kn, 1, kc, tf, HD, 1, dqc + (size_t)i0 * HD, HD, T, dn, Kn, 0.f),
+                           (long long)H * blk, blk, (long long)S * HD, dn, (long long)S * HD, dn)));
+      MLA_TRY(GEMM(batched(sg(ab.dS, tf, Kn, 1, kr, tf, dr, 1, dqr + (size_t)i0 * HR, HR, T, dr, Kn, 0.f),
+                           (long long)H * blk, blk, (long long)S * dr, 0, (long long)S * HR, dr)));
+      // dk[0:Kn] += dS^T q_blk (per head; the rotary parts are summed over heads below)
+      MLA_TRY(GEMM(batched(sg(ab.dS, tf, 1, Kn, qb, tf, HQ, 1, dkc, HD, Kn, dn, T, 1.f), (long long)H * blk, blk,
+                           (long long)S * HQ, dq, (long long)S * HD, dn)));
+      MLA_TRY(GEMM(batched(sg(ab.dS, tf, 1, Kn, static_cast<const char*>(qb) + (size_t)dn * es, tf, HQ, 1, dkr, HR,
+                              Kn, dr, T, 1.f),
+                           (long long)H * blk, blk, (long long)S * HQ, dq, (long long)S * HR, dr)));
+    }
   }
 
   // rotary parts back through the rotations (negative angle); k_R summed over heads

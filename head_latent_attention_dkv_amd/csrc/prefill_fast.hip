@@ -68,7 +68,9 @@ struct FlashCfg {
   static_assert(DR == 0 || DR == 64, "rotary width");
 };
 
-template <int DN, int DR, int QB>
+// TRAIN: the training forward -- dropout on the attention weights (keep bits drawn per group
+// of four keys, see dropout_keep4) and the per-row log-sum-exp written for the backward.
+template <int DN, int DR, int QB, bool TRAIN>
 __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashParams p) {
   using C = FlashCfg<DN, DR, QB>;
   constexpr int QW = 32 * QB;                          // queries per wave
@@ -101,6 +103,7 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
   const int qwa = p.q_off + qw;                         // its position
   const int kend = min(S, p.q_off + q0 + FQ);           // keys 0 .. kend-1 (multiple of 64)
   const int ntiles = kend / FK;
+  const long long bh_q = (long long)b * p.H + h;         // query head stream (dropout counter)
   // key / value head of this query head (grouped heads share one)
   const int kvg = p.kv_group > 1 ? p.kv_group : 1;
   const long long bh = (long long)b * (p.H / kvg) + h / kvg;
@@ -253,15 +256,32 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
       for (int qb = 0; qb < QB; ++qb) ps[qb] = l_run[qb];
       float pv0[QB][16], pv1[QB][16];
       // probability x = 16 qb + e of a half: exponential, and on every odd e the bf16 pair
-      // and its contribution to the denominator
-      auto prob = [&](const f32x16 (&sc)[QB], float (&pv)[QB][16], Frag<bf16> (&pf)[QB][2], int x) {
+      // and its contribution to the denominator.  TRAIN: the pair then loses its dropped
+      // weights (the denominator keeps them; 1 / (1 - p) is applied with the normalisation).
+      // Element e of half kb is key key0 + 32 kb + 8 (e / 4) + 4 half + e % 4: one draw per
+      // group of four e serves four consecutive keys.
+      uint64_t draw[QB];
+      auto prob = [&](const f32x16 (&sc)[QB], float (&pv)[QB][16], Frag<bf16> (&pf)[QB][2], int x, int kb) {
         const int qb = x >> 4, e = x & 15;
         pv[qb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][e], p.scale_log2, nm[qb]));
+        if constexpr (TRAIN) {
+          if ((e & 3) == 0 && p.keep_thr)
+            draw[qb] = dropout_draw(p.seed, dropout_counter4((int)bh_q, qwa + 32 * qb + col,
+                                                              (key0 + 32 * kb + 8 * (e >> 2) + 4 * half) >> 2));
+        }
         if (e & 1) {
           pf[qb][e >> 3].v[(e & 7) - 1] = (bf16)pv[qb][e - 1];
           pf[qb][e >> 3].v[e & 7] = (bf16)pv[qb][e];
           ps[qb] = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[qb][e >> 3].v[(e & 7) - 1], pf[qb][e >> 3].v[e & 7]},
                                                    kOnes2, ps[qb], false);
+          if constexpr (TRAIN) {
+            if (p.keep_thr) {
+              const uint32_t f0 = (uint32_t)(draw[qb] >> (16 * ((e - 1) & 3))) & 0xFFFFu;
+              const uint32_t f1 = (uint32_t)(draw[qb] >> (16 * (e & 3))) & 0xFFFFu;
+              if (f0 < p.keep_thr) pf[qb][e >> 3].v[(e & 7) - 1] = (bf16)0.f;
+              if (f1 < p.keep_thr) pf[qb][e >> 3].v[e & 7] = (bf16)0.f;
+            }
+          }
         }
       };
       Frag<bf16> ring[PF + 1];
@@ -291,11 +311,11 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
         if constexpr (n >= KS && n < 2 * KS) {
           constexpr int k = n - KS;
 #pragma unroll
-          for (int x = (NE * k) / KS; x < (NE * (k + 1)) / KS; ++x) prob(s0, pv0, pf0, x);
+          for (int x = (NE * k) / KS; x < (NE * (k + 1)) / KS; ++x) prob(s0, pv0, pf0, x, 0);
         } else if constexpr (n >= 2 * KS && n < 2 * KS + NV) {
           constexpr int k = n - 2 * KS;
 #pragma unroll
-          for (int x = (NE * k) / NV; x < (NE * (k + 1)) / NV; ++x) prob(s1, pv1, pf1, x);
+          for (int x = (NE * k) / NV; x < (NE * (k + 1)) / NV; ++x) prob(s1, pv1, pf1, x, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -400,9 +420,10 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const float inv = 1.f / lt;
+    const float inv = (TRAIN && p.keep_thr ? p.keep_scale : 1.f) / lt;
     const int qi = qw + 32 * qb + col;
     if (qi >= p.T) continue;
+    if (TRAIN && p.lse && half == 0) p.lse[bh_q * p.T + qi] = m_ref[qb] + __log2f(lt);
     const int dvo = p.dv_out > 0 ? p.dv_out : C::DV;
     bf16* op = reinterpret_cast<bf16*>(p.o) + (((long long)b * p.T + qi) * p.H + h) * dvo + 4 * half;
 #pragma unroll
@@ -425,13 +446,13 @@ bool prefill_fast_supported(int dn, int d_rope, int dv, int S) {
 }
 
 namespace {
-template <int DN, int DR, int QB>
+template <int DN, int DR, int QB, bool TRAIN = false>
 hipError_t launch_flash(const FlashParams& pin, hipStream_t s) {
   FlashParams p = pin;
   p.ntq = cdiv(p.T, FQ);
   dim3 grid(p.ntq * p.H * p.B);
   constexpr size_t lds = FlashCfg<DN, DR, QB>::LDS;
-  hipLaunchKernelGGL((prefill_flash_kernel<DN, DR, QB>), grid, dim3(64 * (8 / QB)), lds, s, p);
+  hipLaunchKernelGGL((prefill_flash_kernel<DN, DR, QB, TRAIN>), grid, dim3(64 * (8 / QB)), lds, s, p);
   return hipGetLastError();
 }
 }  // namespace
@@ -440,6 +461,12 @@ hipError_t launch_prefill_fast(const FlashParams& p, hipStream_t s) {
   const int kvg = p.kv_group > 1 ? p.kv_group : 1;
   if (p.H % kvg) return hipErrorInvalidValue;
   if (p.dv_out < 0 || p.dv_out > p.dn || p.dv_out % 32) return hipErrorInvalidValue;
+  if (p.keep_thr || p.lse) {
+    // training forward: the decoupled-RoPE shape only
+    if (p.dn == 128 && p.d_rope == 64 && p.kv_group <= 1 && p.dv_out == 0)
+      return launch_flash<128, 64, kFlashQB, true>(p, s);
+    return hipErrorInvalidValue;
+  }
   if (p.dn == 128 && p.d_rope == 64) return launch_flash<128, 64, kFlashQB>(p, s);
   if (p.dn == 128 && p.d_rope == 0) return launch_flash<128, 0, kFlashQB>(p, s);
   if (p.dn == 64 && p.d_rope == 0) return launch_flash<64, 0, kFlashQB>(p, s);

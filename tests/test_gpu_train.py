@@ -22,6 +22,10 @@ TINY = S.CONFIGS["tiny_fp32"]
 # DeepSeek-V2 per-head shapes at a reduced width and head count; 600 tokens: three query blocks
 # of the backward (256, 256, 88) and ragged key tiles
 DSV2_T = S.CONFIGS["dsv2_prefill"].replace(name="dsv2_train", d_model=256, n_heads=16, r_q=384, batch=2, seq=600)
+# whole 64-token tiles: the flash forward and the flash backward kernels (key blocks of 128 with
+# a ragged last block of 64; three heads: (sequence, head) groups not a multiple of 8)
+DSV2_F = DSV2_T.replace(name="dsv2_train_flash", seq=320)
+DSV2_F3 = DSV2_T.replace(name="dsv2_train_flash_h3", n_heads=3, d_model=192, seq=192)
 
 
 @pytest.fixture(scope="module")
@@ -82,8 +86,10 @@ def _oracle(cfg, W, p, seed, xs, dys):
     return np.stack(ys), gs
 
 
-@pytest.mark.parametrize("cfg,p,seed", [(TINY, 0.3, 42), (TINY, 0.0, 1), (DSV2_T, 0.1, 7), (DSV2_T, 0.5, 9)],
-                         ids=["tiny_p0.3", "tiny_p0", "dsv2_p0.1", "dsv2_p0.5"])
+@pytest.mark.parametrize("cfg,p,seed", [(TINY, 0.3, 42), (TINY, 0.0, 1), (DSV2_T, 0.1, 7), (DSV2_T, 0.5, 9),
+                                        (DSV2_F, 0.1, 7), (DSV2_F, 0.5, 9), (DSV2_F, 0.0, 2), (DSV2_F3, 0.25, 3)],
+                         ids=["tiny_p0.3", "tiny_p0", "dsv2_p0.1", "dsv2_p0.5", "flash_p0.1", "flash_p0.5",
+                              "flash_p0", "flash_h3_p0.25"])
 def test_train_forward_backward(gu, cfg, p, seed):
     gu.say(f"[train] {cfg.name} p={p} seed={seed} B={cfg.batch} S={cfg.seq}")
     rng = np.random.default_rng(seed)
