@@ -9,6 +9,8 @@
 //     the same generator counters as the forward);
 //   * rowdot_kernel (rowsum(dO o)), rope_bwd_kernel (rotations by the negative angle, the
 //     rotary key's gradient summed over heads), fill_f32_kernel.
+#include <initializer_list>
+
 #include "common.h"
 #include "internal.h"
 
@@ -171,6 +173,176 @@ __global__ void __launch_bounds__(256) rope_bwd_kernel(const float* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Tiled MFMA GEMM for the bf16 layers' training products: C = alpha A B + beta C with A
+// [M][K] and B [K][N] of any strides whose contiguous dimension is K or M (A) / K or N (B),
+// stored bf16 or fp32 (rounded to bf16 when staged), batches as in sgemm_kernel.
+// 128 x 128 block tile, 32-deep k steps, 4 waves of 64 x 64 (2 x 2 accumulators of 32 x 32);
+// 16-byte (bf16) or 2 x 16-byte (fp32) loads along the contiguous dimension, two LDS
+// buffers filled through registers while the other is consumed.  An operand stored
+// k-contiguous is staged [row][k] and read with plain 16-byte reads; one stored row-
+// contiguous is staged [k][row] and read with LDS transpose reads.
+// ---------------------------------------------------------------------------------------
+constexpr int TM = 128, TN = 128, TK = 32;
+constexpr int LDKC = TK + 8;    // [row][k] tiles: rows 80 B apart (16-row reads on distinct banks)
+constexpr int LDMC = TM + 8;    // [k][row] tiles: rows 272 B apart
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// 8 consecutive elements along the operand's contiguous dimension (the first `avail` of them;
+// zeros for the rest)
+template <bool F32>
+__device__ __forceinline__ bf16x8 load8(const void* base, long long off, int avail) {
+  bf16x8 v;
+  if (avail >= 8) {
+    if constexpr (F32) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off + 4);
+      v = (bf16x8){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    } else {
+      v = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(base) + off);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float x = 0.f;
+      if (j < avail) x = F32 ? static_cast<const float*>(base)[off + j] : (float)static_cast<const bf16*>(base)[off + j];
+      v[j] = (bf16)x;
+    }
+  }
+  return v;
+}
+
+// Operand from a [k][row] tile by two transpose reads: the lane gets column c0 + lane % 32 at
+// k rows r0 + 8 half .. r0 + 8 half + 7 (the natural k order of a 16-deep MFMA step)
+__device__ __forceinline__ Frag<bf16> tr_natural(const bf16* tile, int ld, int r0, int c0, int lane) {
+  const int k16 = lane & 15, g16 = lane >> 4, half = lane >> 5;
+  const int r = r0 + 8 * half + (k16 >> 2);
+  const int c = c0 + 16 * (g16 & 1) + 4 * (k16 & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + r * ld + c));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + (r + 4) * ld + c));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, v);
+  return f;
+}
+
+// AKC: A stored k-contiguous (sAk == 1), else m-contiguous (sAm == 1); BKC likewise for B
+// (sBk == 1, else sBn == 1); AF / BF: fp32 storage.
+template <bool AKC, bool BKC, bool AF, bool BF>
+__global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(SgemmParams p) {
+  constexpr int A_TILE = AKC ? TM * LDKC : TK * LDMC;
+  constexpr int B_TILE = BKC ? TN * LDKC : TK * LDMC;
+  __shared__ __attribute__((aligned(16))) bf16 As[2][A_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][B_TILE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  const int z = blockIdx.z, z0 = z / p.zdiv, z1 = z - z0 * p.zdiv;
+  const long long offA = z0 * p.sAz0 + z1 * p.sAz1, offB = z0 * p.sBz0 + z1 * p.sBz1;
+  const long long offC = z0 * p.sCz0 + z1 * p.sCz1;
+
+  // staging: each operand tile is 128 x 32 = 512 vectors of 8; two per thread
+  bf16x8 pa[2], pb[2];
+  auto gload = [&](int k0, bf16x8 (&va)[2], bf16x8 (&vb)[2]) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int idx = tid + 256 * v;
+      if constexpr (AKC) {
+        const int r = idx >> 2, kc = (idx & 3) * 8, m = m0 + r, k = k0 + kc;
+        va[v] = load8<AF>(p.A, offA + (long long)min(m, p.M - 1) * p.sAm + k, m < p.M ? p.K - k : 0);
+      } else {
+        const int kr = idx >> 4, mc = (idx & 15) * 8, k = k0 + kr, m = m0 + mc;
+        va[v] = load8<AF>(p.A, offA + (long long)min(k, p.K - 1) * p.sAk + m, k < p.K ? p.M - m : 0);
+      }
+      if constexpr (BKC) {
+        const int r = idx >> 2, kc = (idx & 3) * 8, n = n0 + r, k = k0 + kc;
+        vb[v] = load8<BF>(p.B, offB + (long long)min(n, p.N - 1) * p.sBn + k, n < p.N ? p.K - k : 0);
+      } else {
+        const int kr = idx >> 4, nc = (idx & 15) * 8, k = k0 + kr, n = n0 + nc;
+        vb[v] = load8<BF>(p.B, offB + (long long)min(k, p.K - 1) * p.sBk + n, k < p.K ? p.N - n : 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf, const bf16x8 (&va)[2], const bf16x8 (&vb)[2]) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int idx = tid + 256 * v;
+      if constexpr (AKC) *reinterpret_cast<bf16x8*>(&As[buf][(idx >> 2) * LDKC + (idx & 3) * 8]) = va[v];
+      else *reinterpret_cast<bf16x8*>(&As[buf][(idx >> 4) * LDMC + (idx & 15) * 8]) = va[v];
+      if constexpr (BKC) *reinterpret_cast<bf16x8*>(&Bs[buf][(idx >> 2) * LDKC + (idx & 3) * 8]) = vb[v];
+      else *reinterpret_cast<bf16x8*>(&Bs[buf][(idx >> 4) * LDMC + (idx & 15) * 8]) = vb[v];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int nk = cdiv(p.K, TK);
+  gload(0, pa, pb);
+  lstore(0, pa, pb);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * TK, pa, pb);
+    const bf16* A = As[buf];
+    const bf16* B = Bs[buf];
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      Frag<bf16> fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm + 32 * i;
+        fa[i] = AKC ? frag_load(A + (r + col) * LDKC + 16 * ks + 8 * half) : tr_natural(A, LDMC, 16 * ks, r, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = wn + 32 * j;
+        fb[j] = BKC ? frag_load(B + (c + col) * LDKC + 16 * ks + 8 * half) : tr_natural(B, LDMC, 16 * ks, c, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mma32(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1, pa, pb);
+    __syncthreads();
+  }
+  // accumulator element e of lane l: row wm + 32 i + 8 (e / 4) + 4 half + e % 4, column
+  // wn + 32 j + l % 32
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn + 32 * j + col;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (m >= p.M) continue;
+        float* c = p.C + offC + m * p.sCm + n * p.sCn;
+        const float v = p.alpha * acc[i][j][e];
+        *c = p.beta != 0.f ? v + p.beta * *c : v;
+      }
+  }
+}
+
+template <bool AKC, bool BKC>
+hipError_t launch_mfma4(const SgemmParams& p, dim3 grid, hipStream_t s) {
+  if (p.a_f32 && p.b_f32) hipLaunchKernelGGL((gemm_mfma_kernel<AKC, BKC, true, true>), grid, dim3(256), 0, s, p);
+  else if (p.a_f32) hipLaunchKernelGGL((gemm_mfma_kernel<AKC, BKC, true, false>), grid, dim3(256), 0, s, p);
+  else if (p.b_f32) hipLaunchKernelGGL((gemm_mfma_kernel<AKC, BKC, false, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((gemm_mfma_kernel<AKC, BKC, false, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 __global__ void fill_f32_kernel(float* p, long long n, float v) {
   for (long long e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (long long)gridDim.x * 256) p[e] = v;
 }
@@ -184,6 +356,32 @@ int grid_for(long long n) {
 
 hipError_t launch_sgemm(const SgemmParams& p, bool use_bf16, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || p.Z <= 0) return hipSuccess;
+  // bf16 layers: the tiled MFMA kernel when each operand has a contiguous dimension whose
+  // 8-element vectors are 16-byte (bf16) / 32-byte (fp32) aligned
+  if (use_bf16) {
+    auto aligned = [](const void* base, bool f32, std::initializer_list<long long> strides) {
+      const long long es = f32 ? 4 : 2;
+      if (reinterpret_cast<uintptr_t>(base) % 16 != 0) return false;
+      for (long long st : strides)
+        if ((st * es) % 16 != 0) return false;
+      return true;
+    };
+    const bool akc = p.sAk == 1, amc = p.sAm == 1, bkc = p.sBk == 1, bnc = p.sBn == 1;
+    const bool a_ok = (akc && aligned(p.A, p.a_f32, {p.sAm, p.sAz0, p.sAz1})) ||
+                      (amc && aligned(p.A, p.a_f32, {p.sAk, p.sAz0, p.sAz1}));
+    const bool b_ok = (bkc && aligned(p.B, p.b_f32, {p.sBn, p.sBz0, p.sBz1})) ||
+                      (bnc && aligned(p.B, p.b_f32, {p.sBk, p.sBz0, p.sBz1}));
+    if (a_ok && b_ok) {
+      const dim3 grid(cdiv(p.N, TN), cdiv(p.M, TM), p.Z);
+      if (grid.y > 65535 || grid.z > 65535) return hipErrorInvalidValue;
+      const bool a_k = akc && aligned(p.A, p.a_f32, {p.sAm, p.sAz0, p.sAz1});
+      const bool b_k = bkc && aligned(p.B, p.b_f32, {p.sBn, p.sBz0, p.sBz1});
+      if (a_k && b_k) return launch_mfma4<true, true>(p, grid, s);
+      if (a_k) return launch_mfma4<true, false>(p, grid, s);
+      if (b_k) return launch_mfma4<false, true>(p, grid, s);
+      return launch_mfma4<false, false>(p, grid, s);
+    }
+  }
   const dim3 grid(cdiv(p.N, BN), cdiv(p.M, BM), p.Z);
   if (grid.y > 65535) return hipErrorInvalidValue;
   if (use_bf16)
