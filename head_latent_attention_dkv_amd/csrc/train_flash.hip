@@ -80,6 +80,7 @@ __global__ void __launch_bounds__(256, 1) train_bwd_kv_kernel(TrainBwdParams p) 
   __shared__ __attribute__((aligned(16))) bf16 Os[2][AQT * OLD];
   __shared__ __attribute__((aligned(16))) float Ls[2][AQT];
   __shared__ __attribute__((aligned(16))) float Dm[2][AQT];
+  __shared__ __attribute__((aligned(16))) bf16 Vk[AKB * VLD];   // the block's values, [key][dv]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -105,20 +106,26 @@ __global__ void __launch_bounds__(256, 1) train_bwd_kv_kernel(TrainBwdParams p) 
   const int key = kw + col;                 // this lane's key (accumulator column)
   const int keyc = min(key, S - 1);
 
-  // K (decompressed | rotary) and V of the lane's key as B operands: k slots = features
-  // 16 ks + 8 half .. + 7
-  Frag<bf16> kf[TDQ / 16], vf[TDV / 16];
+  // K (decompressed | rotary) of the lane's key as B operands in registers: k slots =
+  // features 16 ks + 8 half .. + 7
+  Frag<bf16> kf[TDQ / 16];
 #pragma unroll
   for (int ks = 0; ks < TDN / 16; ++ks) kf[ks] = frag_load(p.kf + (bh * S + keyc) * TDN + 16 * ks + 8 * half);
 #pragma unroll
   for (int ks = 0; ks < TDR / 16; ++ks)
     kf[TDN / 16 + ks] = frag_load(p.kr + ((long long)b * S + keyc) * TDR + 16 * ks + 8 * half);
+  // the block's values, de-permuted into LDS as [key][dv] (their B operands are read from
+  // there: registers are short); rows past S are clamped copies, never used
   {
-    const int slot = perm16(keyc);
+    constexpr int NVC = TDV * (AKB / 8) / 256;   // 16-byte chunks per thread
 #pragma unroll
-    for (int ks = 0; ks < TDV / 16; ++ks)
+    for (int i = 0; i < NVC; ++i) {
+      const int c = tid + 256 * i, d = c / (AKB / 8), u = c - d * (AKB / 8);
+      const int s0 = min(k0 + 8 * u, S - 8);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(p.vt + (bh * TDV + d) * S + s0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vf[ks].v[j] = p.vt[(bh * TDV + 16 * ks + 8 * half + j) * S + slot];
+      for (int j = 0; j < 8; ++j) Vk[perm16(8 * u + j) * VLD + d] = v[j];
+    }
   }
 
   f32x16 dk[TDQ / 32], dv[TDV / 32];
@@ -132,7 +139,7 @@ __global__ void __launch_bounds__(256, 1) train_bwd_kv_kernel(TrainBwdParams p) 
   static_assert(AQT * RCH % 256 == 0, "staging chunks split evenly");
   // (the staged registers are plain locals of the loop body below: an array captured by a
   // lambda stays in scratch memory)
-#define MLA_A_GLOAD(qt_)                                                                        \
+#define MLA_A_GLOAD(qt_, pre, pre_s)                                                                        \
   {                                                                                             \
     const int q0_ = (qt_) * AQT;                                                                \
     _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                           \
@@ -144,7 +151,7 @@ __global__ void __launch_bounds__(256, 1) train_bwd_kv_kernel(TrainBwdParams p) 
     if (tid < AQT) pre_s = p.lse[bh * S + q0_ + tid];                                           \
     else if (tid < 2 * AQT) pre_s = p.D[bh * S + q0_ + tid - AQT];                              \
   }
-#define MLA_A_LSTORE(buf_)                                                                      \
+#define MLA_A_LSTORE(buf_, pre, pre_s)                                                                      \
   {                                                                                             \
     _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                           \
       const int c = tid + 256 * i, r = c / RCH, u = c - r * RCH;                                \
@@ -154,87 +161,103 @@ __global__ void __launch_bounds__(256, 1) train_bwd_kv_kernel(TrainBwdParams p) 
     if (tid < AQT) Ls[buf_][tid] = pre_s;                                                       \
     else if (tid < 2 * AQT) Dm[buf_][tid - AQT] = pre_s;                                        \
   }
-  bf16x8 pre[NCH];
-  float pre_s = 0.f;
+  // the accumulators live in accumulation registers across tiles (without this the compiler
+  // keeps them in VGPRs for the products and parks them in AGPRs between tiles: 320 copies
+  // per tile)
+#define MLA_A_PIN()                                                         \
+  {                                                                         \
+    _Pragma("unroll") for (int i = 0; i < TDQ / 32; ++i) asm volatile("" : "+a"(dk[i])); \
+    _Pragma("unroll") for (int i = 0; i < TDV / 32; ++i) asm volatile("" : "+a"(dv[i])); \
+  }
+  // Tile loop: the global loads of tile qt + 1 are in flight while tile qt is computed.
+#define MLA_A_TILE(buf, qt) \
+    if (qt * AQT + AQT - 1 >= kw) { /* else every query of the tile is before the wave's keys */ \
+      const int q0 = qt * AQT; \
+      const bf16* Q = Qs[buf]; \
+      const bf16* O = Os[buf]; \
+      /* S[q][key] = Q K^T and dP[q][key] = dO V^T (A operands: query row col of the tile) */ \
+      f32x16 sa = f32x16{}, dpa = f32x16{}; \
+_Pragma("unroll") \
+      for (int ks = 0; ks < TDQ / 16; ++ks) sa = mma32(frag_load(Q + col * QLD + 16 * ks + 8 * half), kf[ks], sa); \
+_Pragma("unroll") \
+      for (int ks = 0; ks < TDV / 16; ++ks) \
+        dpa = mma32(frag_load(O + col * OLD + 16 * ks + 8 * half), frag_load(Vk + (32 * wave + col) * VLD + 16 * ks + 8 * half), \
+                    dpa); \
+      /* element e: query q0 + qr(e), qr(e) = 8 (e / 4) + 4 half + e % 4; key: the lane's */ \
+      /* keep bits: the four lanes of a quad hold four consecutive keys (one draw per query); */ \
+      /* lane r of the quad draws for the queries of e = r, r + 4, r + 8, r + 12 and the quad */ \
+      /* shares them */ \
+      unsigned keep = 0xFFFFu; \
+      if (p.keep_thr) { \
+        const int r = col & 3; \
+        uint64_t dr[4]; \
+_Pragma("unroll") \
+        for (int g4 = 0; g4 < 4; ++g4) \
+          dr[g4] = dropout_draw(p.seed, dropout_counter4((int)bh, q0 + 8 * g4 + 4 * half + r, key >> 2)); \
+        const int sh = 16 * (col & 3); \
+        keep = 0; \
+_Pragma("unroll") \
+        for (int g4 = 0; g4 < 4; ++g4) { \
+          const uint64_t d0 = quad_bcast<0>(dr[g4]), d1 = quad_bcast<1>(dr[g4]); \
+          const uint64_t d2 = quad_bcast<2>(dr[g4]), d3 = quad_bcast<3>(dr[g4]); \
+          keep |= (((uint32_t)(d0 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 0); \
+          keep |= (((uint32_t)(d1 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 1); \
+          keep |= (((uint32_t)(d2 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 2); \
+          keep |= (((uint32_t)(d3 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 3); \
+        } \
+      } \
+      __builtin_amdgcn_sched_barrier(0); \
+      const float kscale = p.keep_thr ? p.keep_scale : 1.f; \
+      float pd[16], ds[16]; \
+_Pragma("unroll") \
+      for (int g4 = 0; g4 < 4; ++g4) { \
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][8 * g4 + 4 * half]); \
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dm[buf][8 * g4 + 4 * half]); \
+_Pragma("unroll") \
+        for (int j = 0; j < 4; ++j) { \
+          const int e = 4 * g4 + j, qi = q0 + 8 * g4 + 4 * half + j; \
+          const float pv = key <= qi ? __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], p.scale_log2, -l4[j])) : 0.f; \
+          const bool kp = (keep >> e) & 1u; \
+          pd[e] = kp ? pv : 0.f; \
+          ds[e] = pv * ((kp ? dpa[e] * kscale : 0.f) - d4[j]); \
+        } \
+      } \
+      /* dV[key][dv] += Pd^T dO and dK[key][f] += dS^T Q over the tile's two 16-query steps */ \
+      /* (sched_barrier: each product's operand read stays next to it, which bounds the live */ \
+      /* registers) */ \
+      const Frag<bf16> pf0 = frag_from_f32<bf16>(pd), pf1 = frag_from_f32<bf16>(pd + 8); \
+      const Frag<bf16> sf0 = frag_from_f32<bf16>(ds), sf1 = frag_from_f32<bf16>(ds + 8); \
+      __builtin_amdgcn_sched_barrier(0); \
+_Pragma("unroll") \
+      for (int db = 0; db < TDV / 32; ++db) { \
+        dv[db] = mma32(pf0, tr_frag(O, OLD, 0, 32 * db, lane), dv[db]); \
+        dv[db] = mma32(pf1, tr_frag(O, OLD, 16, 32 * db, lane), dv[db]); \
+        __builtin_amdgcn_sched_barrier(0); \
+      } \
+_Pragma("unroll") \
+      for (int fb = 0; fb < TDQ / 32; ++fb) { \
+        dk[fb] = mma32(sf0, tr_frag(Q, QLD, 0, 32 * fb, lane), dk[fb]); \
+        dk[fb] = mma32(sf1, tr_frag(Q, QLD, 16, 32 * fb, lane), dk[fb]); \
+        __builtin_amdgcn_sched_barrier(0); \
+      } \
+    }
+  bf16x8 pa[NCH];
+  float pa_s = 0.f;
 
   const int qt0 = k0 / AQT, nqt = S / AQT;
-  MLA_A_GLOAD(qt0);
-  MLA_A_LSTORE(0);
+  MLA_A_GLOAD(qt0, pa, pa_s);
+  MLA_A_LSTORE(0, pa, pa_s);
   __syncthreads();
   for (int qt = qt0; qt < nqt; ++qt) {
     const int buf = (qt - qt0) & 1;
-    if (qt + 1 < nqt) MLA_A_GLOAD(qt + 1);
-    if (qt * AQT + AQT - 1 >= kw) {          // else every query of the tile is before the wave's keys
-      const int q0 = qt * AQT;
-      const bf16* Q = Qs[buf];
-      const bf16* O = Os[buf];
-      // S[q][key] = Q K^T and dP[q][key] = dO V^T (A operands: query row col of the tile)
-      f32x16 sa = f32x16{}, dpa = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < TDQ / 16; ++ks) sa = mma32(frag_load(Q + col * QLD + 16 * ks + 8 * half), kf[ks], sa);
-#pragma unroll
-      for (int ks = 0; ks < TDV / 16; ++ks) dpa = mma32(frag_load(O + col * OLD + 16 * ks + 8 * half), vf[ks], dpa);
-      // element e: query q0 + qr(e), qr(e) = 8 (e / 4) + 4 half + e % 4; key: the lane's
-      // keep bits: the four lanes of a quad hold four consecutive keys (one draw per query);
-      // lane r of the quad draws for the queries of e = r, r + 4, r + 8, r + 12 and the quad
-      // shares them
-      unsigned keep = 0xFFFFu;
-      if (p.keep_thr) {
-        const int r = col & 3;
-        uint64_t dr[4];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          dr[g4] = dropout_draw(p.seed, dropout_counter4((int)bh, q0 + 8 * g4 + 4 * half + r, key >> 2));
-        const int sh = 16 * (col & 3);
-        keep = 0;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const uint64_t d0 = quad_bcast<0>(dr[g4]), d1 = quad_bcast<1>(dr[g4]);
-          const uint64_t d2 = quad_bcast<2>(dr[g4]), d3 = quad_bcast<3>(dr[g4]);
-          keep |= (((uint32_t)(d0 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 0);
-          keep |= (((uint32_t)(d1 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 1);
-          keep |= (((uint32_t)(d2 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 2);
-          keep |= (((uint32_t)(d3 >> sh) & 0xFFFFu) >= p.keep_thr ? 1u : 0u) << (4 * g4 + 3);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const float kscale = p.keep_thr ? p.keep_scale : 1.f;
-      float pd[16], ds[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][8 * g4 + 4 * half]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dm[buf][8 * g4 + 4 * half]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * g4 + j, qi = q0 + 8 * g4 + 4 * half + j;
-          const float pv = key <= qi ? __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], p.scale_log2, -l4[j])) : 0.f;
-          const bool kp = (keep >> e) & 1u;
-          pd[e] = kp ? pv : 0.f;
-          ds[e] = pv * ((kp ? dpa[e] * kscale : 0.f) - d4[j]);
-        }
-      }
-      // dV[key][dv] += Pd^T dO and dK[key][f] += dS^T Q over the tile's two 16-query steps
-      // (sched_barrier: each product's operand read stays next to it, which bounds the live
-      // registers)
-      const Frag<bf16> pf0 = frag_from_f32<bf16>(pd), pf1 = frag_from_f32<bf16>(pd + 8);
-      const Frag<bf16> sf0 = frag_from_f32<bf16>(ds), sf1 = frag_from_f32<bf16>(ds + 8);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < TDV / 32; ++db) {
-        dv[db] = mma32(pf0, tr_frag(O, OLD, 0, 32 * db, lane), dv[db]);
-        dv[db] = mma32(pf1, tr_frag(O, OLD, 16, 32 * db, lane), dv[db]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int fb = 0; fb < TDQ / 32; ++fb) {
-        dk[fb] = mma32(sf0, tr_frag(Q, QLD, 0, 32 * fb, lane), dk[fb]);
-        dk[fb] = mma32(sf1, tr_frag(Q, QLD, 16, 32 * fb, lane), dk[fb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (qt + 1 < nqt) MLA_A_LSTORE(buf ^ 1);
+    if (qt + 1 < nqt) MLA_A_GLOAD(qt + 1, pa, pa_s);
+    MLA_A_TILE(buf, qt);
+    if (qt + 1 < nqt) MLA_A_LSTORE(buf ^ 1, pa, pa_s);
+    MLA_A_PIN();
     __syncthreads();
   }
+#undef MLA_A_TILE
+#undef MLA_A_PIN
 #undef MLA_A_GLOAD
 #undef MLA_A_LSTORE
 
@@ -261,6 +284,7 @@ __global__ void __launch_bounds__(256, 1) train_bwd_kv_kernel(TrainBwdParams p) 
 __global__ void __launch_bounds__(256, 1) train_bwd_q_kernel(TrainBwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BKT * KLD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][BKT * VLD];
+  __shared__ __attribute__((aligned(16))) bf16 Ob[BQB * OLD];    // the block's dO rows
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -286,13 +310,21 @@ __global__ void __launch_bounds__(256, 1) train_bwd_q_kernel(TrainBwdParams p) {
   const int qi = qw + col;                  // this lane's query (accumulator column)
   const int qic = min(qi, S - 1);
 
-  // Q and dO of the lane's query as B operands (k slots: features 16 ks + 8 half .. + 7)
-  Frag<bf16> qf[TDQ / 16], of[TDV / 16];
+  // Q of the lane's query as B operands in registers (k slots: features 16 ks + 8 half ..
+  // + 7); the block's dO rows in LDS (their B operands are read from there)
+  Frag<bf16> qf[TDQ / 16];
   const long long qrow = ((long long)b * S + qic) * H + h;
 #pragma unroll
   for (int ks = 0; ks < TDQ / 16; ++ks) qf[ks] = frag_load(p.q + qrow * TDQ + 16 * ks + 8 * half);
+  {
+    constexpr int NOC = BQB * (TDV / 8) / 256;   // 16-byte chunks per thread
 #pragma unroll
-  for (int ks = 0; ks < TDV / 16; ++ks) of[ks] = frag_load(p.dO + qrow * TDV + 16 * ks + 8 * half);
+    for (int i = 0; i < NOC; ++i) {
+      const int c = tid + 256 * i, r = c / (TDV / 8), u = c - r * (TDV / 8);
+      const long long orow = ((long long)b * S + min(q0 + r, S - 1)) * H + h;
+      *reinterpret_cast<bf16x8*>(&Ob[r * OLD + 8 * u]) = *reinterpret_cast<const bf16x8*>(p.dO + orow * TDV + 8 * u);
+    }
+  }
   const float lse_q = p.lse[bh * S + qic], d_q = p.D[bh * S + qic];
 
   f32x16 dq[TDQ / 32];
@@ -352,7 +384,8 @@ __global__ void __launch_bounds__(256, 1) train_bwd_q_kernel(TrainBwdParams p) {
         st = mma32(frag_load(K + (32 * kh + col) * KLD + 16 * ks + 8 * half), qf[ks], st);
 #pragma unroll
       for (int ks = 0; ks < TDV / 16; ++ks)
-        dpt = mma32(frag_load(V + (32 * kh + col) * VLD + 16 * ks + 8 * half), of[ks], dpt);
+        dpt = mma32(frag_load(V + (32 * kh + col) * VLD + 16 * ks + 8 * half),
+                    frag_load(Ob + (32 * wave + col) * OLD + 16 * ks + 8 * half), dpt);
       // element e: key kb0 + 8 (e / 4) + 4 half + e % 4, query: the lane's; one draw per
       // four consecutive keys
       float ds[16];
@@ -389,6 +422,8 @@ __global__ void __launch_bounds__(256, 1) train_bwd_q_kernel(TrainBwdParams p) {
     if (kt + 1 < nkt) MLA_B_GLOAD(kt + 1);
     if (kt * BKT <= qw + 31) compute(buf, kt);
     if (kt + 1 < nkt) MLA_B_LSTORE(buf ^ 1);
+#pragma unroll
+    for (int i = 0; i < TDQ / 32; ++i) asm volatile("" : "+a"(dq[i]));   // (as in the key kernel)
     __syncthreads();
   }
 #undef MLA_B_GLOAD
