@@ -448,7 +448,7 @@ def cpu_baseline(cfg, budget_s=15.0, max_seqs=64):
                       f"explicit K/V up-projection), {t_tot:.1f} s; value = their latent-cache bytes / time"}
 
 
-def cpu_baseline_prefill(cfg, budget_s=12.0, rows_per_seq=32):
+def cpu_baseline_prefill(cfg, budget_s=12.0, rows_per_seq=256):
     """fp64 oracle on a bounded sample of the prefill workload: for each sampled sequence,
     its whole explicit K/V up-projection and the causal attention of `rows_per_seq` query rows
     spread over the sequence (the oracle's forward restricted to those rows).  The value counts

@@ -214,11 +214,19 @@ __host__ __device__ constexpr int round_up(int a, int b) { return cdiv(a, b) * b
 // i 2^18 + j4, i.e. the state seed + (n + 1) gamma through the output function (two
 // xor-shift-multiply steps, a final xor-shift).  Key 4 j4 + e uses bits 16 e .. 16 e + 15 and
 // is kept when they are >= thr = floor(p 2^16).
-__device__ __forceinline__ uint64_t dropout_draw(uint64_t seed, uint64_t n) {
-  uint64_t z = seed + (n + 1ull) * 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kSplitmixGamma = 0x9E3779B97F4A7C15ull;
+// the generator's output function applied to a state
+__device__ __forceinline__ uint64_t splitmix_mix(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
+}
+// the state of draw n: linear in n, so kernels that walk the counters step it by additions
+__device__ __forceinline__ uint64_t splitmix_state(uint64_t seed, uint64_t n) {
+  return seed + (n + 1ull) * kSplitmixGamma;
+}
+__device__ __forceinline__ uint64_t dropout_draw(uint64_t seed, uint64_t n) {
+  return splitmix_mix(splitmix_state(seed, n));
 }
 __device__ __forceinline__ uint64_t dropout_counter4(int zh, int i, int j4) {
   return ((uint64_t)(uint32_t)zh << 38) + ((uint64_t)(uint32_t)i << 18) + (uint64_t)(uint32_t)j4;

@@ -260,14 +260,23 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
       // weights (the denominator keeps them; 1 / (1 - p) is applied with the normalisation).
       // Element e of half kb is key key0 + 32 kb + 8 (e / 4) + 4 half + e % 4: one draw per
       // group of four e serves four consecutive keys.
-      uint64_t draw[QB];
+      uint64_t draw[QB], dbase[QB];
+      if constexpr (TRAIN) {
+        // draw state of this tile's first key group of the lane (keys key0 + 4 half ..); the
+        // group of element e of half kb is 8 kb + 2 (e / 4) groups further (state steps by
+        // additions)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          dbase[qb] = p.keep_thr ? splitmix_state(p.seed, dropout_counter4((int)bh_q, qwa + 32 * qb + col,
+                                                                          (key0 >> 2) + half))
+                                 : 0ull;
+      }
       auto prob = [&](const f32x16 (&sc)[QB], float (&pv)[QB][16], Frag<bf16> (&pf)[QB][2], int x, int kb) {
         const int qb = x >> 4, e = x & 15;
         pv[qb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][e], p.scale_log2, nm[qb]));
         if constexpr (TRAIN) {
           if ((e & 3) == 0 && p.keep_thr)
-            draw[qb] = dropout_draw(p.seed, dropout_counter4((int)bh_q, qwa + 32 * qb + col,
-                                                              (key0 + 32 * kb + 8 * (e >> 2) + 4 * half) >> 2));
+            draw[qb] = splitmix_mix(dbase[qb] + (uint64_t)(8 * kb + 2 * (e >> 2)) * kSplitmixGamma);
         }
         if (e & 1) {
           pf[qb][e >> 3].v[(e & 7) - 1] = (bf16)pv[qb][e - 1];

@@ -139,27 +139,42 @@ __global__ void __launch_bounds__(256, 1) train_bwd_kv_kernel(TrainBwdParams p) 
   static_assert(AQT * RCH % 256 == 0, "staging chunks split evenly");
   // (the staged registers are plain locals of the loop body below: an array captured by a
   // lambda stays in scratch memory)
-#define MLA_A_GLOAD(qt_, pre, pre_s)                                                                        \
-  {                                                                                             \
-    const int q0_ = (qt_) * AQT;                                                                \
-    _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                           \
-      const int c = tid + 256 * i, r = c / RCH, u = c - r * RCH;                                \
-      const long long row = ((long long)b * S + q0_ + r) * H + h;                               \
-      const bf16* src = u < QCH ? p.q + row * TDQ + 8 * u : p.dO + row * TDV + 8 * (u - QCH);   \
-      pre[i] = *reinterpret_cast<const bf16x8*>(src);                                           \
-    }                                                                                           \
-    if (tid < AQT) pre_s = p.lse[bh * S + q0_ + tid];                                           \
-    else if (tid < 2 * AQT) pre_s = p.D[bh * S + q0_ + tid - AQT];                              \
+  // Chunk i of a thread is a Q chunk for i < NQC and a dO chunk after (the split is a
+  // compile-time fact: 768 Q chunks and 512 dO chunks per tile); its offset inside the tile's
+  // rows is fixed, so a tile costs one add per chunk.  Rows of query q: (b S + q) H + h.
+  constexpr int NQC = AQT * QCH / 256, NOC_ = AQT * OCH / 256;
+  static_assert(NQC * 256 == AQT * QCH && NOC_ * 256 == AQT * OCH && NQC + NOC_ == NCH, "typed chunks");
+  int goff[NCH], loff[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (i < NQC) {
+      const int c = tid + 256 * i, r = c / QCH, u = c - r * QCH;
+      goff[i] = r * H * TDQ + 8 * u;
+      loff[i] = r * QLD + 8 * u;
+    } else {
+      const int c = tid + 256 * (i - NQC), r = c / OCH, u = c - r * OCH;
+      goff[i] = r * H * TDV + 8 * u;
+      loff[i] = r * OLD + 8 * u;
+    }
   }
-#define MLA_A_LSTORE(buf_, pre, pre_s)                                                                      \
-  {                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                           \
-      const int c = tid + 256 * i, r = c / RCH, u = c - r * RCH;                                \
-      bf16* dst = u < QCH ? &Qs[buf_][r * QLD + 8 * u] : &Os[buf_][r * OLD + 8 * (u - QCH)];    \
-      *reinterpret_cast<bf16x8*>(dst) = pre[i];                                                 \
-    }                                                                                           \
-    if (tid < AQT) Ls[buf_][tid] = pre_s;                                                       \
-    else if (tid < 2 * AQT) Dm[buf_][tid - AQT] = pre_s;                                        \
+  const bf16* qbase = p.q + ((long long)b * S * H + h) * TDQ;     // query 0 of (b, h)
+  const bf16* obase = p.dO + ((long long)b * S * H + h) * TDV;
+#define MLA_A_GLOAD(qt_, pre, pre_s)                                                          \
+  {                                                                                           \
+    const int q0_ = (qt_) * AQT;                                                              \
+    const bf16* qt_base = qbase + (long long)q0_ * H * TDQ;                                   \
+    const bf16* ot_base = obase + (long long)q0_ * H * TDV;                                   \
+    _Pragma("unroll") for (int i = 0; i < NCH; ++i)                                           \
+      pre[i] = *reinterpret_cast<const bf16x8*>((i < NQC ? qt_base : ot_base) + goff[i]);     \
+    if (tid < AQT) pre_s = p.lse[bh * S + q0_ + tid];                                         \
+    else if (tid < 2 * AQT) pre_s = p.D[bh * S + q0_ + tid - AQT];                            \
+  }
+#define MLA_A_LSTORE(buf_, pre, pre_s)                                                        \
+  {                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < NCH; ++i)                                           \
+      *reinterpret_cast<bf16x8*>(i < NQC ? &Qs[buf_][loff[i]] : &Os[buf_][loff[i]]) = pre[i]; \
+    if (tid < AQT) Ls[buf_][tid] = pre_s;                                                     \
+    else if (tid < 2 * AQT) Dm[buf_][tid - AQT] = pre_s;                                      \
   }
   // the accumulators live in accumulation registers across tiles (without this the compiler
   // keeps them in VGPRs for the products and parks them in AGPRs between tiles: 320 copies
@@ -189,11 +204,12 @@ _Pragma("unroll") \
       /* shares them */ \
       unsigned keep = 0xFFFFu; \
       if (p.keep_thr) { \
-        const int r = col & 3; \
+        /* the draws' states step by additions: + 8 queries per group (dstate: this tile's */ \
+        /* first, for query q0 + 4 half + col % 4 and key / 4) */ \
         uint64_t dr[4]; \
 _Pragma("unroll") \
         for (int g4 = 0; g4 < 4; ++g4) \
-          dr[g4] = dropout_draw(p.seed, dropout_counter4((int)bh, q0 + 8 * g4 + 4 * half + r, key >> 2)); \
+          dr[g4] = splitmix_mix(dstate + (uint64_t)(8 * g4) * ((1ull << 18) * kSplitmixGamma)); \
         const int sh = 16 * (col & 3); \
         keep = 0; \
 _Pragma("unroll") \
@@ -245,6 +261,9 @@ _Pragma("unroll") \
   float pa_s = 0.f;
 
   const int qt0 = k0 / AQT, nqt = S / AQT;
+  // dropout draw state of tile qt0 for query qt0 AQT + 4 half + col % 4 and the lane's key
+  // group (stepped by AQT queries per tile)
+  uint64_t dstate = splitmix_state(p.seed, dropout_counter4((int)bh, qt0 * AQT + 4 * half + (col & 3), key >> 2));
   MLA_A_GLOAD(qt0, pa, pa_s);
   MLA_A_LSTORE(0, pa, pa_s);
   __syncthreads();
@@ -252,6 +271,7 @@ _Pragma("unroll") \
     const int buf = (qt - qt0) & 1;
     if (qt + 1 < nqt) MLA_A_GLOAD(qt + 1, pa, pa_s);
     MLA_A_TILE(buf, qt);
+    dstate += (uint64_t)AQT * ((1ull << 18) * kSplitmixGamma);
     if (qt + 1 < nqt) MLA_A_LSTORE(buf ^ 1, pa, pa_s);
     MLA_A_PIN();
     __syncthreads();
@@ -336,39 +356,57 @@ __global__ void __launch_bounds__(256, 1) train_bwd_q_kernel(TrainBwdParams p) {
   constexpr int KCH = TDQ / 8, NKC = BKT * KCH, NVC = TDV * (BKT / 8);
   constexpr int NCH = (NKC + NVC) / 256;   // 10 per thread
   static_assert((NKC + NVC) % 256 == 0 && NKC % 256 == 0, "staging chunks split evenly");
+  // Chunk i of a thread: decompressed-key chunks for i < 4, rotary-key chunks for i < 6,
+  // value chunks after (1024 + 512 + 1024 per tile); offsets fixed, one add per chunk a tile.
+  constexpr int NKN = BKT * (TDN / 8) / 256, NKR = BKT * (TDR / 8) / 256, NVV = TDV * (BKT / 8) / 256;
+  static_assert(NKN * 256 == BKT * (TDN / 8) && NKR * 256 == BKT * (TDR / 8) && NVV * 256 == TDV * (BKT / 8) &&
+                NKN + NKR + NVV == NCH, "typed chunks");
+  int goff[NCH], loff[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (i < NKN) {
+      const int c = tid + 256 * i, r = c / (TDN / 8), u = c - r * (TDN / 8);
+      goff[i] = r * TDN + 8 * u;
+      loff[i] = r * KLD + 8 * u;
+    } else if (i < NKN + NKR) {
+      const int c = tid + 256 * (i - NKN), r = c / (TDR / 8), u = c - r * (TDR / 8);
+      goff[i] = r * TDR + 8 * u;
+      loff[i] = r * KLD + TDN + 8 * u;
+    } else {
+      const int c = tid + 256 * (i - NKN - NKR), d = c >> 3, u = c & 7;
+      goff[i] = d * S + 8 * u;
+      loff[i] = (d << 3) | u;          // value row d, slot group u (stored element by element)
+    }
+  }
+  const bf16* kfb = p.kf + bh * S * TDN;                 // key 0 of (b, h)
+  const bf16* krb = p.kr + (long long)b * S * TDR;
+  const bf16* vtb = p.vt + bh * TDV * S;
 #define MLA_B_GLOAD(kt_)                                                                          \
   {                                                                                               \
     const int kt0_ = (kt_) * BKT;                                                                 \
     _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                             \
-      const int c = tid + 256 * i;                                                                \
-      const bf16* src;                                                                            \
-      if (c < NKC) {                                                                              \
-        const int r = c / KCH, u = c - r * KCH;                                                   \
-        src = u < TDN / 8 ? p.kf + (bh * S + kt0_ + r) * TDN + 8 * u                              \
-                          : p.kr + ((long long)b * S + kt0_ + r) * TDR + 8 * (u - TDN / 8);       \
-      } else {                                                                                    \
-        const int cv = c - NKC, d = cv >> 3, u = cv & 7;                                          \
-        src = p.vt + (bh * TDV + d) * S + kt0_ + 8 * u;                                           \
-      }                                                                                           \
-      pre[i] = *reinterpret_cast<const bf16x8*>(src);                                             \
+      const bf16* src = i < NKN ? kfb + (long long)kt0_ * TDN : i < NKN + NKR ? krb + (long long)kt0_ * TDR \
+                                                                                : vtb + kt0_;     \
+      pre[i] = *reinterpret_cast<const bf16x8*>(src + goff[i]);                                   \
     }                                                                                             \
   }
 #define MLA_B_LSTORE(buf_)                                                                        \
   {                                                                                               \
     _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                             \
-      const int c = tid + 256 * i;                                                                \
-      if (c < NKC) {                                                                              \
-        const int r = c / KCH, u = c - r * KCH;                                                   \
-        *reinterpret_cast<bf16x8*>(&Ks[buf_][r * KLD + 8 * u]) = pre[i];                          \
+      if (i < NKN + NKR) {                                                                        \
+        *reinterpret_cast<bf16x8*>(&Ks[buf_][loff[i]]) = pre[i];                                  \
       } else {                                                                                    \
         /* value row d, slots 8 u .. 8 u + 7 of the tile -> keys perm16(slot), column d */        \
-        const int cv = c - NKC, d = cv >> 3, u = cv & 7;                                          \
+        const int d = loff[i] >> 3, u = loff[i] & 7;                                              \
         _Pragma("unroll") for (int j = 0; j < 8; ++j) Vs[buf_][perm16(8 * u + j) * VLD + d] = pre[i][j]; \
       }                                                                                           \
     }                                                                                             \
   }
   bf16x8 pre[NCH];
 
+  // dropout draw state of the current key tile for the lane's query and keys kt0 + 4 half ..
+  // (stepped by BKT / 4 draws per tile)
+  uint64_t dstate = splitmix_state(p.seed, dropout_counter4((int)bh, qi, half));
   auto compute = [&](int buf, int kt) {
     const int kt0 = kt * BKT;
     const bf16* K = Ks[buf];
@@ -392,7 +430,9 @@ __global__ void __launch_bounds__(256, 1) train_bwd_q_kernel(TrainBwdParams p) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int kg = kb0 + 8 * g4 + 4 * half;
-        const uint64_t dr = p.keep_thr ? dropout_draw(p.seed, dropout_counter4((int)bh, qi, kg >> 2)) : 0ull;
+        // draw for keys kg .. kg + 3: the tile's state stepped by (kb0 - kt0 + 8 g4) / 4
+        const uint64_t dr =
+            p.keep_thr ? splitmix_mix(dstate + (uint64_t)(8 * kh + 2 * g4) * kSplitmixGamma) : 0ull;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * g4 + j;
@@ -421,6 +461,7 @@ __global__ void __launch_bounds__(256, 1) train_bwd_q_kernel(TrainBwdParams p) {
     const int buf = kt & 1;
     if (kt + 1 < nkt) MLA_B_GLOAD(kt + 1);
     if (kt * BKT <= qw + 31) compute(buf, kt);
+    dstate += (uint64_t)(BKT / 4) * kSplitmixGamma;
     if (kt + 1 < nkt) MLA_B_LSTORE(buf ^ 1);
 #pragma unroll
     for (int i = 0; i < TDQ / 32; ++i) asm volatile("" : "+a"(dq[i]));   // (as in the key kernel)
