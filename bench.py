@@ -915,6 +915,8 @@ def main():
         "roofline": {"kernel": "mla_decode_attention unit (split kernel + combine)", "bound": "hbm",
                      "achieved": ml["attention_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ml["attention_GBps"] / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles("mlra_decode_attention",
+                                                      src_digest(*UNIT_SOURCES["mlra_decode_attention"])),
                      "algorithmic_bytes_per_launch": ml["cache_bytes"], "ms_per_launch": ml["attention_ms"]},
     }
     lh = out["mlra_lh"]
@@ -925,6 +927,8 @@ def main():
         "roofline": {"kernel": "mla_decode_attention unit (token-split kernel + combine)", "bound": "hbm",
                      "achieved": lh["attention_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": lh["attention_GBps"] / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles("mlra_latent_head_decode_attention",
+                                                      src_digest(*UNIT_SOURCES["mlra_latent_head_decode_attention"])),
                      "algorithmic_bytes_per_launch": lh["cache_bytes"], "ms_per_launch": lh["attention_ms"]},
     }
     sm = out["small"]
