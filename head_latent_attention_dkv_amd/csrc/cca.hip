@@ -67,6 +67,108 @@ PrepLds prep_lds(const CcaPrepParams& p) {
   return l;
 }
 
+// The steps after the convolutions and the q-k-mean, shared by both kernels: the key head's
+// value rows staged in vs ([TB][dh + 1], shifted by one token in the second half of the value
+// channels), the per-row L2 norm of o ([TB][dh]) with the key temperature, the half-split
+// rotation, and the stores of q / k / v.  Every thread of the workgroup calls it; o is complete
+// and vs free when it is called.
+template <typename T>
+__device__ __forceinline__ void cca_finish(const CcaPrepParams& p, float* o, float* vs, float* rscale, int dh,
+                                           int t0, int g, int b, int tid) {
+  const bool is_q = g < p.Hq;
+  const int Lkv = p.Hkv * dh;
+  // the key head's value rows of the block, shifted by one token in the second half of the
+  // value channels (read along the channels; stored below)
+  if (!is_q) {
+    const int j = g - p.Hq;
+    for (int e0 = tid; e0 < TB * dh; e0 += kUnroll * 256) {
+      float v[kUnroll];
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        const int e = e0 + 256 * k;
+        const int r = e / dh, c = e - r * dh;
+        const int t = t0 + r, ch = j * dh + c;
+        const int ts = (p.value_shift && ch >= Lkv / 2) ? t - 1 : t;
+        v[k] = (e < TB * dh && t < p.S && ts >= 0) ? p.V[((long long)b * p.S + ts) * Lkv + ch] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        const int e = e0 + 256 * k;
+        const int r = e / dh, c = e - r * dh;
+        if (e < TB * dh) vs[r * (dh + 1) + c] = v[k];
+      }
+    }
+  }
+  __syncthreads();
+
+  // per-row L2 norm over the head's d_h channels (4 threads per row)
+  {
+    const int r = tid >> 2, l = tid & 3;
+    float ss = 0.f;
+    for (int c = l; c < dh; c += 4) ss = __builtin_fmaf(o[r * dh + c], o[r * dh + c], ss);
+    ss += __shfl_xor(ss, 2, 4);
+    ss += __shfl_xor(ss, 1, 4);
+    if (l == 0) rscale[r] = p.sqrt_dh / fmaxf(sqrtf(ss), 1e-6f) * (is_q ? 1.f : p.key_gain);
+  }
+  __syncthreads();
+
+  // half-split rotation at the token's position, then the store
+  const int half = dh >> 1;
+  T* dst = is_q ? reinterpret_cast<T*>(p.q) : reinterpret_cast<T*>(p.k);
+  const int nh = is_q ? p.Hq : p.Hkv, hh = is_q ? g : g - p.Hq;
+  const int dw = p.flash ? p.dqp : dh;                  // stored features per head row
+  auto qk_row = [&](int t) -> T* {
+    if (p.flash && !is_q) return dst + (((long long)b * p.Hkv + hh) * p.S + t) * dw;   // head-major keys
+    return dst + (((long long)b * p.S + t) * nh + hh) * dw;
+  };
+  for (int e = tid; e < TB * half; e += 256) {
+    const int r = e / half, jj = e - r * half;
+    const int t = t0 + r;
+    if (t >= p.S) continue;
+    const float x1 = o[r * dh + jj] * rscale[r], x2 = o[r * dh + jj + half] * rscale[r];
+    float sn, cs;
+    rope_sincos(t, p.rope.hi[jj], p.rope.lo[jj], &sn, &cs);
+    T* row = qk_row(t);
+    row[jj] = from_f32<T>(x1 * cs - x2 * sn);
+    row[jj + half] = from_f32<T>(x1 * sn + x2 * cs);
+  }
+  if (dw > dh) {                                        // zero padding of the feature rows
+    const int pad = dw - dh;
+    for (int e = tid; e < TB * pad; e += 256) {
+      const int r = e / pad, c = dh + e - r * pad;
+      if (t0 + r < p.S) qk_row(t0 + r)[c] = from_f32<T>(0.f);
+    }
+  }
+
+  // the key head's values (staged above)
+  if (!is_q) {
+    const int j = g - p.Hq;
+    T* vdst = reinterpret_cast<T*>(p.v);
+    if (p.flash) {
+      // transposed per head: feature row c holds the tokens, each 16-group stored in the
+      // order 0-3, 8-11, 4-7, 12-15 (token slots 4-7 and 8-11 swapped); consecutive threads
+      // take consecutive tokens of one row (the staged rows' padded stride keeps the column
+      // reads on distinct banks)
+      for (int e = tid; e < TB * dw; e += 256) {
+        const int c = e / TB, r = e - c * TB;
+        const int t = t0 + r;
+        if (t >= p.S) continue;
+        const float val = c < dh ? vs[r * (dh + 1) + c] : 0.f;
+        const int t16 = t & 15;
+        const int slot = (t & ~15) + ((t16 >= 4 && t16 < 8) ? t16 + 4 : (t16 >= 8 && t16 < 12) ? t16 - 4 : t16);
+        vdst[(((long long)b * p.Hkv + j) * dw + c) * p.S + slot] = from_f32<T>(val);
+      }
+    } else {
+      for (int e = tid; e < TB * dh; e += 256) {
+        const int r = e / dh, c = e - r * dh;
+        const int t = t0 + r;
+        if (t >= p.S) continue;
+        vdst[(((long long)b * p.S + t) * p.Hkv + j) * dh + c] = from_f32<T>(vs[r * (dh + 1) + c]);
+      }
+    }
+  }
+}
+
 // DH: the head width as a compile-time constant (32, 64, 128), or 0 for any other width.
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) cca_prep_kernel(CcaPrepParams p, PrepLds lay) {
@@ -234,96 +336,167 @@ __global__ void __launch_bounds__(256) cca_prep_kernel(CcaPrepParams p, PrepLds 
     for (int r = 0; r < TPT; ++r)
       if (r < tpt && rbeg + r < TB) o[(rbeg + r) * dh + oc] = acc[r];
   }
-  // the key head's value rows of the block, shifted by one token in the second half of the
-  // value channels (read along the channels; stored below)
-  if (!is_q) {
-    const int j = g - p.Hq;
+  cca_finish<T>(p, o, vs, rscale, dh, t0, g, b, tid);
+}
+
+// MFMA form of the grouped channel convolution for bf16 layers with both convolutions and a
+// head width of 32, 64 or 128: for each tap j the contraction over input channels is a
+// [64 tokens x d_h] x [d_h x d_h] product, A_j[t][c] = a0[t + j][c] (the sequence
+// convolution's output, shifted by j rows) and B_j[c][oc] = w[oc][c][j]; a0 is kept in LDS
+// in bf16 and the tap's weights are staged [oc][c], both read with plain 16-byte operand
+// reads (32x32x16 MFMA, fp32 accumulation).  The other steps are those of cca_prep_kernel.
+struct PrepLdsM {
+  int R, R1, ald, wld;                 // staged rows, conv rows, LDS strides of a0 and a tap (bf16)
+  size_t u_fl, a0_bytes, w_bytes, o_fl;
+  size_t bytes;
+};
+
+PrepLdsM prep_lds_mfma(const CcaPrepParams& p) {
+  PrepLdsM l;
+  const int h0 = p.kseq - 1, h1 = p.kch - 1;
+  l.R = TB + h0 + h1;
+  l.R1 = TB + h1;
+  l.ald = p.dh + 8;
+  l.wld = p.dh + 8;
+  // u holds the staged rows, later the value rows ([TB][dh + 1])
+  l.u_fl = (size_t)l.R * p.dh > (size_t)TB * (p.dh + 1) ? (size_t)l.R * p.dh : (size_t)TB * (p.dh + 1);
+  l.a0_bytes = ((size_t)(TB + kCcaMaxKernel - 1) * l.ald * 2 + 15) / 16 * 16;
+  l.w_bytes = ((size_t)p.dh * l.wld * 2 + 15) / 16 * 16;
+  l.o_fl = (size_t)TB * p.dh;
+  l.bytes = l.u_fl * 4 + l.a0_bytes + l.w_bytes + l.o_fl * 4 + (size_t)p.dh * p.kseq * 4 + TB * 4;
+  return l;
+}
+
+template <int DH>
+__global__ void __launch_bounds__(256) cca_prep_mfma_kernel(CcaPrepParams p, PrepLdsM lay) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  constexpr int dh = DH;
+  const int t0 = blockIdx.x * TB, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const bool is_q = g < p.Hq;
+  const int Lq = p.Hq * dh, Lkv = p.Hkv * dh, Cp = Lq + Lkv;
+  const int gs = p.Hq / p.Hkv;
+  const int c0 = is_q ? g * dh : Lq + (g - p.Hq) * dh;
+  const int kseq = p.kseq, kch = p.kch, h0 = kseq - 1, h1 = kch - 1;
+  const float* P = p.P + (long long)b * p.S * Cp;
+  const bf16* wseq = reinterpret_cast<const bf16*>(p.conv_seq);
+  const bf16* wch = reinterpret_cast<const bf16*>(p.conv_ch);
+  const int R = lay.R, R1 = lay.R1, ALD = lay.ald, WLD = lay.wld;
+  float* u = sm;                                                           // [R][dh], later vs
+  bf16* a0b = reinterpret_cast<bf16*>(u + lay.u_fl);                       // [TB + 7][ALD]
+  bf16* wt = reinterpret_cast<bf16*>(reinterpret_cast<char*>(a0b) + lay.a0_bytes);   // [dh][WLD]
+  float* o = reinterpret_cast<float*>(reinterpret_cast<char*>(wt) + lay.w_bytes);    // [TB][dh]
+  float* wsq = o + lay.o_fl;                                               // [dh][kseq]
+  float* rscale = wsq + dh * kseq;                                         // [TB]
+
+  // packed rows t0 - h0 - h1 .. t0 + TB - 1 and the head's sequence-convolution weights
+  for (int e0 = tid; e0 < R * dh; e0 += kUnroll * 256) {
+    float v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int e = e0 + 256 * k;
+      const int i = e / dh, c = e - i * dh;
+      const int t = t0 - h0 - h1 + i;
+      v[k] = (e < R * dh && t >= 0 && t < p.S) ? P[(long long)t * Cp + c0 + c] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+      if (e0 + 256 * k < R * dh) u[e0 + 256 * k] = v[k];
+  }
+  for (int e = tid; e < dh * kseq; e += 256) wsq[e] = (float)wseq[(long long)c0 * kseq + e];
+  __syncthreads();
+
+  // depth-wise sequence convolution into a0b (bf16): row i is token t0 - h1 + i, zero before
+  // the sequence
+  for (int e = tid; e < R1 * dh; e += 256) {
+    const int i = e / dh, c = e - i * dh;
+    float acc = 0.f;
+    if (t0 - h1 + i >= 0)
+      for (int j = 0; j < kseq; ++j) acc = __builtin_fmaf(wsq[c * kseq + j], u[(i + j) * dh + c], acc);
+    a0b[i * ALD + c] = (bf16)acc;
+  }
+
+  // grouped channel convolution: wave w takes output blocks w and w + 4 of the 2 x dh / 32
+  // blocks of 32 tokens x 32 channels
+  constexpr int NB = 2 * (dh / 32), BPW = (NB + 3) / 4;
+  f32x16 acc[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) acc[i] = f32x16{};
+  for (int j = 0; j < kch; ++j) {
+    __syncthreads();                  // a0b complete / the previous tap's weights consumed
+    // tap j's weights: wt[oc][c] = w[c0 + oc][c][j] (dh^2 / 256 loads per thread, all in flight)
+    {
+      constexpr int NWE = dh * dh / 256;
+      bf16 wv[NWE];
+#pragma unroll
+      for (int k = 0; k < NWE; ++k) {
+        const int e = tid + 256 * k, oc = e / dh, c = e - oc * dh;
+        wv[k] = wch[((long long)(c0 + oc) * dh + c) * kch + j];
+      }
+#pragma unroll
+      for (int k = 0; k < NWE; ++k) {
+        const int e = tid + 256 * k, oc = e / dh, c = e - oc * dh;
+        wt[oc * WLD + c] = wv[k];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wave + 4 * i;
+      if (blk < NB) {
+        const int mb = blk & 1, nb = blk >> 1;
+#pragma unroll
+        for (int ks = 0; ks < dh / 16; ++ks) {
+          const Frag<bf16> fa = frag_load(a0b + (32 * mb + col + j) * ALD + 16 * ks + 8 * half);
+          const Frag<bf16> fb = frag_load(wt + (32 * nb + col) * WLD + 16 * ks + 8 * half);
+          acc[i] = mma32(fa, fb, acc[i]);
+        }
+      }
+    }
+  }
+  // o[t][oc]: lane column oc = 32 nb + col, rows t = 32 mb + 8 (e / 4) + 4 half + e % 4
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + 4 * i;
+    if (blk < NB) {
+      const int mb = blk & 1, nb = blk >> 1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[(32 * mb + 8 * (e >> 2) + 4 * half + (e & 3)) * dh + 32 * nb + col] = acc[i][e];
+    }
+  }
+  __syncthreads();
+
+  // q-k-mean of the pre-convolution values (the head's own are in u; its partner heads'
+  // come from the packed projections)
+  if (p.qk_mean) {
+    // partner values loaded kUnroll elements at a time (all in flight), then added
+    const int jh = g - p.Hq;
     for (int e0 = tid; e0 < TB * dh; e0 += kUnroll * 256) {
-      float v[kUnroll];
+      float m[kUnroll];
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
-        const int e = e0 + 256 * k;
-        const int r = e / dh, c = e - r * dh;
-        const int t = t0 + r, ch = j * dh + c;
-        const int ts = (p.value_shift && ch >= Lkv / 2) ? t - 1 : t;
-        v[k] = (e < TB * dh && t < p.S && ts >= 0) ? p.V[((long long)b * p.S + ts) * Lkv + ch] : 0.f;
+        const int e = e0 + 256 * k, r = e / dh, c = e - r * dh, t = t0 + r;
+        m[k] = 0.f;
+        if (e < TB * dh && t < p.S) {
+          const float* row = P + (long long)t * Cp;
+          if (is_q) {
+            m[k] = row[Lq + (g / gs) * dh + c];
+          } else {
+            for (int hq = jh * gs; hq < (jh + 1) * gs; ++hq) m[k] += row[hq * dh + c];
+            m[k] /= (float)gs;
+          }
+        }
       }
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
-        const int e = e0 + 256 * k;
-        const int r = e / dh, c = e - r * dh;
-        if (e < TB * dh) vs[r * (dh + 1) + c] = v[k];
+        const int e = e0 + 256 * k, r = e / dh, c = e - r * dh;
+        if (e < TB * dh && t0 + r < p.S) o[e] += 0.5f * (m[k] + u[(r + h0 + h1) * dh + c]);
       }
     }
   }
-  __syncthreads();
-
-  // per-row L2 norm over the head's d_h channels (4 threads per row)
-  {
-    const int r = tid >> 2, l = tid & 3;
-    float ss = 0.f;
-    for (int c = l; c < dh; c += 4) ss = __builtin_fmaf(o[r * dh + c], o[r * dh + c], ss);
-    ss += __shfl_xor(ss, 2, 4);
-    ss += __shfl_xor(ss, 1, 4);
-    if (l == 0) rscale[r] = p.sqrt_dh / fmaxf(sqrtf(ss), 1e-6f) * (is_q ? 1.f : p.key_gain);
-  }
-  __syncthreads();
-
-  // half-split rotation at the token's position, then the store
-  const int half = dh >> 1;
-  T* dst = is_q ? reinterpret_cast<T*>(p.q) : reinterpret_cast<T*>(p.k);
-  const int nh = is_q ? p.Hq : p.Hkv, hh = is_q ? g : g - p.Hq;
-  const int dw = p.flash ? p.dqp : dh;                  // stored features per head row
-  auto qk_row = [&](int t) -> T* {
-    if (p.flash && !is_q) return dst + (((long long)b * p.Hkv + hh) * p.S + t) * dw;   // head-major keys
-    return dst + (((long long)b * p.S + t) * nh + hh) * dw;
-  };
-  for (int e = tid; e < TB * half; e += 256) {
-    const int r = e / half, jj = e - r * half;
-    const int t = t0 + r;
-    if (t >= p.S) continue;
-    const float x1 = o[r * dh + jj] * rscale[r], x2 = o[r * dh + jj + half] * rscale[r];
-    float sn, cs;
-    rope_sincos(t, p.rope.hi[jj], p.rope.lo[jj], &sn, &cs);
-    T* row = qk_row(t);
-    row[jj] = from_f32<T>(x1 * cs - x2 * sn);
-    row[jj + half] = from_f32<T>(x1 * sn + x2 * cs);
-  }
-  if (dw > dh) {                                        // zero padding of the feature rows
-    const int pad = dw - dh;
-    for (int e = tid; e < TB * pad; e += 256) {
-      const int r = e / pad, c = dh + e - r * pad;
-      if (t0 + r < p.S) qk_row(t0 + r)[c] = from_f32<T>(0.f);
-    }
-  }
-
-  // the key head's values (staged above)
-  if (!is_q) {
-    const int j = g - p.Hq;
-    T* vdst = reinterpret_cast<T*>(p.v);
-    if (p.flash) {
-      // transposed per head: feature row c holds the tokens, each 16-group stored in the
-      // order 0-3, 8-11, 4-7, 12-15 (token slots 4-7 and 8-11 swapped); consecutive threads
-      // take consecutive tokens of one row (the staged rows' padded stride keeps the column
-      // reads on distinct banks)
-      for (int e = tid; e < TB * dw; e += 256) {
-        const int c = e / TB, r = e - c * TB;
-        const int t = t0 + r;
-        if (t >= p.S) continue;
-        const float val = c < dh ? vs[r * (dh + 1) + c] : 0.f;
-        const int t16 = t & 15;
-        const int slot = (t & ~15) + ((t16 >= 4 && t16 < 8) ? t16 + 4 : (t16 >= 8 && t16 < 12) ? t16 - 4 : t16);
-        vdst[(((long long)b * p.Hkv + j) * dw + c) * p.S + slot] = from_f32<T>(val);
-      }
-    } else {
-      for (int e = tid; e < TB * dh; e += 256) {
-        const int r = e / dh, c = e - r * dh;
-        const int t = t0 + r;
-        if (t >= p.S) continue;
-        vdst[(((long long)b * p.S + t) * p.Hkv + j) * dh + c] = from_f32<T>(vs[r * (dh + 1) + c]);
-      }
-    }
-  }
+  __syncthreads();                    // u is free: the value rows take its place
+  cca_finish<bf16>(p, o, u, rscale, dh, t0, g, b, tid);
 }
 
 }  // namespace
@@ -335,6 +508,13 @@ hipError_t launch_cca_prep(const CcaPrepParams& p, bool use_bf16, hipStream_t s)
   if (p.flash && (p.dqp < p.dh || p.S % 16 != 0)) return hipErrorInvalidValue;
   const PrepLds lay = prep_lds(p);
   const dim3 grid(cdiv(p.S, TB), p.Hq + p.Hkv, p.B);
+  if (use_bf16 && p.layers == 2 && (p.dh == 32 || p.dh == 64 || p.dh == 128)) {
+    const PrepLdsM lm = prep_lds_mfma(p);
+    if (p.dh == 32) hipLaunchKernelGGL(cca_prep_mfma_kernel<32>, grid, dim3(256), lm.bytes, s, p, lm);
+    else if (p.dh == 64) hipLaunchKernelGGL(cca_prep_mfma_kernel<64>, grid, dim3(256), lm.bytes, s, p, lm);
+    else hipLaunchKernelGGL(cca_prep_mfma_kernel<128>, grid, dim3(256), lm.bytes, s, p, lm);
+    return hipGetLastError();
+  }
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, p, lay); };
   if (use_bf16) {
     if (p.dh == 32) go(cca_prep_kernel<bf16, 32>);
