@@ -26,6 +26,9 @@ DSV2_T = S.CONFIGS["dsv2_prefill"].replace(name="dsv2_train", d_model=256, n_hea
 # a ragged last block of 64; three heads: (sequence, head) groups not a multiple of 8)
 DSV2_F = DSV2_T.replace(name="dsv2_train_flash", seq=320)
 DSV2_F3 = DSV2_T.replace(name="dsv2_train_flash_h3", n_heads=3, d_model=192, seq=192)
+# one 64-token tile and a single sequence; a longer sequence (eight key blocks of 128)
+DSV2_F1 = DSV2_T.replace(name="dsv2_train_flash_s64", batch=1, seq=64)
+DSV2_FL = DSV2_T.replace(name="dsv2_train_flash_s1024", batch=1, n_heads=4, d_model=256, seq=1024)
 
 
 @pytest.fixture(scope="module")
@@ -87,9 +90,10 @@ def _oracle(cfg, W, p, seed, xs, dys):
 
 
 @pytest.mark.parametrize("cfg,p,seed", [(TINY, 0.3, 42), (TINY, 0.0, 1), (DSV2_T, 0.1, 7), (DSV2_T, 0.5, 9),
-                                        (DSV2_F, 0.1, 7), (DSV2_F, 0.5, 9), (DSV2_F, 0.0, 2), (DSV2_F3, 0.25, 3)],
+                                        (DSV2_F, 0.1, 7), (DSV2_F, 0.5, 9), (DSV2_F, 0.0, 2), (DSV2_F3, 0.25, 3),
+                                        (DSV2_F1, 0.9, 5), (DSV2_FL, 0.2, 13)],
                          ids=["tiny_p0.3", "tiny_p0", "dsv2_p0.1", "dsv2_p0.5", "flash_p0.1", "flash_p0.5",
-                              "flash_p0", "flash_h3_p0.25"])
+                              "flash_p0", "flash_h3_p0.25", "flash_s64_p0.9", "flash_s1024_p0.2"])
 def test_train_forward_backward(gu, cfg, p, seed):
     gu.say(f"[train] {cfg.name} p={p} seed={seed} B={cfg.batch} S={cfg.seq}")
     rng = np.random.default_rng(seed)
