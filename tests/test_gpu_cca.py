@@ -63,6 +63,9 @@ VARIANTS = [
     (GQA_S.replace(name="ccgqa_s320", seq=320), {}),
     (GQA_S.replace(name="ccgqa_dh128_s256", head_dim=128, seq=256), {}),
     (GQA_S.replace(name="ccgqa_dh32_s64", head_dim=32, seq=64), dict(num_conv_layers=1, value_shift=False)),
+    # the longest convolution kernels the library takes, and odd ones (MFMA channel convolution)
+    (CCA_S.replace(name="cca_k8_s128", seq=128), dict(conv_kernel_seq=8, conv_kernel_ch=8)),
+    (GQA_S.replace(name="ccgqa_k2k5_s192", seq=192), dict(conv_kernel_seq=2, conv_kernel_ch=5)),
 ]
 
 
