@@ -75,7 +75,7 @@ def _train(gu, cfg, p, seed, xs, dys):
 
 
 def _oracle(cfg, W, p, seed, xs, dys):
-    p = float(np.float32(p))       # the library takes p as a float32 (keep threshold floor(p 2^32))
+    p = float(np.float32(p))       # the library takes p as a float32 (keep threshold floor(p 2^16))
     d = O.Dims.from_cfg(cfg)
     ys, gs = [], {}
     for b, (x, dy) in enumerate(zip(xs, dys)):
