@@ -278,6 +278,256 @@ __global__ void __launch_bounds__(64 * NW, BigCfg<NW>::MINB) gemm_big_kernel(Gem
   }
 }
 
+
+// ---- Flash-layout K/V up-projection, persistent form ----
+//
+// The prefill keys / values (the output stage of DIRECT above) from 256 x 256 tiles held by
+// four waves of 128 x 128 (4 x 4 accumulator blocks each, in the accumulation registers):
+// per 16-wide k-step a wave reads 8 operand fragments for 16 products, two thirds of the LDS
+// operand bytes per product of the 64 x 128 wave tile, whose two waves per SIMD left the
+// main loop bound by LDS traffic.  One workgroup per CU walks its tiles with the copy
+// pipeline running across tile boundaries: while a tile's results are stored, the next
+// tile's first two stages are already in flight, so no workgroup start, operand prologue or
+// drain sits between tiles.  The key transposes use a per-wave LDS buffer of their own.
+//
+// The stores of a tile are in flight together with the next tile's copies (the exception for
+// stores in lds_dma.h: a wait for "all but the newest N copies" stays exact for the copies).
+constexpr int KVP_T = 256;                         // tile rows and columns
+constexpr int KVP_NST = 3;                         // LDS stages
+constexpr int KVP_AB = KVP_T * GBK * 2;            // bytes per operand per stage (16 KB)
+constexpr int KVP_STAGE = 2 * KVP_AB;
+constexpr int KVP_CPW = KVP_AB / 1024 / 4;         // copies per wave per operand per stage
+constexpr int KVP_DPW = 2 * KVP_CPW;
+constexpr size_t KVP_TR = (size_t)KVP_NST * KVP_STAGE;   // key transpose buffers follow the stages
+constexpr size_t KVP_LDS = KVP_TR + 4 * KV_BUF;
+static_assert(KVP_LDS <= 160 * 1024, "LDS budget");
+static_assert(128 * 64 <= KV_BUF, "the value transpose (128 rows of 64 bytes) fits a key transpose buffer");
+
+// Tile i of workgroup w (tiles: mt row tiles x nt column tiles).  With whole XCD groups,
+// XCD x (workgroups w = x mod 8) takes the column tiles x nt/8 .. (x+1) nt/8 - 1 in phases
+// of up to 8, each phase over all row tiles, and its workgroups deal the XCD's list out
+// round-robin: the XCD's 32 workgroups then hold a few row tiles and one phase's weight
+// rows (8 x 256 x K bf16, 2 MB at K = 512) in its L2.
+struct KvpOrder {
+  int mt, nt, G, xcd, j, gx, per, pw, count;
+  __device__ KvpOrder(int mt_, int nt_, int G_, int w) : mt(mt_), nt(nt_), G(G_) {
+    if (G % 8 == 0 && nt % 8 == 0) {
+      xcd = w & 7;
+      j = w >> 3;
+      gx = G >> 3;
+      per = nt >> 3;
+      pw = per % 8 == 0 ? 8 : per;
+      const int len = per * mt;
+      count = j < len ? (len - 1 - j) / gx + 1 : 0;
+    } else {
+      xcd = -1;
+      j = w;
+      count = j < mt * nt ? (mt * nt - 1 - j) / G + 1 : 0;
+    }
+  }
+  __device__ void tile(int i, int& by, int& bx) const {
+    if (xcd >= 0) {
+      const int e = j + gx * i;
+      const int ph = e / (mt * pw), rem = e - ph * (mt * pw);
+      by = rem / pw;
+      bx = xcd * per + ph * pw + (rem - by * pw);
+    } else {
+      const int t = j + G * i;
+      by = t / nt;
+      bx = t - by * nt;
+    }
+  }
+};
+
+__global__ void __launch_bounds__(256, 1) gemm_kv_kernel(GemmParams p, int mt, int nt) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;           // 128-row block wm, 128-column block wn
+  const int col = lane & 31, half = lane >> 5;
+  const int N = p.seg[0].n + (p.nseg > 1 ? p.seg[1].n : 0);
+  const int nst = p.K / GBK;
+  const KvpOrder ord(mt, nt, gridDim.x, blockIdx.x);
+  const int total = ord.count * nst;                 // stages this workgroup consumes
+  if (total == 0) return;
+
+  // copy j of wave w covers rows 16 (KVP_CPW w + j) + lane / 4 of each operand, physical
+  // chunk lane % 4 (logical chunk (lane % 4) ^ ((row >> 2) & 3))
+  const bf16* asrc[KVP_CPW];
+  const bf16* wsrc[KVP_CPW];
+  auto set_src = [&](int i) {
+    int by, bx;
+    ord.tile(i, by, bx);
+#pragma unroll
+    for (int j = 0; j < KVP_CPW; ++j) {
+      const int t = 16 * (KVP_CPW * wave + j) + lane / 4;
+      const int c = (lane & 3) ^ ((t >> 2) & 3);
+      const int m = min(by * KVP_T + t, p.M - 1);
+      asrc[j] = reinterpret_cast<const bf16*>(p.a) + big_a_row(p, m) * p.a_ld + 8 * c;
+      const int n = min(bx * KVP_T + t, N - 1);
+      const int s = (n < p.seg[0].n) ? 0 : 1;
+      const int nn = n - (s ? p.seg[0].n : 0);
+      wsrc[j] = reinterpret_cast<const bf16*>(p.seg[s].w) + (long long)nn * p.seg[s].w_ld + 8 * c;
+    }
+  };
+  const uint32_t lds0 = lds_addr_of(smem);
+  // issue position: stage gi of the flattened (tile, k-step) sequence, tile ii, k-step ik
+  int gi = 0, ii = 0, ik = 0;
+  auto issue_next = [&]() {
+    const uint32_t base = lds0 + (gi % KVP_NST) * KVP_STAGE;
+    const int k0 = ik * GBK;
+#pragma unroll
+    for (int j = 0; j < KVP_CPW; ++j)
+      dma16(asrc[j] + k0, __builtin_amdgcn_readfirstlane(base + (KVP_CPW * wave + j) * 1024));
+#pragma unroll
+    for (int j = 0; j < KVP_CPW; ++j)
+      dma16(wsrc[j] + k0, __builtin_amdgcn_readfirstlane(base + KVP_AB + (KVP_CPW * wave + j) * 1024));
+    ++gi;
+    if (++ik == nst) {
+      ik = 0;
+      if (++ii < ord.count) set_src(ii);
+    }
+  };
+
+  const int rd_base = col * 64 | ((((col >> 2) & 3) ^ half) << 4);   // as in gemm_big_kernel
+  f32x16 acc[4][4];
+
+  copies_begin();   // lds_dma.h, rule 1 (nothing compiler-visible is in flight)
+  set_src(0);
+  issue_next();
+  if (total > 1) issue_next();
+  // one k-step of stage gs; FIRST: the tile's first, whose products start from zero (the
+  // accumulators are not live across tiles, which keeps the allocator from moving them)
+  auto step = [&](int gs, auto first_c) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    if (gs + 1 < total) wait_vmcnt<KVP_DPW>();
+    else wait_vmcnt<0>();
+    barrier_only();
+    if (gi < total) issue_next();
+    const unsigned char* T = smem + (gs % KVP_NST) * KVP_STAGE;
+    const int rb0 = opaque_int(rd_base);
+    Frag<bf16> fa[2][4], fb[2][4];
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      const int off = rb0 ^ (ks << 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[ks][i] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + off + (128 * wm + 32 * i) * 64));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[ks][j] = frag_load<bf16>(reinterpret_cast<const bf16*>(T + KVP_AB + off + (128 * wn + 32 * j) * 64));
+    }
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma32(fa[ks][i], fb[ks][j], (FIRST && ks == 0) ? f32x16{} : acc[i][j]);
+    // the first k-step's 8 reads, then its 16 products with the second k-step's 8 reads
+    // slotted in after the first 8, then the second k-step's products
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+  };
+  int gs = 0;
+  for (int ti = 0; ti < ord.count; ++ti) {
+    step(gs++, std::true_type{});
+    for (int it = 1; it < nst; ++it) step(gs++, std::false_type{});
+
+    // ---- output stage of tile ti (flash layouts; see gemm_big_kernel's DIRECT stage) ----
+    // Each accumulator block moves to VGPRs at an explicit point (the empty asm with the memory
+    // clobber keeps the move after the previous block's stores): left to itself the compiler
+    // copies all 256 accumulators out at once and spills.
+    int by, bx;
+    ord.tile(ti, by, bx);
+    const int N0 = bx * KVP_T + 128 * wn;
+    if (N0 < N) {
+      const int s = N0 < p.seg[0].n ? 0 : 1;
+      const GemmSeg& sg = p.seg[s];
+      const int cc = N0 - (s ? p.seg[0].n : 0);
+      const int head = cc / sg.out_hw, j0 = cc - head * sg.out_hw;
+      bf16* out = reinterpret_cast<bf16*>(sg.out);
+      const bool vt = sg.layout == OUT_HEAD_T16;
+      unsigned char* buf = smem + KVP_TR + wave * KV_BUF;
+      const int g16 = lane >> 4, x16 = lane & 15;
+      auto chunk = [&](auto I, int m) {
+        constexpr int i = decltype(I)::value;
+        const int b = m / p.rows_per_batch, t = m - b * p.rows_per_batch;
+        if (vt) {
+          // Values: the chunk's [128 features][32 tokens] block goes through the wave's LDS
+          // buffer (rows of 64 bytes, 16-byte pieces XOR-swizzled by (row >> 1) & 3: both the
+          // writes and the reads below are free of bank conflicts), so that 4 lanes store one
+          // feature row's 64 bytes together; 16-byte pieces scattered over 32 rows straight
+          // from the accumulators cost the kernel a quarter of its time.  Piece 2 g + half of a
+          // row is perm16 positions 8 half .. 8 half + 7 of token group g, i.e. accumulator
+          // elements 8 g .. 8 g + 7.
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            asm volatile("" : "+v"(acc[i][j])::"memory");
+            const int row = 32 * j + col;
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              bf16x8 o;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] = (bf16)acc[i][j][8 * g + e];
+              *reinterpret_cast<bf16x8*>(buf + row * 64 + (((2 * g + half) ^ ((row >> 1) & 3)) << 4)) = o;
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+          __builtin_amdgcn_wave_barrier();
+          bf16* base = out + ((long long)(b * sg.out_nh + head) * sg.out_hw + j0) * sg.out_ld + t + 8 * (lane & 3);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int row = 16 * k + (lane >> 2);
+            const s16x8 v = *reinterpret_cast<const s16x8*>(buf + row * 64 + (((lane & 3) ^ ((row >> 1) & 3)) << 4));
+            *reinterpret_cast<s16x8*>(base + (long long)row * sg.out_ld) = v;
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // the reads are done before the next chunk's writes
+          __builtin_amdgcn_wave_barrier();
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            asm volatile("" : "+v"(acc[i][j])::"memory");
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              bf16x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[i][j][4 * q + e];
+              *reinterpret_cast<bf16x4*>(buf + (32 * j + col) * KV_CS + (8 * q + 4 * half) * 2) = o;
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+          __builtin_amdgcn_wave_barrier();
+          bf16* base = out + ((long long)(b * sg.out_nh + head) * p.rows_per_batch + t) * sg.out_hw + j0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int r0 = 16 * (u & 1), c0 = 32 * (u >> 1) + 8 * g16;
+            const unsigned char* rd = buf + (c0 + (x16 >> 2)) * KV_CS + (r0 + 4 * (x16 & 3)) * 2;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(rd));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(rd + 4 * KV_CS));
+            const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<s16x8*>(base + (r0 + x16) * sg.out_hw + c0) = v;
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // the reads are done before the next chunk's writes
+          __builtin_amdgcn_wave_barrier();
+        }
+      };
+      const int mw = by * KVP_T + 128 * wm;
+      if (mw < p.M) chunk(std::integral_constant<int, 0>{}, mw);
+      if (mw + 32 < p.M) chunk(std::integral_constant<int, 1>{}, mw + 32);
+      if (mw + 64 < p.M) chunk(std::integral_constant<int, 2>{}, mw + 64);
+      if (mw + 96 < p.M) chunk(std::integral_constant<int, 3>{}, mw + 96);
+    }
+  }
+  copies_end();   // lds_dma.h, rule 3
+}
+
 }  // namespace
 
 bool gemm_big_supported(const GemmParams& p, int groups) {
@@ -343,6 +593,13 @@ hipError_t launch_gemm_big(const GemmParams& pin, int groups, hipStream_t s) {
   // The flash-layout stage (the prefill K/V up-projection) takes 256 x 128 tiles, two
   // workgroups per CU (820 -> 780 us at B=4, S=4096); the other projections measured the
   // same or slower that way and keep 256 x 256.
+  if (p.fast_epilogue == 2 && groups == 1 && N % KVP_T == 0) {
+    // persistent form: one workgroup per CU (or per tile when there are fewer tiles)
+    const int mt = cdiv(p.M, KVP_T), nt = N / KVP_T;
+    const int G = min(mt * nt, device_cu_count());
+    hipLaunchKernelGGL(gemm_kv_kernel, dim3(G), dim3(256), KVP_LDS, s, p, mt, nt);
+    return hipGetLastError();
+  }
   if (p.fast_epilogue == 2) {
     using C = BigCfg<4>;
     dim3 grid(cdiv(N, C::BN), cdiv(p.M, GBM), groups);

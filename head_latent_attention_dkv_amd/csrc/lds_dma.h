@@ -28,6 +28,13 @@ namespace mla {
 //      vector-memory operation after the loop (partial-result stores, the epilogue).
 // A kernel that once issued later tiles' copies behind its query loads, against rule 1,
 // read wrong tiles although the bytes in HBM were right.
+//
+// Stores are the one exception a kernel may take to rules 2 and 3 (the persistent K/V
+// up-projection stores a tile while the next tile's copies are in flight): copies complete
+// in issue order among themselves, so while an awaited copy is outstanding every later copy
+// is too, and the count stays above N whatever the stores do; an outstanding store only
+// holds the count above N longer.  The compiler emits no wait of its own for a store.  Loads
+// into VGPRs stay excluded: the compiler's waits for them would be wrong.
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
