@@ -246,7 +246,7 @@ __device__ __forceinline__ void rope_sincos(int pos, float inv_freq_hi, float in
                                             float* s, float* c) {
   double a = (double)pos * ((double)inv_freq_hi + (double)inv_freq_lo);
   const double two_pi = 6.283185307179586476925286766559;
-  a = a - two_pi * rint(a / two_pi);
+  a = a - two_pi * rint(a * (1.0 / two_pi));   // a multiply: a double division is ~10x the work
   sincosf((float)a, s, c);
 }
 

@@ -296,7 +296,13 @@ __global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_k
     __syncthreads();
   }
   if (p.splits == 1) {
-    epilogue_block<bf16>(p, Cs, C::LDC, 0, C::XROWS, n0, C::ROWS, g.o, tid, 256);
+    if (p.fast_epilogue) {
+      // vectorised stage: each wave a quarter of the rows, 8 columns per lane
+      constexpr int RW = C::XROWS / 4;
+      epilogue_block_fast<bf16>(p, Cs + wave * RW * C::LDC, C::LDC, wave * RW, RW, n0, C::ROWS, g.o, lane);
+    } else {
+      epilogue_block<bf16>(p, Cs, C::LDC, 0, C::XROWS, n0, C::ROWS, g.o, tid, 256);
+    }
     return;
   }
   float* part = p.part + ((long long)z * p.splits + split) * p.M * N;
@@ -495,8 +501,17 @@ bool skinny_supported(const GemmParams& p, int groups) {
   return true;
 }
 
+// The vectorised output stage (8 columns per lane, one sine / cosine per rotary pair) when the
+// segments allow it; transposed segments keep the generic stage (they need 32-row chunks).
+bool skinny_fast_epilogue(const GemmParams& p, int groups) {
+  for (int i = 0; i < p.nseg; ++i)
+    if (p.seg[i].layout == OUT_HEAD_T16) return false;
+  return gemm_fast_epilogue_ok(p, groups);
+}
+
 hipError_t launch_skinny(GemmParams p, int groups, hipStream_t s) {
   const int N = seg_total(p);
+  p.fast_epilogue = skinny_fast_epilogue(p, groups) ? 1 : 0;
   SkinnyPlan pl = plan(p.M, N, p.K, groups, min_stream_rows(p));
   const size_t need = pl.splits > 1 ? (size_t)pl.splits * groups * p.M * N * sizeof(float) : 0;
   if (pl.splits > 1 && (p.part == nullptr || p.part_bytes < need)) {

@@ -64,6 +64,30 @@ def test_decode_full(gu, name, sample):
         gu.assert_close(y[b], O.decode(seq, lay.prob.weights, d), cfg.dtype, f"y b={b} ctx={ctx[b]}")
 
 
+@pytest.mark.parametrize("B,sample", [(20, None), (40, [0, 1, 19, 31, 32, 33, 38, 39])])
+def test_decode_full_dims_short_contexts(gu, B, sample):
+    """The DeepSeek-V2 decode dimensions (d_model 5120, 128 heads, r_q 1536) with 20 and 40
+    sequences of short ragged contexts: the few-row projections with one (20 rows) and two
+    (40 rows, the second block ragged) 32-row activation blocks, the vectorised output stage
+    (rotary pairs, cache rows); every sampled sequence's output and appended cache row
+    against the oracle."""
+    cfg = S.CONFIGS["dsv2_decode"].replace(name=f"dsv2_decode_b{B}", batch=B, ctx_lo=16, ctx_hi=64)
+    sample = list(range(B)) if sample is None else sample
+    gu.say(f"[decode-full-dims] {cfg.name} B={B} sample={len(sample)} sequences")
+    lay = gu.Layer(cfg)
+    ctx = [int(c) for c in lay.prob.ctx_lens]
+    ckv, kr = lay.new_cache(B, max(ctx) + 8, fill=3.0)
+    last = _fill_with_last(gu, lay, ckv, kr, ctx)
+    y = gu.to_host(lay.decode(gu.to_dev(last, cfg), ctx, lay.cache_view(ckv, kr, 0, B)))
+    assert np.all(np.isfinite(y))
+    d = O.Dims.from_cfg(cfg)
+    for b in sample:
+        seq = S.make_x(cfg, b, ctx[b] + 1)
+        c, _ = O.latent_rows(seq[-1:], lay.prob.weights, d, np.array([ctx[b]]))
+        gu.assert_close(gu.to_host(ckv[b, ctx[b]]), c[0], cfg.dtype, f"appended row b={b}")
+        gu.assert_close(y[b], O.decode(seq, lay.prob.weights, d), cfg.dtype, f"y b={b} ctx={ctx[b]}")
+
+
 def test_decode_latent_head_full(gu):
     """One MLRA latent head on its own (rank 128, its 4 query heads) over the full MLRA
     contexts: the token-split decode kernel with 4096-token splits, four partial rows each."""
