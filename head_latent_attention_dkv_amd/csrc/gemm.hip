@@ -178,6 +178,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   }
 
   // ---- epilogue through LDS: rotary pairs may sit in other lanes / waves ----
+  __shared__ float rtab[kRopeTabFloats];
+  if (gemm_has_rope(p)) stage_rope_table(p, rtab, tid, 256);
   float* Cs = reinterpret_cast<float*>(smem_raw);
   constexpr int LDC = TL::LDC;
 #pragma unroll
@@ -192,7 +194,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
       }
   __syncthreads();
 
-  epilogue_block<T>(p, Cs, LDC, m0, BM, n0, BN, o_goff, tid, 256);
+  epilogue_block<T>(p, Cs, LDC, m0, BM, n0, BN, o_goff, tid, 256, rtab);
 }
 
 template <typename T, int BM, int BN>

@@ -180,6 +180,17 @@ __global__ void __launch_bounds__(64 * NW, BigCfg<NW>::MINB) gemm_big_kernel(Gem
     __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
   }
   copies_end();   // lds_dma.h, rule 3
+  // The output stage reads the parameters from a copy in LDS: it indexes the segments and the
+  // inverse-frequency table per lane, which on the kernel arguments would be vector loads,
+  // one memory round trip each (and picking the fields by selects keeps too many registers).
+  __shared__ GemmParams sp;
+  if constexpr (!DIRECT) {
+    static_assert(sizeof(GemmParams) % 4 == 0, "parameter copy in 4-byte words");
+    const int* src = reinterpret_cast<const int*>(&p);
+    int* dst = reinterpret_cast<int*>(&sp);
+    for (int i = threadIdx.x; i < (int)(sizeof(GemmParams) / 4); i += 64 * NW) dst[i] = src[i];
+  }
+  const float* rtab = sp.rope.hi;   // hi[], then lo[] (RopeTable)
   __syncthreads();
 
   if constexpr (DIRECT) {
@@ -269,9 +280,10 @@ __global__ void __launch_bounds__(64 * NW, BigCfg<NW>::MINB) gemm_big_kernel(Gem
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
     if (p.fast_epilogue)
-      epilogue_block_fast<bf16>(p, Cs, G_LDC, m0 + 64 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane);
+      epilogue_block_fast<bf16, 32, 1, 1, true>(sp, Cs, G_LDC, 0, m0 + 64 * wm + 32 * i, n0 + 128 * wn, 128, o_goff,
+                                                lane, rtab);
     else
-      epilogue_block<bf16>(p, Cs, G_LDC, m0 + 64 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane, 64);
+      epilogue_block<bf16, true>(sp, Cs, G_LDC, m0 + 64 * wm + 32 * i, 32, n0 + 128 * wn, 128, o_goff, lane, 64, rtab);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
   }

@@ -13,12 +13,28 @@
 
 namespace mla {
 
+// Segment s of p for a lane-dependent s: picked from the kernel arguments (seg_out), or
+// read straight from p when p is a copy in LDS (fewer registers live: the fields are loaded
+// where they are used).
+template <bool PLDS>
+__device__ __forceinline__ decltype(auto) seg_view(const GemmParams& p, int s) {
+  if constexpr (PLDS) {
+    return (p.seg[s]);   // a reference into the LDS copy
+  } else {
+    return seg_out(p, s);
+  }
+}
+
 // Cs[r * ldc + c] holds out[m0 + r][n0 + c] for r < rows, c < cols.  All threads of the
-// block take part (stride `nthreads`); the caller synchronises before and after.
-template <typename T>
+// block take part (stride `nthreads`); the caller synchronises before and after.  rtab: the
+// inverse-frequency table staged in LDS by stage_rope_table (read only for rotated segments).
+//
+// PLDS: p is a copy of the parameters in LDS, whose segments are indexed per lane directly;
+// otherwise p is the kernel argument block and seg_out picks the fields.
+template <typename T, bool PLDS = false>
 __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float* Cs, int ldc, int m0,
                                                int rows, int n0, int cols, long long o_goff,
-                                               int tid, int nthreads) {
+                                               int tid, int nthreads, const float* rtab) {
   const int N = seg_total(p);
   bool any_t = false;
   for (int i = 0; i < p.nseg; ++i) any_t = any_t || p.seg[i].layout == OUT_HEAD_T16;
@@ -38,7 +54,7 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
       if (m >= p.M || n >= N) continue;
       int nn;
       const int s = seg_of(p, n, &nn);
-      const GemmSeg& sg = p.seg[s];
+      const auto& sg = seg_view<PLDS>(p, s);
       if ((sg.layout == OUT_HEAD_T16) != (pass == 1)) continue;
       float v = Cs[r * ldc + c];
       const int b = m / p.rows_per_batch;
@@ -49,7 +65,7 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
         float sn, cs;
         if (sg.rope == ROPE_INTERLEAVED) {
           const int j = hh >> 1;
-          rope_sincos(pos, p.rope.hi[j], p.rope.lo[j], &sn, &cs);
+          rope_sincos(pos, rtab[j], rtab[kMaxRopePairs + j], &sn, &cs);
           if ((hh & 1) == 0) {
             const float o = Cs[r * ldc + c + 1];
             v = v * cs - o * sn;
@@ -60,7 +76,7 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
         } else {
           const int half = sg.rope_d >> 1;
           const int j = hh % half;
-          rope_sincos(pos, p.rope.hi[j], p.rope.lo[j], &sn, &cs);
+          rope_sincos(pos, rtab[j], rtab[kMaxRopePairs + j], &sn, &cs);
           if (hh < half) {
             const float o = Cs[r * ldc + c + half];
             v = v * cs - o * sn;
@@ -102,61 +118,105 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
 
 namespace mla {
 
-// Vectorised form of epilogue_block for one wave and a block of `rows` (a multiple of 4;
-// a multiple of 32 starting at a multiple of 32 inside one batch entry when a segment is
+// Vectorised form of epilogue_block for one wave and a block of ROWS (a multiple of 4; a
+// multiple of 32 starting at a multiple of 32 inside one batch entry when a segment is
 // transposed) x `cols` (a multiple of 8) values: lane l takes the 8-column runs l % 16
-// (+16 ...) and rows l / 16 (+4 ...) and stores 8 outputs at once; transposed segments are
-// written 16 bytes per lane along the token axis.
-// Requires gemm_fast_epilogue_ok() on the host.
-template <typename T>
-__device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const float* Cs, int ldc, int m0,
-                                                    int rows, int n0, int cols, long long o_goff, int lane) {
+// (+16 ...) and rows l / 16 + 4 i, and stores 8 outputs at once; transposed segments are
+// written 16 bytes per lane along the token axis.  The value at (r, c) is the sum of NPART
+// blocks part_stride floats apart, added in block order.
+//
+// The rows of a lane are independent, so each phase (operand reads, rotation, stores) runs
+// over all of them at once: with one wave per SIMD nothing else hides a row's dependent
+// chain (reads, 64-bit index arithmetic, conversion), and row after row the stage had cost
+// about a thousand cycles per row.
+// Requires gemm_fast_epilogue_ok() on the host.  rtab as in epilogue_block.
+template <typename T, int ROWS, int NPART = 1, int RGMAX = 4, bool PLDS = false>
+__device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const float* Cs, int ldc, int part_stride,
+                                                    int m0, int n0, int cols, long long o_goff, int lane,
+                                                    const float* rtab) {
+  static_assert(ROWS % 4 == 0, "rows per lane");
+  constexpr int RL = ROWS / 4;                         // rows per lane
+  constexpr int RG = RL < RGMAX ? RL : RGMAX;          // rows per lane taken together
   const int N = seg_total(p);
+  auto cs_sum8 = [&](const float* src, float* v) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = src[e];
+#pragma unroll
+    for (int w = 1; w < NPART; ++w)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += src[w * part_stride + e];
+  };
   for (int cr = lane & 15; cr < cols / 8; cr += 16) {
     const int n = n0 + 8 * cr;
     if (n >= N) continue;
     int nn;
     const int s = seg_of(p, n, &nn);
-    const GemmSeg& sg = p.seg[s];
+    const auto& sg = seg_view<PLDS>(p, s);
     if (sg.layout == OUT_HEAD_T16) continue;
     const long long cc = nn + o_goff;
     const int hw = sg.out_hw;
-    const long long head = hw ? cc / hw : 0, j0 = hw ? cc - head * hw : cc;
+    long long head = 0, j0 = cc;
+    if (hw) {
+      // 32-bit division whenever the column fits (it always does for the library's shapes)
+      if ((cc >> 31) == 0) {
+        head = (long long)((unsigned)cc / (unsigned)hw);
+      } else {
+        head = cc / hw;
+      }
+      j0 = cc - head * hw;
+    }
     const int hh = sg.rope != ROPE_OFF ? nn % sg.rope_d : 0;
     const int half = sg.rope_d >> 1;
-    for (int r = lane >> 4; r < rows; r += 4) {
-      const int m = m0 + r;
-      if (m >= p.M) break;
-      const int b = m / p.rows_per_batch;
-      const int t = m - b * p.rows_per_batch;
-      const float* src = Cs + r * ldc + 8 * cr;
-      float v[8];
+    const bool lo = hh < half;
+    // rows in groups of RG (the registers of more rows at once spilled in the larger blocks)
+#pragma nounroll
+    for (int g0 = 0; g0 < RL; g0 += RG) {
+    float v[RG][8];
+    int mrow[RG], brow[RG], trow[RG];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = src[e];
-      if (sg.rope == ROPE_INTERLEAVED) {
-        const int pos = (p.pos0 ? p.pos0[b] : 0) + t;
+    for (int i = 0; i < RG; ++i) {
+      const int r = (lane >> 4) + 4 * (g0 + i);
+      mrow[i] = m0 + r;
+      brow[i] = mrow[i] / p.rows_per_batch;
+      trow[i] = mrow[i] - brow[i] * p.rows_per_batch;
+      cs_sum8(Cs + r * ldc + 8 * cr, v[i]);
+    }
+    if (sg.rope == ROPE_INTERLEAVED) {
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        if (mrow[i] >= p.M) continue;
+        const int pos = (p.pos0 ? p.pos0[brow[i]] : 0) + trow[i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float sn, cs;
           const int jj = (hh >> 1) + q;
-          rope_sincos(pos, p.rope.hi[jj], p.rope.lo[jj], &sn, &cs);
-          const float x0 = v[2 * q], x1 = v[2 * q + 1];
-          v[2 * q] = x0 * cs - x1 * sn;
-          v[2 * q + 1] = x0 * sn + x1 * cs;
+          rope_sincos(pos, rtab[jj], rtab[kMaxRopePairs + jj], &sn, &cs);
+          const float x0 = v[i][2 * q], x1 = v[i][2 * q + 1];
+          v[i][2 * q] = x0 * cs - x1 * sn;
+          v[i][2 * q + 1] = x0 * sn + x1 * cs;
         }
-      } else if (sg.rope == ROPE_HALFSPLIT) {
-        const int pos = (p.pos0 ? p.pos0[b] : 0) + t;
-        const bool lo = hh < half;
-        const float* ps = src + (lo ? half : -half);
+      }
+    } else if (sg.rope == ROPE_HALFSPLIT) {
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        if (mrow[i] >= p.M) continue;
+        const int r = (lane >> 4) + 4 * (g0 + i);
+        const int pos = (p.pos0 ? p.pos0[brow[i]] : 0) + trow[i];
+        float o[8];
+        cs_sum8(Cs + r * ldc + 8 * cr + (lo ? half : -half), o);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float sn, cs;
           const int jj = (hh + e) % half;
-          rope_sincos(pos, p.rope.hi[jj], p.rope.lo[jj], &sn, &cs);
-          const float o = ps[e];
-          v[e] = lo ? v[e] * cs - o * sn : o * sn + v[e] * cs;
+          rope_sincos(pos, rtab[jj], rtab[kMaxRopePairs + jj], &sn, &cs);
+          v[i][e] = lo ? v[i][e] * cs - o[e] * sn : o[e] * sn + v[i][e] * cs;
         }
       }
+    }
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const int m = mrow[i], b = brow[i], t = trow[i];
+      if (m >= p.M) continue;
       long long idx;
       if (sg.layout == OUT_ROWS) {
         const long long oc = hw ? head * sg.out_hs + j0 : cc;
@@ -172,21 +232,28 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
       }
       if (sg.out_f32) {
         float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(sg.out) + idx);
-        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+        dst[0] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+        dst[1] = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
       } else {
         bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)v[i][e];
         *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sg.out) + idx) = o;
       }
+    }
     }
   }
   // transposed segments: 8 consecutive output positions (16 bytes) per lane, 4 lanes per
   // 32-position row segment, so one store instruction fills 16 whole 64-byte segments.
   // Positions 8 u .. 8 u + 7 of a 16-group hold tokens 4 u' .. 4 u' + 3 and 8 + 4 u' ..
   // 8 + 4 u' + 3 (u' = u % 2) of the same group (perm16).
-  for (int base = 0; base < rows; base += 32) {
+  auto cs_at = [&](int r, int c) {
+    float x = Cs[r * ldc + c];
+#pragma unroll
+    for (int w = 1; w < NPART; ++w) x += Cs[w * part_stride + r * ldc + c];
+    return x;
+  };
+  for (int base = 0; base < ROWS; base += 32) {
     const int m = m0 + base;
     if (m >= p.M) break;
     const int b = m / p.rows_per_batch;
@@ -199,7 +266,7 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
       if (n >= N) continue;
       int nn;
       const int s = seg_of(p, n, &nn);
-      const GemmSeg& sg = p.seg[s];
+      const auto& sg = seg_view<PLDS>(p, s);
       if (sg.layout != OUT_HEAD_T16) continue;
       const long long cc = nn + o_goff;
       const long long head = cc / sg.out_hw, j = cc - head * sg.out_hw;
@@ -207,8 +274,8 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[e] = (bf16)Cs[(ra + e) * ldc + c];
-        o[4 + e] = (bf16)Cs[(ra + 8 + e) * ldc + c];
+        o[e] = (bf16)cs_at(ra + e, c);
+        o[4 + e] = (bf16)cs_at(ra + 8 + e, c);
       }
       *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sg.out) + idx) = o;
     }

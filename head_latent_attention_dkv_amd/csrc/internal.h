@@ -93,6 +93,52 @@ __host__ __device__ inline int seg_of(const GemmParams& p, int n, int* nn) {
   return s;
 }
 
+// Output fields of segment s when s differs between the lanes of a wave.  Every field is
+// read at a constant index (a scalar load of the kernel arguments) and picked per lane:
+// indexing p.seg with a lane-dependent s makes the compiler read the argument block with
+// vector loads, one memory round trip per field, one behind the other (a projection's
+// output stage waited several microseconds on such chains).
+struct SegOut {
+  void* out;
+  long long out_ld;
+  int out_f32, out_hw, out_hs, out_cache, rope, rope_d, layout, out_nh;
+};
+
+__device__ __forceinline__ SegOut seg_out(const GemmParams& p, int s) {
+  SegOut r;
+#define MLA_SEG_PICK(f) (s == 0 ? p.seg[0].f : s == 1 ? p.seg[1].f : p.seg[2].f)
+  r.out = MLA_SEG_PICK(out);
+  r.out_ld = MLA_SEG_PICK(out_ld);
+  r.out_f32 = MLA_SEG_PICK(out_f32);
+  r.out_hw = MLA_SEG_PICK(out_hw);
+  r.out_hs = MLA_SEG_PICK(out_hs);
+  r.out_cache = MLA_SEG_PICK(out_cache);
+  r.rope = MLA_SEG_PICK(rope);
+  r.rope_d = MLA_SEG_PICK(rope_d);
+  r.layout = MLA_SEG_PICK(layout);
+  r.out_nh = MLA_SEG_PICK(out_nh);
+#undef MLA_SEG_PICK
+  return r;
+}
+
+// The inverse-frequency table in LDS (hi[0..kMaxRopePairs), then lo[...]) for output stages
+// that look entries up per lane: on the kernel arguments each lookup would be a vector load.
+constexpr int kRopeTabFloats = 2 * kMaxRopePairs;
+
+__device__ __forceinline__ bool gemm_has_rope(const GemmParams& p) {
+  return p.seg[0].rope != ROPE_OFF || (p.nseg > 1 && p.seg[1].rope != ROPE_OFF) ||
+         (p.nseg > 2 && p.seg[2].rope != ROPE_OFF);
+}
+
+// Threads tid, tid + nthreads, ... copy the table (one round of loads, in parallel); the
+// caller synchronises before the first lookup.
+__device__ __forceinline__ void stage_rope_table(const GemmParams& p, float* tab, int tid, int nthreads) {
+  for (int j = tid; j < kMaxRopePairs; j += nthreads) {
+    tab[j] = p.rope.hi[j];
+    tab[kMaxRopePairs + j] = p.rope.lo[j];
+  }
+}
+
 hipError_t launch_gemm(const GemmParams& p, int groups, bool use_bf16, hipStream_t s);
 
 // Few-row (M <= 128) weight-streaming path used by launch_gemm when its layout allows.

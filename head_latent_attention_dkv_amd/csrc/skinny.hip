@@ -44,6 +44,7 @@ __device__ __forceinline__ long long a_row(const GemmParams& p, int m) {
 template <int CB, int U>
 __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
   __shared__ float Cs[32 * CB * kLdc];
+  __shared__ float rtab[kRopeTabFloats];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform k schedule
@@ -132,6 +133,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
     mma(0);
   }
 
+  if (p.splits == 1 && gemm_has_rope(p)) stage_rope_table(p, rtab, tid, 256);
   // Sum the four waves' partial products in wave order.  Accumulator element e of lane l
   // is out[32 cb + l%32][32 rb + 8 (e/4) + 4 (l/32) + e%4].
   for (int w = 0; w < 4; ++w) {
@@ -150,7 +152,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
   }
 
   if (p.splits == 1) {
-    epilogue_block<bf16>(p, Cs, kLdc, 0, 32 * CB, n0, kCols, g.o, tid, 256);
+    epilogue_block<bf16>(p, Cs, kLdc, 0, 32 * CB, n0, kCols, g.o, tid, 256, rtab);
     return;
   }
   float* part = p.part + ((long long)z * p.splits + split) * p.M * N;
@@ -170,7 +172,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmParams p) {
 // stage; the waves' partial sums meet in LDS as in the direct kernel.
 template <int CB, int ROWS_, int KT, int NST>
 struct StreamCfg {
-  static constexpr int ROWS = ROWS_;               // weight rows per block (32, 64 or 128)
+  static constexpr int ROWS = ROWS_;               // weight rows per block (32, 64, 96 or 128)
   static constexpr int RB = ROWS / 32;
   static constexpr int XROWS = 32 * CB;            // activation rows per block
   static constexpr int CHUNKS = KT / 8;            // 16-byte chunks per row segment
@@ -182,8 +184,8 @@ struct StreamCfg {
   static constexpr int WBYTES = ROWS * KT * 2;
   static constexpr int STAGE = (ROWS + XROWS) * KT * 2;
   static constexpr int LDC = ROWS + 4;
-  static constexpr size_t LDS = (size_t)NST * STAGE > (size_t)XROWS * LDC * 4
-                                    ? (size_t)NST * STAGE : (size_t)XROWS * LDC * 4;
+  static constexpr size_t PART = (size_t)XROWS * LDC;   // floats of one wave's partial block
+  static constexpr size_t LDS = (size_t)NST * STAGE > 4 * PART * 4 ? (size_t)NST * STAGE : 4 * PART * 4;
   static_assert(KT == 64 || KT == 128, "stage width");
   static_assert(XPW >= 1 && WPW >= 1 && NST >= 2 && NST <= 4, "pipeline shape");
 };
@@ -277,39 +279,68 @@ __global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_k
     }
   }
   copies_end();   // lds_dma.h, rule 3
+  // the inverse-frequency table sits behind the stages and partial buffers
+  float* rtab = reinterpret_cast<float*>(smem + C::LDS);
+  if (p.splits == 1 && gemm_has_rope(p)) stage_rope_table(p, rtab, tid, 256);
   __syncthreads();
 
-  // Sum the four waves' partial products in wave order (Cs aliases the stages).
+  // The four waves' partial products are summed in wave order.  Each wave stores its block
+  // to a buffer of its own (accumulator elements 4q..4q+3 of a lane are four consecutive
+  // columns: one 16-byte store); the readers then add buffers 0, 1, 2, 3 in that order.
+  // (Adding them wave after wave into one buffer -- a load, an add and a store per element,
+  // a barrier per wave -- had cost more than the whole K loop of a block.)
   float* Cs = reinterpret_cast<float*>(smem);
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+  {
+    float* Pw = Cs + wave * C::PART;
 #pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb)
+    for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float* dst = &Cs[(32 * cb + col) * C::LDC + 32 * rb + 8 * (e >> 2) + 4 * half + (e & 3)];
-            *dst = (w == 0) ? acc[rb][cb][e] : *dst + acc[rb][cb][e];
-          }
-    }
-    __syncthreads();
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(&Pw[(32 * cb + col) * C::LDC + 32 * rb + 8 * q + 4 * half]) =
+              (f32x4){acc[rb][cb][4 * q], acc[rb][cb][4 * q + 1], acc[rb][cb][4 * q + 2], acc[rb][cb][4 * q + 3]};
   }
-  if (p.splits == 1) {
-    if (p.fast_epilogue) {
-      // vectorised stage: each wave a quarter of the rows, 8 columns per lane
-      constexpr int RW = C::XROWS / 4;
-      epilogue_block_fast<bf16>(p, Cs + wave * RW * C::LDC, C::LDC, wave * RW, RW, n0, C::ROWS, g.o, lane);
-    } else {
-      epilogue_block<bf16>(p, Cs, C::LDC, 0, C::XROWS, n0, C::ROWS, g.o, tid, 256);
+  __syncthreads();
+  auto sum4 = [&](int r, int c) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(&Cs[r * C::LDC + c]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v = v + *reinterpret_cast<const f32x4*>(&Cs[w * C::PART + r * C::LDC + c]);
+    return v;
+  };
+  if (p.splits == 1 && p.fast_epilogue) {
+    // vectorised stage straight from the four buffers: each wave a quarter of the rows,
+    // 8 columns per lane
+    constexpr int RW = C::XROWS / 4;
+    epilogue_block_fast<bf16, RW, 4>(p, Cs + wave * RW * C::LDC, C::LDC, (int)C::PART, wave * RW, n0, C::ROWS,
+                                     g.o, lane, rtab);
+    return;
+  }
+  if (p.splits > 1) {
+    // split K: the block's sums go to the workspace in fp32, 16 bytes per store where the
+    // row allows it
+    float* part = p.part + ((long long)z * p.splits + split) * p.M * N;
+    for (int i = tid; i < C::XROWS * (C::ROWS / 4); i += 256) {
+      const int r = i / (C::ROWS / 4), c = 4 * (i - r * (C::ROWS / 4));
+      if (r >= p.M || n0 + c >= N) continue;
+      const f32x4 v = sum4(r, c);
+      float* dst = part + (long long)r * N + n0 + c;
+      if ((N & 3) == 0 && n0 + c + 4 <= N) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+        for (int e = 0; e < 4 && n0 + c + e < N; ++e) dst[e] = v[e];
+      }
     }
     return;
   }
-  float* part = p.part + ((long long)z * p.splits + split) * p.M * N;
-  for (int e = tid; e < C::XROWS * C::ROWS; e += 256) {
-    const int r = e / C::ROWS, c = e - r * C::ROWS;
-    if (r < p.M && n0 + c < N) part[(long long)r * N + n0 + c] = Cs[r * C::LDC + c];
+  // generic stage: the sums into buffer 0 first
+  for (int i = tid; i < C::XROWS * (C::ROWS / 4); i += 256) {
+    const int r = i / (C::ROWS / 4), c = 4 * (i - r * (C::ROWS / 4));
+    const f32x4 v = sum4(r, c);
+    *reinterpret_cast<f32x4*>(&Cs[r * C::LDC + c]) = v;
   }
+  __syncthreads();
+  epilogue_block<bf16>(p, Cs, C::LDC, 0, C::XROWS, n0, C::ROWS, g.o, tid, 256, rtab);
 }
 
 // Sum of the slabs' partial blocks (slab order) followed by the shared epilogue; a
@@ -318,7 +349,9 @@ constexpr int kRedRows = 4;
 
 __global__ void __launch_bounds__(256) split_reduce_kernel(GemmParams p) {
   __shared__ float Cs[kRedRows * kLdc];
+  __shared__ float rtab[kRopeTabFloats];
   const int tid = threadIdx.x;
+  if (gemm_has_rope(p)) stage_rope_table(p, rtab, tid, 256);
   const int n0 = blockIdx.x * kCols;
   const int m0 = blockIdx.y * kRedRows;
   const int z = blockIdx.z;
@@ -341,7 +374,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(GemmParams p) {
   }
   Cs[r * kLdc + c] = v;
   __syncthreads();
-  epilogue_block<bf16>(p, Cs, kLdc, m0, kRedRows, n0, kCols, g.o, tid, 256);
+  epilogue_block<bf16>(p, Cs, kLdc, m0, kRedRows, n0, kCols, g.o, tid, 256, rtab);
 }
 
 bool aligned16(const void* ptr, long long elem_off) {
@@ -401,6 +434,14 @@ SkinnyPlan plan_stream(int M, int N, int K, int groups, int min_rows = 32) {
   // on a CU, so the blocks land evenly on the compute units (64-row tiles leave half of
   // them with one block and half with two).
   const bool wide = (long long)cdiv(N, 32) * groups >= 512;
+  // Wide outputs whose 96-row tiles number between half a CU and one CU each take them, one
+  // block per CU: every CU then reads the activation rows once (with 32-row tiles, three
+  // blocks per CU read them three times).  The decode step's query up-projection (24576 x
+  // 1536) is 256 such tiles.
+  if (wide && min_rows <= 32 && M <= 64) {
+    const long long t96 = (long long)cdiv(N, 96) * groups;
+    if (t96 <= kCUs && 2 * t96 > kCUs) return SkinnyPlan{96, 1, K, false};
+  }
   for (int rows : {128, 64, 32}) {
     if (M > 64 && rows == 128) continue;                 // accumulator budget
     if (rows < min_rows) continue;
@@ -460,7 +501,7 @@ hipError_t launch_stream(const GemmParams& p, int groups, hipStream_t s) {
   using C = StreamCfg<CB, ROWS, kStreamKT, NST>;
   const int N = seg_total(p);
   dim3 grid(cdiv(N, ROWS), p.splits, groups);
-  hipLaunchKernelGGL((skinny_stream_kernel<CB, ROWS, kStreamKT, NST>), grid, dim3(256), C::LDS, s, p);
+  hipLaunchKernelGGL((skinny_stream_kernel<CB, ROWS, kStreamKT, NST>), grid, dim3(256), C::LDS + kRopeTabFloats * 4, s, p);
   return hipGetLastError();
 }
 
@@ -469,6 +510,7 @@ hipError_t launch_stream_rows(const GemmParams& p, const SkinnyPlan& pl, int gro
   if (pl.rows == 32) return launch_stream<CB, 32>(p, groups, s);
   if (pl.rows == 64) return launch_stream<CB, 64>(p, groups, s);
   if constexpr (CB <= 2) {
+    if (pl.rows == 96) return launch_stream<CB, 96, 4>(p, groups, s);
     if (pl.deep) return launch_stream<CB, 128, 4>(p, groups, s);
     return launch_stream<CB, 128>(p, groups, s);
   }
