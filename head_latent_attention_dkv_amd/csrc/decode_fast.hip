@@ -384,20 +384,24 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
     }
   };
 
-  // ---- Q^T (B operand): lane holds head col, k = 16 ks + 8 half + [0..7]; all loads land
-  // before the first tile copy is issued ----
+  // ---- the first tiles' copies, then Q^T (B operand: lane holds head col, k = 16 ks +
+  // 8 half + [0..7]) behind them, so that the query block and the pipeline's first tiles
+  // arrive together; one full drain before anything is used (lds_dma.h, rule 4) ----
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < ntiles) issue_tile(st, st);
   const int head_ld = head_ok ? head : 0;
   const bf16* qlp = reinterpret_cast<const bf16*>(p.q_lat) + ((long long)b * p.H + head_ld) * p.q_lat_hs + 8 * half;
   const bf16* qrp = reinterpret_cast<const bf16*>(p.q_rope) + ((long long)b * p.H + head_ld) * p.q_rope_hs + 8 * half;
   Frag<bf16> qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_load<bf16>(ks < KSL ? qlp + 16 * ks : qrp + 16 * (ks - KSL));
+  drain_all();   // lds_dma.h, rule 4
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (!head_ok) qf[ks] = frag_zero<bf16>();
     asm volatile("" ::"v"(qf[ks].v));
   }
-  copies_begin();   // lds_dma.h, rule 1
 
   // ---- per-lane LDS byte offsets inside a stage.  The XOR swizzle only touches the low 4
   // bits of a chunk index, so for a step index n = 8 j + r (scores) or 4 j + r (values) the
@@ -535,9 +539,11 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
 
   auto pass = [&](auto mode_c) {
     constexpr int MODE = decltype(mode_c)::value;
+    if constexpr (MODE != 0) {   // (the main pass's first tiles went out with the query loads)
 #pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st)
-      if (st < ntiles) issue_tile(st, st);
+      for (int st = 0; st < NSTAGE - 1; ++st)
+        if (st < ntiles) issue_tile(st, st);
+    }
     for (int it = 0; it < ntiles; ++it) {
       // wait until only the newest tile is outstanding: two tiles in flight per CU while a
       // tile computes (a third in flight measured slower: more concurrent DRAM streams)
@@ -575,25 +581,39 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
 
   auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(c[0]) + __uint_as_float(c[1]);
-  if (!head_ok) return;
   const long long pidx = ((long long)b * p.H + head) * p.nsplit + split;
-  if (half == 0) {
+  if (head_ok && half == 0) {
     p.part_ml[pidx * 2 + 0] = m_ref;
     p.part_ml[pidx * 2 + 1] = l_tot;
   }
   // The split's result is stored normalised (z / l, bf16, like the output z itself); the
   // combine weights it by l 2^(m - M) in fp32.  l >= 1: the reference maximum is a score of
   // this split, whose p is 1.
-  // accumulator element e of lane l in block mb: latent column 32 mb + 8 (e/4) + 4 (l/32) + e%4
+  // Accumulator element e of lane l in block mb is latent column 32 mb + 8 (e/4) + 4 (l/32)
+  // + e%4 of head col: each wave first writes its 32 rows to LDS (row stride 1040 B), then
+  // stores one whole 1 KB row per instruction (written straight from the accumulators, a
+  // store instruction touched 32 rows 16 bytes each).
+  __syncthreads();   // every wave is done with the stages
+  unsigned char* rows = smem_raw + wave * 32 * 1040;
   const float inv_l = 1.f / l_tot;
-  bf16* pz = reinterpret_cast<bf16*>(p.part_z) + pidx * VL + 4 * half;
 #pragma unroll
   for (int mb = 0; mb < MBS; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<bf16x4*>(pz + 32 * mb + 8 * q) =
+      *reinterpret_cast<bf16x4*>(rows + col * 1040 + (32 * mb + 8 * q + 4 * half) * 2) =
           (bf16x4){(bf16)(acc[mb][4 * q + 0] * inv_l), (bf16)(acc[mb][4 * q + 1] * inv_l),
                    (bf16)(acc[mb][4 * q + 2] * inv_l), (bf16)(acc[mb][4 * q + 3] * inv_l)};
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const int head0 = hg * 128 + 32 * wave;   // the wave's first head
+  bf16* pz0 = reinterpret_cast<bf16*>(p.part_z) + (((long long)b * p.H + head0) * p.nsplit + split) * VL + 8 * lane;
+  const long long hstride = (long long)p.nsplit * VL;
+#pragma unroll
+  for (int h = 0; h < 32; ++h) {
+    if (head0 + h >= p.hpb) break;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(rows + h * 1040 + 16 * lane);
+    *reinterpret_cast<bf16x8*>(pz0 + h * hstride) = v;
+  }
 }
 
 }  // namespace

@@ -26,8 +26,13 @@ namespace mla {
 //      body reads LDS only);
 //   3. calls copies_end() -- which drains the copies -- before the first compiler-visible
 //      vector-memory operation after the loop (partial-result stores, the epilogue).
-// A kernel that once issued later tiles' copies behind its query loads, against rule 1,
-// read wrong tiles although the bytes in HBM were right.
+//   4. may instead issue its first copies, then its own loads, and drain everything
+//      (drain_all()) before it uses any loaded value or copied tile: with nothing outstanding
+//      after the drain, the count is exact again for the copy loop that follows.  The loads'
+//      latency then overlaps the first copies'.
+// A kernel that once issued later tiles' copies behind its query loads and waited for them
+// with partial counts, against rules 1 and 4, read wrong tiles although the bytes in HBM
+// were right.
 //
 // Stores are the one exception a kernel may take to rules 2 and 3 (the persistent K/V
 // up-projection stores a tile while the next tile's copies are in flight): copies complete
@@ -46,6 +51,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void copies_begin() { wait_vmcnt<0>(); }
 // Closes a copy phase (rule 3): every copy has landed in LDS.
 __device__ __forceinline__ void copies_end() { wait_vmcnt<0>(); }
+// Rule 4: every vector-memory operation of the wave, copy or load, has completed.
+__device__ __forceinline__ void drain_all() { wait_vmcnt<0>(); }
 // Workgroup barrier without the compiler's implicit wait for all outstanding memory.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
