@@ -346,8 +346,17 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
   const int col = lane & 31, half = lane >> 5;
   const int i16 = lane & 15, g16 = lane >> 4;
 
-  const int hg = blockIdx.x % p.head_tiles;
-  const int pair = blockIdx.x / p.head_tiles;
+  // Workgroups are dealt to the 8 XCDs round robin (XCD = index % 8).  When the grid is a
+  // multiple of 8 whose per-XCD share holds whole sequences, XCD x takes the x-th contiguous
+  // range of (sequence, split) work items, so the splits of a sequence share one L2 for
+  // their query block.
+  int wi = blockIdx.x;
+  {
+    const int G = gridDim.x, per = G >> 3;
+    if ((G & 7) == 0 && per % (p.nsplit * p.head_tiles) == 0) wi = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  const int hg = wi % p.head_tiles;
+  const int pair = wi / p.head_tiles;
   const int b = pair / p.nsplit;
   const int split = pair - b * p.nsplit;
   const int n_tok = decode_tokens(p, b);
