@@ -129,25 +129,34 @@ def timed(torch, fn, steps, warmup, stats=None):
     """Average ms per call of fn(i) over `steps` calls after `warmup` calls.
 
     HIP events on the current stream (the stream the library launches on) bracket the
-    timed calls, with a device synchronisation on both sides; an event between calls gives
-    each call's duration, whose median / p10 / p90 go into `stats` when it is a dict.
+    timed calls, with a device synchronisation on both sides; nothing else is enqueued
+    between the calls (an event record between calls adds a few microseconds of its own).
+    When `stats` is a dict, a second loop of `steps` calls with an event after each call
+    gives the per-call median / p10 / p90 that go into it.
     """
     if steps <= 0:
         return float("nan")
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(steps):
         fn(warmup + i)
-        ev[i + 1].record()
+    e1.record()
     torch.cuda.synchronize()
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    ms = e0.elapsed_time(e1) / steps
     if stats is not None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            fn(warmup + steps + i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
         stats.update({"median_ms": float(np.median(per)), "p10_ms": float(np.percentile(per, 10)),
                       "p90_ms": float(np.percentile(per, 90))})
-    return ev[0].elapsed_time(ev[steps]) / steps
+    return ms
 
 
 # Sources of each measured kernel unit (a stored counter measurement is valid only for them).
@@ -285,16 +294,10 @@ def bench_prefill(cfg, steps, warmup, parts=("call", "attention", "chunk")):
     def call(i):
         M.mla_prefill(d.dims, d.wst, x, B, S_, cs, y, ws, nws)
 
-    st_call = {}
-    ms = float("nan")
-    if "call" in parts:
-        log(f"[bench] {cfg.name}: timing mla_prefill")
-        ms = timed(torch, call, steps, warmup, st_call)
-    else:
-        # the latent cache must hold the workload's rows (a zero cache gives all-zero keys and
-        # values, whose products draw less power and run at a higher clock)
-        call(0)
-        torch.cuda.synchronize()
+    # the latent cache must hold the workload's rows (a zero cache gives all-zero keys and
+    # values, whose products draw less power and run at a higher clock)
+    call(0)
+    torch.cuda.synchronize()
     H, dn, dr, dv = cfg.n_heads, cfg.d_nope, cfg.d_rope, cfg.d_v
     g = torch.Generator(device="cpu").manual_seed(cfg.seed)
     q = torch.randn((B, S_, H, dn + dr), generator=g).to(d.dt).cuda()
@@ -304,9 +307,16 @@ def bench_prefill(cfg, steps, warmup, parts=("call", "attention", "chunk")):
     def att(i):
         M.mla_prefill_attention(d.dims, d.wst, q, B, S_, cs, o, wsa, nwsa)
 
+    # the attention unit is timed first, on its own (as its rocprofv3 summary times it): a
+    # loop of whole-layer calls before it leaves the clock lower for a while
     log(f"[bench] {cfg.name}: timing mla_prefill_attention")
     st_att = {}
     ms_att = timed(torch, att, steps, warmup, st_att)
+    st_call = {}
+    ms = float("nan")
+    if "call" in parts:
+        log(f"[bench] {cfg.name}: timing mla_prefill")
+        ms = timed(torch, call, steps, warmup, st_call)
     core = 2.0 * B * H * (S_ * (S_ + 1) / 2) * (dn + dr + dv)
     kvup = 2.0 * B * S_ * cfg.r_kv * H * (dn + dv) / cfg.n_latent_heads
     w = d.prob.weights

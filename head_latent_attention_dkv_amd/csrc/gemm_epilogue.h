@@ -13,6 +13,30 @@
 
 namespace mla {
 
+// The rotation of rope_sincos for outputs stored in bf16: the angle in revolutions, reduced to
+// [-1/2, 1/2] in double, then the hardware sine and cosine (V_SIN_F32 / V_COS_F32 take
+// revolutions).  Their error, about 1e-6, is far below the bf16 rounding of the rotated
+// values, and they cost a few instructions against a few dozen for sincosf.
+__device__ __forceinline__ void rope_sincos_rev(int pos, float inv_freq_hi, float inv_freq_lo,
+                                                float* s, float* c) {
+  double r = (double)pos * (((double)inv_freq_hi + (double)inv_freq_lo) * 0.15915494309189533577);
+  r -= rint(r);
+  const float rf = (float)r;
+  *s = __builtin_amdgcn_sinf(rf);
+  *c = __builtin_amdgcn_cosf(rf);
+}
+
+// Sine and cosine of a rotary angle: fp32 outputs keep sincosf, bf16 outputs take the
+// hardware functions (rope_sincos_rev).
+template <typename T>
+__device__ __forceinline__ void rope_angle(int pos, float hi, float lo, float* s, float* c) {
+  if constexpr (sizeof(T) == 2) {
+    rope_sincos_rev(pos, hi, lo, s, c);
+  } else {
+    rope_sincos(pos, hi, lo, s, c);
+  }
+}
+
 // Segment s of p for a lane-dependent s: picked from the kernel arguments (seg_out), or
 // read straight from p when p is a copy in LDS (fewer registers live: the fields are loaded
 // where they are used).
@@ -65,7 +89,7 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
         float sn, cs;
         if (sg.rope == ROPE_INTERLEAVED) {
           const int j = hh >> 1;
-          rope_sincos(pos, rtab[j], rtab[kMaxRopePairs + j], &sn, &cs);
+          rope_angle<T>(pos, rtab[j], rtab[kMaxRopePairs + j], &sn, &cs);
           if ((hh & 1) == 0) {
             const float o = Cs[r * ldc + c + 1];
             v = v * cs - o * sn;
@@ -76,7 +100,7 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, const float*
         } else {
           const int half = sg.rope_d >> 1;
           const int j = hh % half;
-          rope_sincos(pos, rtab[j], rtab[kMaxRopePairs + j], &sn, &cs);
+          rope_angle<T>(pos, rtab[j], rtab[kMaxRopePairs + j], &sn, &cs);
           if (hh < half) {
             const float o = Cs[r * ldc + c + half];
             v = v * cs - o * sn;
@@ -190,7 +214,7 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
         for (int q = 0; q < 4; ++q) {
           float sn, cs;
           const int jj = (hh >> 1) + q;
-          rope_sincos(pos, rtab[jj], rtab[kMaxRopePairs + jj], &sn, &cs);
+          rope_angle<T>(pos, rtab[jj], rtab[kMaxRopePairs + jj], &sn, &cs);
           const float x0 = v[i][2 * q], x1 = v[i][2 * q + 1];
           v[i][2 * q] = x0 * cs - x1 * sn;
           v[i][2 * q + 1] = x0 * sn + x1 * cs;
@@ -208,7 +232,7 @@ __device__ __forceinline__ void epilogue_block_fast(const GemmParams& p, const f
         for (int e = 0; e < 8; ++e) {
           float sn, cs;
           const int jj = (hh + e) % half;
-          rope_sincos(pos, rtab[jj], rtab[kMaxRopePairs + jj], &sn, &cs);
+          rope_angle<T>(pos, rtab[jj], rtab[kMaxRopePairs + jj], &sn, &cs);
           v[i][e] = lo ? v[i][e] * cs - o[e] * sn : o[e] * sn + v[i][e] * cs;
         }
       }
