@@ -125,6 +125,11 @@ class Dev:
         return last
 
 
+# Per-call spread (a second loop with an event after every call).  Off for `--only` runs,
+# whose rocprofv3 traces then hold back-to-back calls only, as the timed loop runs them.
+PER_CALL_STATS = True
+
+
 def timed(torch, fn, steps, warmup, stats=None):
     """Average ms per call of fn(i) over `steps` calls after `warmup` calls.
 
@@ -146,7 +151,7 @@ def timed(torch, fn, steps, warmup, stats=None):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    if stats is not None:
+    if stats is not None and PER_CALL_STATS:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record()
         for i in range(steps):
@@ -790,6 +795,9 @@ def main():
     if args.summarize:
         summarize_profiles(args.summarize)
         return
+    if args.only != "all":
+        global PER_CALL_STATS
+        PER_CALL_STATS = False
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: there is no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
