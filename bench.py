@@ -227,6 +227,22 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None, ctx_from=No
     def step(i):
         M.mla_decode(d.dims, d.wst, x, B, cl, max_ctx, cstructs[i % copies], y, ws, nws)
 
+    # dominant kernel unit: split-context latent attention + combine (timed first, as its
+    # rocprofv3 summary times it: right after the cache fill)
+    H, L = cfg.n_heads, cfg.n_latent_heads
+    rb = cfg.r_kv // L
+    g = torch.Generator(device="cpu").manual_seed(cfg.seed)
+    q_lat = (torch.randn((B, H, rb), generator=g) * 0.6).to(d.dt).cuda()
+    q_rope = (torch.randn((B, H, cfg.d_rope), generator=g) * 0.6).to(d.dt).cuda() if cfg.d_rope else None
+    z = torch.empty((B, H, rb), dtype=d.dt, device="cuda")
+    wsa, nwsa = d.workspace(M.MLA_OP_DECODE_ATTENTION, B, max_ctx)
+
+    def att(i):
+        M.mla_decode_attention(d.dims, q_lat, q_rope, B, cl, max_ctx, cstructs[i % copies], z, wsa, nwsa)
+
+    log(f"[bench] {cfg.name}: timing mla_decode_attention")
+    st_att = {}
+    ms_att = timed(torch, att, attention_steps or steps, warmup, st_att)
     log(f"[bench] {cfg.name}: timing mla_decode")
     st_call = {}
     ms = timed(torch, step, steps, warmup, st_call)
@@ -252,21 +268,6 @@ def bench_decode(cfg, steps, warmup, copies=2, attention_steps=None, ctx_from=No
         ms_graph = timed(torch, lambda i: graphs[i % copies].replay(), steps, warmup, st_graph)
         del graphs
 
-    # dominant kernel unit: split-context latent attention + combine
-    H, L = cfg.n_heads, cfg.n_latent_heads
-    rb = cfg.r_kv // L
-    g = torch.Generator(device="cpu").manual_seed(cfg.seed)
-    q_lat = (torch.randn((B, H, rb), generator=g) * 0.6).to(d.dt).cuda()
-    q_rope = (torch.randn((B, H, cfg.d_rope), generator=g) * 0.6).to(d.dt).cuda() if cfg.d_rope else None
-    z = torch.empty((B, H, rb), dtype=d.dt, device="cuda")
-    wsa, nwsa = d.workspace(M.MLA_OP_DECODE_ATTENTION, B, max_ctx)
-
-    def att(i):
-        M.mla_decode_attention(d.dims, q_lat, q_rope, B, cl, max_ctx, cstructs[i % copies], z, wsa, nwsa)
-
-    log(f"[bench] {cfg.name}: timing mla_decode_attention")
-    st_att = {}
-    ms_att = timed(torch, att, attention_steps or steps, warmup, st_att)
     res = {
         "call_stats": st_call, "attention_stats": st_att, "ms_per_call_graph": ms_graph, "graph_stats": st_graph,
         "workload": cfg.name, "batch": B, "ctx_total": int(sum(ctx)), "max_ctx": max_ctx,
