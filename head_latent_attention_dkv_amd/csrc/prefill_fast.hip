@@ -68,13 +68,14 @@ struct FlashCfg {
   static_assert(DR == 0 || DR == 64, "rotary width");
 };
 
-// TRAIN: the training forward -- dropout on the attention weights (keep bits drawn per group
-// of four keys, see dropout_keep4) and the per-row log-sum-exp written for the backward.
+// One work item: the 256 queries of query tile L's (sequence, head), in the block order
+// below.  TRAIN: the training forward -- dropout on the attention weights (keep bits drawn
+// per group of four keys, see dropout_keep4) and the per-row log-sum-exp written for the
+// backward.
 template <int DN, int DR, int QB, bool TRAIN>
-__global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashParams p) {
+__device__ __forceinline__ void flash_item(const FlashParams& p, const int L, unsigned char* smem) {
   using C = FlashCfg<DN, DR, QB>;
   constexpr int QW = 32 * QB;                          // queries per wave
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -84,7 +85,6 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
   // Every XCD then gets the same work, and a group's keys / values are reused from its
   // XCD's L2.  (Group counts not divisible by 8 use the plain order.)
   const int ntq = p.ntq;
-  const int L = blockIdx.x;
   const int ngroups = p.B * p.H;
   int g, qrev;
   if (ngroups % 8 == 0) {
@@ -423,28 +423,76 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
     __syncthreads();
     pass(std::integral_constant<int, 2>{});
     copies_end();
+    __syncthreads();   // every wave is done with the stages before the output staging below
   }
 
-  // ---- normalise and store o[b][q][h][:] (4 consecutive features per 8-byte store) ----
+  // ---- normalise and store o[b][q][h][:].  The wave's rows (one query each) go through LDS
+  // (row stride DV * 2 + 16 bytes) so that every store instruction writes whole 16-byte
+  // pieces of four query rows; written from the accumulators, a store instruction touched
+  // 32 query rows 16 bytes each.  Every wave is past the vote barriers: the stages are free.
+  constexpr int ORS = C::DV * 2 + 16;                  // staging row stride (bytes)
+  static_assert(C::NWV * QW * ORS <= C::LDS, "output staging fits the stages");
+  unsigned char* orow = smem + wave * QW * ORS;
+  const int dvo = p.dv_out > 0 ? p.dv_out : C::DV;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const float inv = (TRAIN && p.keep_thr ? p.keep_scale : 1.f) / lt;
     const int qi = qw + 32 * qb + col;
-    if (qi >= p.T) continue;
-    if (TRAIN && p.lse && half == 0) p.lse[bh_q * p.T + qi] = m_ref[qb] + __log2f(lt);
-    const int dvo = p.dv_out > 0 ? p.dv_out : C::DV;
-    bf16* op = reinterpret_cast<bf16*>(p.o) + (((long long)b * p.T + qi) * p.H + h) * dvo + 4 * half;
+    if (TRAIN && p.lse && half == 0 && qi < p.T) p.lse[bh_q * p.T + qi] = m_ref[qb] + __log2f(lt);
+    // accumulator element 4 g + e of lane l in block db: feature 32 db + 8 g + 4 (l/32) + e
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if (32 * db >= dvo) continue;
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][qb][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = v;
+        *reinterpret_cast<bf16x4*>(orow + (32 * qb + col) * ORS + (32 * db + 8 * g + 4 * half) * 2) = v;
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  constexpr int CPR = C::DV / 8;                       // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;                        // rows per store instruction
+#pragma unroll
+  for (int r0 = 0; r0 < QW; r0 += RPI) {
+    const int r = r0 + lane / CPR, c = lane % CPR;
+    const int qi = qw + r;
+    if (qi >= p.T || 8 * c >= dvo) continue;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(orow + r * ORS + 16 * c);
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(p.o) + (((long long)b * p.T + qi) * p.H + h) * dvo + 8 * c) = v;
+  }
+}
+
+// One workgroup per work item.
+template <int DN, int DR, int QB, bool TRAIN>
+__global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashParams p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  flash_item<DN, DR, QB, TRAIN>(p, blockIdx.x, smem);
+}
+
+// Persistent form: one workgroup per CU walks the items of its XCD (block w runs on XCD
+// w % 8, so workgroup w takes the items L with L % 8 = w % 8).  Launching one workgroup per
+// item left a CU idle between items for ~14 % of the kernel (per-workgroup stamps: 220 of
+// 256 workgroups active on average).  XCD x's items are its slots (groups x, x + 8, ..., ntq
+// query tiles each, longest first); round k of its CPX workgroups covers slots CPX k ..
+// CPX k + CPX - 1, i.e. CPX / ntq whole groups, whose keys / values the XCD's L2 then holds,
+// and workgroup c takes query tile (c + k) % ntq of group c / ntq of the round, so that
+// over ntq rounds every workgroup runs every tile length once: equal work per CU.
+template <int DN, int DR, int QB, bool TRAIN>
+__global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_persist_kernel(FlashParams p, int n_items) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int ntq = p.ntq;
+  const int cpx = gridDim.x >> 3;                      // workgroups per XCD (a multiple of ntq)
+  const int x = blockIdx.x & 7, c = blockIdx.x >> 3;
+  const int n_slots = n_items >> 3;
+  const int jbase = (c / ntq) * ntq, jq = c % ntq;
+  for (int k = 0;; ++k) {
+    const int slot = cpx * k + jbase + (jq + k) % ntq;
+    if (slot >= n_slots) break;
+    flash_item<DN, DR, QB, TRAIN>(p, slot * 8 + x, smem);
+    __syncthreads();   // every wave is done with the item's LDS before the next one's copies
   }
 }
 
@@ -459,9 +507,17 @@ template <int DN, int DR, int QB, bool TRAIN = false>
 hipError_t launch_flash(const FlashParams& pin, hipStream_t s) {
   FlashParams p = pin;
   p.ntq = cdiv(p.T, FQ);
-  dim3 grid(p.ntq * p.H * p.B);
+  const int n_items = p.ntq * p.H * p.B;
   constexpr size_t lds = FlashCfg<DN, DR, QB>::LDS;
-  hipLaunchKernelGGL((prefill_flash_kernel<DN, DR, QB, TRAIN>), grid, dim3(64 * (8 / QB)), lds, s, p);
+  // persistent form when the items split evenly over the XCDs and a round of whole groups
+  // fits the XCD's CUs
+  const int cpx = (device_cu_count() / 8) / p.ntq * p.ntq;
+  if ((p.B * p.H) % 8 == 0 && cpx > 0 && n_items > 8 * cpx) {
+    hipLaunchKernelGGL((prefill_flash_persist_kernel<DN, DR, QB, TRAIN>), dim3(8 * cpx), dim3(64 * (8 / QB)), lds, s,
+                       p, n_items);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((prefill_flash_kernel<DN, DR, QB, TRAIN>), dim3(n_items), dim3(64 * (8 / QB)), lds, s, p);
   return hipGetLastError();
 }
 }  // namespace
