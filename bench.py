@@ -513,7 +513,7 @@ PROFILE_UNITS = {
                          work=lambda: MLRA_LATENT_HEAD, bound="hbm", file="mlra_latent_head_decode_attention"),
     "prefill_attention": dict(title="mla_prefill_attention, DeepSeek-V2 prefill (B=4, S=4096, H=128): K/V "
                                     "up-projection + flash causal attention",
-                              kernels=("gemm_kv_kernel", "prefill_flash_kernel"),
+                              kernels=("gemm_kv_kernel", "prefill_flash"),
                               work=lambda: S.CONFIGS["dsv2_prefill"], bound="mfma", file="dsv2_prefill_attention"),
 }
 
