@@ -475,24 +475,40 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
 // Persistent form: one workgroup per CU walks the items of its XCD (block w runs on XCD
 // w % 8, so workgroup w takes the items L with L % 8 = w % 8).  Launching one workgroup per
 // item left a CU idle between items for ~14 % of the kernel (per-workgroup stamps: 220 of
-// 256 workgroups active on average).  XCD x's items are its slots (groups x, x + 8, ..., ntq
-// query tiles each, longest first); round k of its CPX workgroups covers slots CPX k ..
-// CPX k + CPX - 1, i.e. CPX / ntq whole groups, whose keys / values the XCD's L2 then holds,
-// and workgroup c takes query tile (c + k) % ntq of group c / ntq of the round, so that
-// over ntq rounds every workgroup runs every tile length once: equal work per CU.
+// 256 workgroups active on average).  XCD x's items are its slots: groups x, x + 8, ...,
+// ntq query tiles each, slot ntq j + r holding query tile ntq - 1 - r of the XCD's group j.
+// With ntq even, a round gives each of ntq / 2 workgroups a pair of one group's tiles, the
+// short tile t and then the long tile ntq - 1 - t: every pair costs the same, so the CPX
+// workgroups of an XCD stay in step and work on CPX / (ntq / 2) groups at a time, whose keys
+// and values their L2 holds; the long tiles start within a short-tile length of each other
+// and read the keys in the same order.  (A rotation of single tiles over the workgroups,
+// equal over ntq rounds but not per round, let the workgroups drift apart over ~10 groups:
+// 9.2 GB fetched per launch against 5.9 GB with pairs, and 1.2 % slower.)  With ntq odd,
+// workgroup c takes query tile (c + k) % ntq of group c / ntq of round k.
 template <int DN, int DR, int QB, bool TRAIN>
 __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_persist_kernel(FlashParams p, int n_items) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int ntq = p.ntq;
-  const int cpx = gridDim.x >> 3;                      // workgroups per XCD (a multiple of ntq)
+  const int cpx = gridDim.x >> 3;                      // workgroups per XCD
   const int x = blockIdx.x & 7, c = blockIdx.x >> 3;
   const int n_slots = n_items >> 3;
-  const int jbase = (c / ntq) * ntq, jq = c % ntq;
+  if (ntq % 2 == 0) {                                  // cpx is a multiple of ntq / 2
+    const int hq = ntq >> 1, n_groups = n_slots / ntq;
+    const int gpr = cpx / hq, t = c % hq;
+    for (int g = c / hq; g < n_groups; g += gpr) {
+      flash_item<DN, DR, QB, TRAIN>(p, (g * ntq + ntq - 1 - t) * 8 + x, smem);   // query tile t
+      __syncthreads();   // every wave is done with the item's LDS before the next one's copies
+      flash_item<DN, DR, QB, TRAIN>(p, (g * ntq + t) * 8 + x, smem);            // tile ntq - 1 - t
+      __syncthreads();
+    }
+    return;
+  }
+  const int jbase = (c / ntq) * ntq, jq = c % ntq;     // cpx is a multiple of ntq
   for (int k = 0;; ++k) {
     const int slot = cpx * k + jbase + (jq + k) % ntq;
     if (slot >= n_slots) break;
     flash_item<DN, DR, QB, TRAIN>(p, slot * 8 + x, smem);
-    __syncthreads();   // every wave is done with the item's LDS before the next one's copies
+    __syncthreads();
   }
 }
 
@@ -510,8 +526,9 @@ hipError_t launch_flash(const FlashParams& pin, hipStream_t s) {
   const int n_items = p.ntq * p.H * p.B;
   constexpr size_t lds = FlashCfg<DN, DR, QB>::LDS;
   // persistent form when the items split evenly over the XCDs and a round of whole groups
-  // fits the XCD's CUs
-  const int cpx = (device_cu_count() / 8) / p.ntq * p.ntq;
+  // (pairs of tiles for even ntq) fits the XCD's CUs
+  const int per = p.ntq % 2 == 0 ? p.ntq / 2 : p.ntq;    // workgroups per group and round
+  const int cpx = (device_cu_count() / 8) / per * per;
   if ((p.B * p.H) % 8 == 0 && cpx > 0 && n_items > 8 * cpx) {
     hipLaunchKernelGGL((prefill_flash_persist_kernel<DN, DR, QB, TRAIN>), dim3(8 * cpx), dim3(64 * (8 / QB)), lds, s,
                        p, n_items);

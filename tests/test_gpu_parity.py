@@ -28,6 +28,9 @@ MLRA = S.CONFIGS["mlra_decode"].replace(d_model=512, batch=4, ctx_lo=0, ctx_hi=0
 # one partial 256-query tile, five key tiles).
 DSV2_PF = S.CONFIGS["dsv2_prefill"].replace(name="dsv2_prefill_s320", d_model=512, batch=2, seq=320)
 SMALL_PF = S.CONFIGS["small_lm"].replace(name="small_lm_s320", batch=2, seq=320)
+# 576 = two full 256-query tiles and a partial one: an odd number of query tiles per head
+# (even counts are walked in pairs of a short and a long tile, odd ones one tile at a time).
+DSV2_PF3 = S.CONFIGS["dsv2_prefill"].replace(name="dsv2_prefill_s576", d_model=512, batch=2, seq=576)
 MLRA_PF = S.CONFIGS["mlra_decode"].replace(name="mlra_prefill_s384", mode="prefill", d_model=512, batch=2,
                                            seq=384, ctx_lo=0, ctx_hi=0)
 # Few-row products (B*S <= 128 rows) of the full-RoPE family: the query and key rotations
@@ -379,7 +382,7 @@ def _decode_attention_case(gu, cfg, ctx, max_seq=None):
     gu.assert_close(gu.to_host(z), want, cfg.dtype, "z")
 
 
-@pytest.mark.parametrize("cfg", [DSV2_P, SMALL, DSV2_PF, SMALL_PF], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [DSV2_P, SMALL, DSV2_PF, SMALL_PF, DSV2_PF3], ids=lambda c: c.name)
 def test_prefill_attention_entry(gu, cfg):
     """mla_prefill_attention on oracle queries and oracle latent rows."""
     import head_latent_attention_dkv_amd as M
