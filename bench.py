@@ -130,8 +130,15 @@ class Dev:
 PER_CALL_STATS = True
 
 
+# Untimed calls before every timed loop run for at least this long (after the `warmup` calls),
+# so that the loop starts at the clock the GPU holds under that load: a loop of a few short
+# calls right after a phase of other work otherwise times part of the clock ramp.
+MIN_WARM_S = 0.1
+
+
 def timed(torch, fn, steps, warmup, stats=None):
-    """Average ms per call of fn(i) over `steps` calls after `warmup` calls.
+    """Average ms per call of fn(i) over `steps` calls after `warmup` calls (and at least
+    MIN_WARM_S seconds of untimed calls).
 
     HIP events on the current stream (the stream the library launches on) bracket the
     timed calls, with a device synchronisation on both sides; nothing else is enqueued
@@ -141,22 +148,31 @@ def timed(torch, fn, steps, warmup, stats=None):
     """
     if steps <= 0:
         return float("nan")
+    i = 0
     for i in range(warmup):
         fn(i)
+    i = warmup
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < MIN_WARM_S:
+        for _ in range(4):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        fn(warmup + i)
+    for j in range(steps):
+        fn(i + j)
     e1.record()
     torch.cuda.synchronize()
+    i += steps
     ms = e0.elapsed_time(e1) / steps
     if stats is not None and PER_CALL_STATS:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record()
-        for i in range(steps):
-            fn(warmup + steps + i)
-            ev[i + 1].record()
+        for j in range(steps):
+            fn(i + j)
+            ev[j + 1].record()
         torch.cuda.synchronize()
         per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
         stats.update({"median_ms": float(np.median(per)), "p10_ms": float(np.percentile(per, 10)),
@@ -797,8 +813,10 @@ def main():
         summarize_profiles(args.summarize)
         return
     if args.only != "all":
-        global PER_CALL_STATS
+        # profiled runs: the trace holds the timed loop's back-to-back calls and few others
+        global PER_CALL_STATS, MIN_WARM_S
         PER_CALL_STATS = False
+        MIN_WARM_S = 0.0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: there is no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -844,7 +862,7 @@ def main():
         dec, _ = bench_decode(S.CONFIGS["dsv2_decode"], args.steps, args.warmup)
         out["decode"] = dec
     if args.only in ("all", "prefill"):
-        out["prefill"] = bench_prefill(S.CONFIGS["dsv2_prefill"], max(3, args.steps // 4), max(1, args.warmup // 2))
+        out["prefill"] = bench_prefill(S.CONFIGS["dsv2_prefill"], max(10, args.steps // 2), max(1, args.warmup // 2))
     if args.only in ("all", "mlra"):
         out["mlra"], _ = bench_decode(S.CONFIGS["mlra_decode"], args.steps, args.warmup, copies=1)
         # one latent head's cache is 288 MB: two copies (576 MB) exceed the 256 MB Infinity Cache
