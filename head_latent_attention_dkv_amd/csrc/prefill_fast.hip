@@ -478,12 +478,13 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_kernel(FlashPa
 // 256 workgroups active on average).  XCD x's items are its slots: groups x, x + 8, ...,
 // ntq query tiles each, slot ntq j + r holding query tile ntq - 1 - r of the XCD's group j.
 // With ntq even, a round gives each of ntq / 2 workgroups a pair of one group's tiles, the
-// short tile t and then the long tile ntq - 1 - t: every pair costs the same, so the CPX
+// long tile ntq - 1 - t and then the short tile t: every pair costs the same, so the CPX
 // workgroups of an XCD stay in step and work on CPX / (ntq / 2) groups at a time, whose keys
-// and values their L2 holds; the long tiles start within a short-tile length of each other
-// and read the keys in the same order.  (A rotation of single tiles over the workgroups,
-// equal over ntq rounds but not per round, let the workgroups drift apart over ~10 groups:
-// 9.2 GB fetched per launch against 5.9 GB with pairs, and 1.2 % slower.)  With ntq odd,
+// and values their L2 holds; the long tiles, most of the work, start together and read the
+// keys in the same order.  (A rotation of single tiles over the workgroups, equal over ntq
+// rounds but not per round, let the workgroups drift apart over ~10 groups: 9.2 GB fetched
+// per launch against 5.9 GB with pairs, and 1.2 % slower; short tile first, 1.3 % slower
+// than long first.)  With ntq odd,
 // workgroup c takes query tile (c + k) % ntq of group c / ntq of round k.
 template <int DN, int DR, int QB, bool TRAIN>
 __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_persist_kernel(FlashParams p, int n_items) {
@@ -496,9 +497,9 @@ __global__ void __launch_bounds__(64 * (8 / QB), 1) prefill_flash_persist_kernel
     const int hq = ntq >> 1, n_groups = n_slots / ntq;
     const int gpr = cpx / hq, t = c % hq;
     for (int g = c / hq; g < n_groups; g += gpr) {
-      flash_item<DN, DR, QB, TRAIN>(p, (g * ntq + ntq - 1 - t) * 8 + x, smem);   // query tile t
-      __syncthreads();   // every wave is done with the item's LDS before the next one's copies
       flash_item<DN, DR, QB, TRAIN>(p, (g * ntq + t) * 8 + x, smem);            // tile ntq - 1 - t
+      __syncthreads();   // every wave is done with the item's LDS before the next one's copies
+      flash_item<DN, DR, QB, TRAIN>(p, (g * ntq + ntq - 1 - t) * 8 + x, smem);   // query tile t
       __syncthreads();
     }
     return;

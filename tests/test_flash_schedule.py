@@ -32,8 +32,8 @@ def walk(grid, n_items, ntq):
             gpr, t = cpx // hq, c % hq
             g = c // hq
             while g < n_groups:
-                mine.append((g * ntq + ntq - 1 - t) * 8 + x)
                 mine.append((g * ntq + t) * 8 + x)
+                mine.append((g * ntq + ntq - 1 - t) * 8 + x)
                 g += gpr
         else:
             jbase, jq = (c // ntq) * ntq, c % ntq
