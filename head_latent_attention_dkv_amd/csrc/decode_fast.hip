@@ -153,10 +153,10 @@ __global__ void __launch_bounds__(NW * 64) decode_fast_kernel(DecodeParams p) {
         // of the tile, its chunk (ln ^ key) % 16 (key < 16 leaves the quarter unchanged)
         const int tok = min(t0 + 32 * (ln >> 4) + t, tok_end - 1);
         const uint32_t c = (uint32_t)((ln ^ bitrev4(t & 15)) & 15);
-        dma16_s(ckv_seq, (uint32_t)tok * (VL * 2) + (c << 4), __builtin_amdgcn_readfirstlane(sbase + t * 1024));
+        dma16_s_nt(ckv_seq, (uint32_t)tok * (VL * 2) + (c << 4), __builtin_amdgcn_readfirstlane(sbase + t * 1024));
       } else {
         const int tok = min(t0 + t, tok_end - 1);
-        dma16_s(ckv_seq + (long long)tok * p.r_kv * 2, ln16 ^ ((uint32_t)bitrev4(t & 15) << 4),
+        dma16_s_nt(ckv_seq + (long long)tok * p.r_kv * 2, ln16 ^ ((uint32_t)bitrev4(t & 15) << 4),
                 __builtin_amdgcn_readfirstlane(sbase + t * 1024));
       }
     }
@@ -383,13 +383,13 @@ __global__ void __launch_bounds__(256, 1) decode_h128_kernel(DecodeParams p) {
       const int t = wave * RPW + i;                    // wave-uniform
       const int tok = min(t0 + t, tok_end - 1);
       const uint32_t key16 = (uint32_t)bitrev4(t & 15) << 4;
-      dma16_s(ckv_seq + (long long)tok * (VL * 2), ln16 ^ key16, __builtin_amdgcn_readfirstlane(sbase + t * 1024));
+      dma16_s_nt(ckv_seq + (long long)tok * (VL * 2), ln16 ^ key16, __builtin_amdgcn_readfirstlane(sbase + t * 1024));
     }
     if constexpr (VR > 0) {
       const int t = wave * RPW + (ln >> 3);
       const int tok = min(t0 + t, tok_end - 1);
       const uint32_t c = (uint32_t)(((ln & 7) ^ ((t >> 1) & 7)) << 4);
-      dma16_s(kr_seq, (uint32_t)tok * (VR * 2) + c, __builtin_amdgcn_readfirstlane(sbase + C::LAT_BYTES + wave * RPW * 128));
+      dma16_s_nt(kr_seq, (uint32_t)tok * (VR * 2) + c, __builtin_amdgcn_readfirstlane(sbase + C::LAT_BYTES + wave * RPW * 128));
     }
   };
 

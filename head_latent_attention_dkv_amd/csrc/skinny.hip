@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(256, CB * ROWS <= 256 ? 2 : 1) skinny_stream_k
     const uint32_t base = lds0 + (st % NST) * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::WPW; ++i)
-      dma16(wsrc[i] + st * KT, __builtin_amdgcn_readfirstlane(base + (wave * C::WPW + i) * 1024));
+      dma16_nt(wsrc[i] + st * KT, __builtin_amdgcn_readfirstlane(base + (wave * C::WPW + i) * 1024));   // read once
 #pragma unroll
     for (int i = 0; i < C::XPW; ++i)
       dma16(xsrc[i] + st * KT, __builtin_amdgcn_readfirstlane(base + C::WBYTES + (wave * C::XPW + i) * 1024));
