@@ -106,11 +106,14 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
     const long long wgs = (long long)B * sp.fast_head_tiles;
     int ns = (int)((kCUs + wgs - 1) / wgs);
     chunk = round_up(cdiv(ntok, ns < 1 ? 1 : ns), 32);
-    // MLRA (latent blocks): splits of at most 1024 tokens keep ragged batches balanced over
-    // the CUs while each workgroup streams long enough to amortise its start
-    if (sp.fast_variant == 2 && chunk > 1024) chunk = 1024;
-    // token split (four waves on four 32-token slices of 128-token tiles): the same bytes per
-    // split as the MLRA kernel's 1024 tokens of 1 KB rows
+    // MLRA (latent blocks): splits of at most 1536 tokens keep ragged batches balanced over
+    // the CUs while each workgroup streams long enough to amortise its start.  Contexts
+    // U[512, 16384] at B = 128 (≈800 splits, just over three per CU): 1024 / 1280 / 1536 /
+    // 1792 / 2048 tokens took 219 / 215 / 190 / 204 / 242 us per call.
+    if (sp.fast_variant == 2 && chunk > 1536) chunk = 1536;
+    // token split (four waves on four 32-token slices of 128-token tiles): at most 4096 tokens
+    // of 256-byte rows (the MLRA latent-head contexts: 5120 and 6144 took 69.5 and 73.8 us per
+    // call against 60.6 us)
     if (sp.fast_variant == 5) chunk = min(round_up(chunk, 128), 4096);
   } else {
     const long long wgs = (long long)B * L * sp.head_tiles;
