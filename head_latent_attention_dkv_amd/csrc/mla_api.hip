@@ -112,8 +112,8 @@ SplitPlan plan_decode(const mla_dims* d, int B, int max_ctx) {
     // 1792 / 2048 tokens took 219 / 215 / 190 / 204 / 242 us per call.
     if (sp.fast_variant == 2 && chunk > 1536) chunk = 1536;
     // token split (four waves on four 32-token slices of 128-token tiles): at most 4096 tokens
-    // of 256-byte rows (the MLRA latent-head contexts: 5120 and 6144 took 69.5 and 73.8 us per
-    // call against 60.6 us)
+    // of 256-byte rows (the MLRA latent-head contexts: caps of 1536 / 2048 / 3072 / 5120 / 6144
+    // took 62.6 / 74.1 / 66.7 / 69.5 / 73.8 us per call against 60.5 us)
     if (sp.fast_variant == 5) chunk = min(round_up(chunk, 128), 4096);
   } else {
     const long long wgs = (long long)B * L * sp.head_tiles;
